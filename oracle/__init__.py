@@ -1,0 +1,178 @@
+"""CPU oracle for the low-precision integer GEMM C[M,N] = A[M,K] . B[N,K]^T.
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only ``tests/``, the smoke check
+in ``__graft_entry__`` and the benchmark's CPU-baseline leg may import this
+module.  It shares no code with the GPU library; the two meet only through the
+seeded input bytes that both are given.
+
+The arithmetic lives in ``lpgemm_oracle.c`` (plain C, int64 accumulation, see
+its header for the passages of the pages it follows).  This module builds it
+with gcc and marshals numpy arrays through ctypes; it does no arithmetic of its
+own.
+
+Pages cited (by title):
+  * tilelang PR "[CUDA] Support int4 T.gemm" (#2063), example gemm_int4.
+  * tilelang PR "[Example] add w4a8 gemm kernel" (#815), reviews of
+    torch_convert / ref_program.
+  * TileLang tutorial ch. 14 sec. 5 "low_precision_gemm.py", pack_int4 and
+    matmul_int4.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against
+hand-worked values, closed forms, brute force and an independent numpy
+computation; no function is left unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lpgemm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_lpgemm_oracle.so")
+
+_ERRORS = {1: "invalid argument", 2: "result outside int32", 3: "out of host memory"}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP over the outer row loop)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+           "-o", tmp, _SRC]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_num_threads.restype = ctypes.c_int
+    for name in ("oracle_unpack_int4", "oracle_pack_int4"):
+        f = getattr(lib, name)
+        f.argtypes = [p, i64, i64, p]
+        f.restype = ctypes.c_int
+    for name in ("oracle_gemm_i4i4", "oracle_gemm_w4a8"):
+        f = getattr(lib, name)
+        f.argtypes = [p, p, i64, i64, i64, p]
+        f.restype = ctypes.c_int
+    for name in ("oracle_gemm_i4i4_at", "oracle_gemm_w4a8_at"):
+        f = getattr(lib, name)
+        f.argtypes = [p, p, i64, i64, i64, p, p, i64, p]
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"oracle {what}: {_ERRORS.get(rc, rc)}")
+
+
+def _bytes2d(x, rows: int, cols: int, name: str) -> np.ndarray:
+    """View an (int8 or uint8) array as contiguous uint8 [rows, cols]."""
+    a = np.ascontiguousarray(x)
+    if a.dtype not in (np.int8, np.uint8):
+        raise TypeError(f"{name} must be int8 or uint8, got {a.dtype}")
+    a = a.view(np.uint8)
+    if a.size != rows * cols:
+        raise ValueError(f"{name} has {a.size} bytes, expected {rows}x{cols}")
+    return a.reshape(rows, cols)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p) if a.size else None
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's row loop uses."""
+    return int(_load().oracle_num_threads())
+
+
+def unpack_int4(packed, K: int) -> np.ndarray:
+    """Packed bytes [rows, K/2] -> logical int4 values as int8 [rows, K]."""
+    p = np.ascontiguousarray(packed)
+    rows = p.shape[0] if p.ndim == 2 else 1
+    if K % 2:
+        raise ValueError("K must be even")
+    p = _bytes2d(p, rows, K // 2, "packed")
+    out = np.empty((rows, K), dtype=np.int8)
+    _check(_load().oracle_unpack_int4(_ptr(p), rows, K, _ptr(out)), "unpack_int4")
+    return out
+
+
+def pack_int4(logical) -> np.ndarray:
+    """Logical int4 held as int8 [rows, K] -> packed uint8 [rows, K/2].
+
+    Mirrors the page's packer: int8 input only (TypeError otherwise), last
+    dimension even (ValueError otherwise).
+    """
+    x = np.asarray(logical)
+    if x.dtype != np.int8:
+        raise TypeError("pack_int4 expects int8 logical values")
+    if x.ndim == 0 or x.shape[-1] % 2:
+        raise ValueError("the last dimension of a logical int4 tensor must be even")
+    K = x.shape[-1]
+    rows = x.size // K if K else int(np.prod(x.shape[:-1]))
+    x2 = np.ascontiguousarray(x).reshape(rows, K)
+    out = np.empty((rows, K // 2), dtype=np.uint8)
+    _check(_load().oracle_pack_int4(_ptr(x2), rows, K, _ptr(out)), "pack_int4")
+    return out.reshape(x.shape[:-1] + (K // 2,))
+
+
+def gemm_i4i4(A_packed, B_packed, M: int, N: int, K: int) -> np.ndarray:
+    """int4 x int4: C[M,N] int32 = A . B^T from packed [M,K/2] and [N,K/2]."""
+    if K % 2 or min(M, N, K) < 0:
+        raise ValueError("need M, N, K >= 0 and K even")
+    a = _bytes2d(A_packed, M, K // 2, "A_packed")
+    b = _bytes2d(B_packed, N, K // 2, "B_packed")
+    C = np.zeros((M, N), dtype=np.int32)
+    _check(_load().oracle_gemm_i4i4(_ptr(a), _ptr(b), M, N, K, _ptr(C)), "gemm_i4i4")
+    return C
+
+
+def gemm_w4a8(A, B_packed, M: int, N: int, K: int) -> np.ndarray:
+    """W4A8: C[M,N] int32 = A . B^T from int8 A [M,K] and packed B [N,K/2]."""
+    if K % 2 or min(M, N, K) < 0:
+        raise ValueError("need M, N, K >= 0 and K even")
+    a = _bytes2d(A, M, K, "A")
+    b = _bytes2d(B_packed, N, K // 2, "B_packed")
+    C = np.zeros((M, N), dtype=np.int32)
+    _check(_load().oracle_gemm_w4a8(_ptr(a), _ptr(b), M, N, K, _ptr(C)), "gemm_w4a8")
+    return C
+
+
+def _at(fn, a, b, M, N, K, ms, ns, what):
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    if ms.shape != ns.shape:
+        raise ValueError("ms and ns must have the same shape")
+    out = np.zeros(ms.shape, dtype=np.int32)
+    _check(fn(_ptr(a), _ptr(b), M, N, K, _ptr(ms), _ptr(ns), ms.size, _ptr(out)), what)
+    return out
+
+
+def gemm_i4i4_at(A_packed, B_packed, M: int, N: int, K: int, ms, ns) -> np.ndarray:
+    """Elements C[ms[i], ns[i]] of the int4 x int4 product, each computed alone."""
+    a = _bytes2d(A_packed, M, K // 2, "A_packed")
+    b = _bytes2d(B_packed, N, K // 2, "B_packed")
+    return _at(_load().oracle_gemm_i4i4_at, a, b, M, N, K, ms, ns, "gemm_i4i4_at")
+
+
+def gemm_w4a8_at(A, B_packed, M: int, N: int, K: int, ms, ns) -> np.ndarray:
+    """Elements C[ms[i], ns[i]] of the W4A8 product, each computed alone."""
+    a = _bytes2d(A, M, K, "A")
+    b = _bytes2d(B_packed, N, K // 2, "B_packed")
+    return _at(_load().oracle_gemm_w4a8_at, a, b, M, N, K, ms, ns, "gemm_w4a8_at")

@@ -1,0 +1,209 @@
+/*
+ * lpgemm_oracle.c -- plain CPU oracle for the low-precision integer GEMM
+ *
+ *     C[M,N] = A[M,K] . B[N,K]^T      (exact integer result, stored as int32)
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only the test-suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load this library.  It
+ * shares no code, header, table or constant with the GPU library: it is the
+ * written-out definition the GPU results are compared against, bit for bit.
+ *
+ * Sources (web pages; cited by title and the passage used):
+ *  [int4-gemm]  tilelang pull request "[CUDA] Support int4 T.gemm" (#2063),
+ *               example "gemm_int4": matmul_nt_int4 -- A[M,K] and B[N,K] int4,
+ *               C[M,N] int32, T.gemm(..., transpose_B=True), i.e. C = A . B^T.
+ *  [w4a8]       tilelang pull request "[Example] add w4a8 gemm kernel" (#815),
+ *               review threads on torch_convert (byte j//2, nibble j%2; the
+ *               vectorised rewrite: low = b & 0x0F, high = b >> 4, subtract 16
+ *               when the 4-bit value is >= 8, interleave low then high),
+ *               ref_program (C = A . B^T of int8 A and the unpacked B; the
+ *               reviewers ask for an integer, not a float, reference) and the
+ *               kernel's in_dtype int8 / accum_dtype int32.
+ *  [tutorial]   TileLang tutorial, chapter 14 section 5 "low_precision_gemm.py":
+ *               matmul_int4 (int4 operands, int32 accumulator, two nibbles per
+ *               byte) and pack_int4 (byte = (x[2j] & 0xF) | ((x[2j+1] & 0xF) << 4),
+ *               last dimension must be even).
+ *
+ * Every routine is the plain definition: unpack each operand once into int8,
+ * then a triple loop m, n, k accumulating in int64.  The outer m loop is split
+ * across OpenMP threads; nothing else is reordered, blocked or fused.  The sum
+ * is checked to fit int32 before it is stored (the pages store int32).
+ *
+ * Return codes: 0 ok, 1 bad argument (negative size, odd K, null pointer),
+ * 2 a result outside int32, 3 out of host memory.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_RANGE 2
+#define ORACLE_ERR_NOMEM 3
+
+/* The 4-bit field holding logical element k of a packed row: element k lives
+ * in byte k/2; even k in the low nibble, odd k in the high nibble ([w4a8]
+ * torch_convert indexes byte j//2, nibble j%2; [tutorial] pack_int4 puts
+ * x[0::2] low and x[1::2] high).  The byte is read as unsigned. */
+static unsigned nibble_of(const uint8_t *row, int64_t k)
+{
+    uint8_t byte = row[k / 2];
+    return (k % 2 == 0) ? (unsigned)(byte & 0x0Fu) : (unsigned)(byte >> 4);
+}
+
+/* Two's-complement value of a 4-bit field: subtract 16 when the field is 8 or
+ * more ([w4a8], the vectorised torch_convert). */
+static int int4_value(unsigned field)
+{
+    return (int)field - (field >= 8u ? 16 : 0);
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Unpack rows x K logical int4 from packed bytes [rows][K/2] into int8 [rows][K]. */
+int oracle_unpack_int4(const uint8_t *packed, int64_t rows, int64_t K, int8_t *out)
+{
+    if (rows < 0 || K < 0 || K % 2 != 0) return ORACLE_ERR_ARG;
+    if (rows * K > 0 && (packed == NULL || out == NULL)) return ORACLE_ERR_ARG;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint8_t *src = packed + r * (K / 2);
+        for (int64_t k = 0; k < K; ++k)
+            out[r * K + k] = (int8_t)int4_value(nibble_of(src, k));
+    }
+    return ORACLE_OK;
+}
+
+/* Pack rows x K logical int4 (held as int8) into bytes [rows][K/2]:
+ * byte j = (x[2j] & 0xF) | ((x[2j+1] & 0xF) << 4)   ([tutorial] pack_int4).
+ * Like the page's packer it keeps only the low four bits of each value. */
+int oracle_pack_int4(const int8_t *logical, int64_t rows, int64_t K, uint8_t *out)
+{
+    if (rows < 0 || K < 0 || K % 2 != 0) return ORACLE_ERR_ARG;
+    if (rows * K > 0 && (logical == NULL || out == NULL)) return ORACLE_ERR_ARG;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int8_t *x = logical + r * K;
+        for (int64_t j = 0; j < K / 2; ++j) {
+            unsigned even = (unsigned)(uint8_t)x[2 * j] & 0x0Fu;
+            unsigned odd = (unsigned)(uint8_t)x[2 * j + 1] & 0x0Fu;
+            out[r * (K / 2) + j] = (uint8_t)(even | (odd << 4));
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* C[m][n] = sum_k a[m][k] * b[n][k] over int8 rows, int64 accumulation. */
+static int gemm_rows_int8(const int8_t *a, const int8_t *b, int64_t M, int64_t N, int64_t K,
+                          int32_t *C)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        const int8_t *arow = a + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const int8_t *brow = b + n * K;
+            int64_t sum = 0;
+            for (int64_t k = 0; k < K; ++k)
+                sum += (int64_t)arow[k] * (int64_t)brow[k];
+            if (sum < INT32_MIN || sum > INT32_MAX) bad = 1;
+            C[m * N + n] = (int32_t)sum;
+        }
+    }
+    return bad ? ORACLE_ERR_RANGE : ORACLE_OK;
+}
+
+static int check_dims(int64_t M, int64_t N, int64_t K)
+{
+    return (M < 0 || N < 0 || K < 0 || K % 2 != 0) ? ORACLE_ERR_ARG : ORACLE_OK;
+}
+
+/* int4 x int4: A packed [M][K/2], B packed [N][K/2], C int32 [M][N]
+ * ([int4-gemm] matmul_nt_int4; [tutorial] matmul_int4). */
+int oracle_gemm_i4i4(const uint8_t *Ap, const uint8_t *Bp, int64_t M, int64_t N, int64_t K,
+                     int32_t *C)
+{
+    int rc = check_dims(M, N, K);
+    if (rc) return rc;
+    if (M * N == 0) return ORACLE_OK;
+    if (C == NULL || (K > 0 && (Ap == NULL || Bp == NULL))) return ORACLE_ERR_ARG;
+    int8_t *a = (int8_t *)malloc((size_t)(M * K > 0 ? M * K : 1));
+    int8_t *b = (int8_t *)malloc((size_t)(N * K > 0 ? N * K : 1));
+    if (a == NULL || b == NULL) { free(a); free(b); return ORACLE_ERR_NOMEM; }
+    oracle_unpack_int4(Ap, M, K, a);
+    oracle_unpack_int4(Bp, N, K, b);
+    rc = gemm_rows_int8(a, b, M, N, K, C);
+    free(a);
+    free(b);
+    return rc;
+}
+
+/* W4A8: A int8 [M][K], B packed int4 [N][K/2], C int32 [M][N]
+ * ([w4a8] ref_program: A . B^T with B unpacked by torch_convert). */
+int oracle_gemm_w4a8(const int8_t *A, const uint8_t *Bp, int64_t M, int64_t N, int64_t K,
+                     int32_t *C)
+{
+    int rc = check_dims(M, N, K);
+    if (rc) return rc;
+    if (M * N == 0) return ORACLE_OK;
+    if (C == NULL || (K > 0 && (A == NULL || Bp == NULL))) return ORACLE_ERR_ARG;
+    int8_t *b = (int8_t *)malloc((size_t)(N * K > 0 ? N * K : 1));
+    if (b == NULL) return ORACLE_ERR_NOMEM;
+    oracle_unpack_int4(Bp, N, K, b);
+    rc = gemm_rows_int8(A, b, M, N, K, C);
+    free(b);
+    return rc;
+}
+
+/* Selected elements one by one, straight from the packed bytes: out[i] =
+ * C[ms[i]][ns[i]].  For shapes too large for the full triple loop. */
+int oracle_gemm_i4i4_at(const uint8_t *Ap, const uint8_t *Bp, int64_t M, int64_t N, int64_t K,
+                        const int64_t *ms, const int64_t *ns, int64_t count, int32_t *out)
+{
+    int rc = check_dims(M, N, K);
+    if (rc) return rc;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        if (m < 0 || m >= M || n < 0 || n >= N) { bad |= 2; continue; }
+        const uint8_t *arow = Ap + m * (K / 2);
+        const uint8_t *brow = Bp + n * (K / 2);
+        int64_t sum = 0;
+        for (int64_t k = 0; k < K; ++k)
+            sum += (int64_t)int4_value(nibble_of(arow, k)) * int4_value(nibble_of(brow, k));
+        if (sum < INT32_MIN || sum > INT32_MAX) bad |= 1;
+        out[i] = (int32_t)sum;
+    }
+    if (bad & 2) return ORACLE_ERR_ARG;
+    return bad ? ORACLE_ERR_RANGE : ORACLE_OK;
+}
+
+int oracle_gemm_w4a8_at(const int8_t *A, const uint8_t *Bp, int64_t M, int64_t N, int64_t K,
+                        const int64_t *ms, const int64_t *ns, int64_t count, int32_t *out)
+{
+    int rc = check_dims(M, N, K);
+    if (rc) return rc;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        if (m < 0 || m >= M || n < 0 || n >= N) { bad |= 2; continue; }
+        const int8_t *arow = A + m * K;
+        const uint8_t *brow = Bp + n * (K / 2);
+        int64_t sum = 0;
+        for (int64_t k = 0; k < K; ++k)
+            sum += (int64_t)arow[k] * int4_value(nibble_of(brow, k));
+        if (sum < INT32_MIN || sum > INT32_MAX) bad |= 1;
+        out[i] = (int32_t)sum;
+    }
+    if (bad & 2) return ORACLE_ERR_ARG;
+    return bad ? ORACLE_ERR_RANGE : ORACLE_OK;
+}

@@ -1,0 +1,112 @@
+"""Seeded synthetic inputs for the low-precision GEMM workloads.
+
+This module only draws random bytes; it holds none of the GEMM's arithmetic
+(no packing, unpacking or products).  Both the GPU path and the CPU oracle are
+fed the bytes it returns.
+
+Generator: SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom
+number generators", OOPSLA 2014), used counter-style: output i of stream s is
+mix(s + (i + 1) * 0x9E3779B97F4A7C15) with the published mix function.  Each
+64-bit output gives 8 bytes, least significant first.
+
+Value distributions follow the pages' workloads:
+  * an int8 operand is uniform over [-128, 127]: one random byte per element;
+  * a packed int4 operand holds logical values uniform over [-8, 7] (the
+    tutorial draws randint(-8, 8)); since every 4-bit pattern is one of the 16
+    values, independent uniform nibbles are exactly uniform random bytes, so
+    the packed bytes are drawn directly, both nibbles of every byte populated.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+
+
+def splitmix64(stream: int, count: int, start: int = 0) -> np.ndarray:
+    """Outputs start .. start+count-1 of SplitMix64 seeded with `stream`."""
+    with np.errstate(over="ignore"):
+        i = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+        z = np.uint64(stream & 0xFFFFFFFFFFFFFFFF) + i * _GOLDEN
+        z = (z ^ (z >> np.uint64(30))) * _M1
+        z = (z ^ (z >> np.uint64(27))) * _M2
+        return z ^ (z >> np.uint64(31))
+
+
+def random_bytes(stream: int, nbytes: int) -> np.ndarray:
+    """`nbytes` uniform random bytes (uint8) from SplitMix64 stream `stream`."""
+    words = splitmix64(stream, (nbytes + 7) // 8)
+    return words.astype("<u8").view(np.uint8)[:nbytes].copy()
+
+
+def operand_stream(seed: int, operand: int) -> int:
+    """Stream id of operand 0 (A) or 1 (B) of the case seeded `seed`."""
+    return (seed << 8) | operand
+
+
+@dataclass(frozen=True)
+class Case:
+    name: str
+    variant: str  # "i4i4" or "w4a8"
+    M: int
+    N: int
+    K: int
+    seed: int
+    a_rows_from: str | None = None  # reuse another case's A rows (prefix)
+
+    @property
+    def ops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def a_bytes(self) -> int:
+        return self.M * (self.K // 2 if self.variant == "i4i4" else self.K)
+
+    @property
+    def b_bytes(self) -> int:
+        return self.N * self.K // 2
+
+    @property
+    def c_bytes(self) -> int:
+        return 4 * self.M * self.N
+
+    @property
+    def alg_bytes(self) -> int:
+        return self.a_bytes + self.b_bytes + self.c_bytes
+
+
+# The workloads: shapes and value distributions of the pages' examples (the
+# int4 example's default 1024^3, square compute-bound shapes, a decode-like
+# skinny W4A8 shape and a ragged one).  Seeds are the case numbers.
+CASES = {
+    "i4i4_256": Case("i4i4_256", "i4i4", 256, 256, 256, 1),
+    "i4i4_1024": Case("i4i4_1024", "i4i4", 1024, 1024, 1024, 2),
+    "w4a8_4096": Case("w4a8_4096", "w4a8", 4096, 4096, 4096, 3),
+    "w4a8_skinny_m16": Case("w4a8_skinny_m16", "w4a8", 16, 28672, 8192, 4),
+    "w4a8_skinny_m1": Case("w4a8_skinny_m1", "w4a8", 1, 28672, 8192, 4,
+                           a_rows_from="w4a8_skinny_m16"),
+    "i4i4_8192": Case("i4i4_8192", "i4i4", 8192, 8192, 8192, 5),
+    "i4i4_ragged": Case("i4i4_ragged", "i4i4", 3000, 5120, 6144, 6),
+}
+
+
+def operands(case: Case) -> tuple[np.ndarray, np.ndarray]:
+    """Host bytes (A, B) of a case: A is int8 [M,K] (w4a8) or packed uint8
+    [M,K/2] (i4i4); B is packed uint8 [N,K/2].  A case with `a_rows_from`
+    takes the first M rows of that case's A and the same B (same seed)."""
+    a_row_bytes = case.K // 2 if case.variant == "i4i4" else case.K
+    a = random_bytes(operand_stream(case.seed, 0), case.M * a_row_bytes)
+    a = a.reshape(case.M, a_row_bytes)
+    if case.variant == "w4a8":
+        a = a.view(np.int8)
+    b = random_bytes(operand_stream(case.seed, 1), case.N * case.K // 2)
+    return a, b.reshape(case.N, case.K // 2)
+
+
+def custom_operands(variant: str, M: int, N: int, K: int, seed: int):
+    """Operands of an ad-hoc shape (tests), drawn like the named cases."""
+    return operands(Case("custom", variant, M, N, K, seed))

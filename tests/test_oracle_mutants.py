@@ -1,0 +1,52 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins in test_oracle_pins.py catch every one of them."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (what the mistake is, text in the oracle, replacement)
+MUTANTS = [
+    ("nibble order swapped", "(k % 2 == 0) ? (unsigned)(byte & 0x0Fu)",
+     "(k % 2 == 1) ? (unsigned)(byte & 0x0Fu)"),
+    ("no sign extension", "return (int)field - (field >= 8u ? 16 : 0);", "return (int)field;"),
+    ("sign threshold 7", "field >= 8u ? 16 : 0", "field >= 7u ? 16 : 0"),
+    ("sign threshold 9", "field >= 8u ? 16 : 0", "field > 8u ? 16 : 0"),
+    ("last k term dropped",
+     "for (int64_t k = 0; k < K; ++k)\n                sum += (int64_t)arow[k] * (int64_t)brow[k];",
+     "for (int64_t k = 0; k + 1 < K; ++k)\n                sum += (int64_t)arow[k] * (int64_t)brow[k];"),
+    ("wrong B row", "const int8_t *brow = b + n * K;",
+     "const int8_t *brow = b + (n % (M > 0 ? M : 1)) * K;"),
+    ("int32 accumulator", "int64_t sum = 0;\n            for", "int32_t sum = 0;\n            for"),
+    ("pack nibbles swapped", "out[r * (K / 2) + j] = (uint8_t)(even | (odd << 4));",
+     "out[r * (K / 2) + j] = (uint8_t)(odd | (even << 4));"),
+    ("sampled w4a8 k order", "sum += (int64_t)arow[k] * int4_value(nibble_of(brow, k));",
+     "sum += (int64_t)arow[k] * int4_value(nibble_of(brow, k ^ 1));"),
+    ("sampled i4i4 drops k=0",
+     "sum += (int64_t)int4_value(nibble_of(arow, k)) * int4_value(nibble_of(brow, k));",
+     "sum += (int64_t)int4_value(nibble_of(arow, k)) * int4_value(nibble_of(brow, k)) * (k > 0);"),
+    ("output transposed", "C[m * N + n] = (int32_t)sum;", "C[n * M + m] = (int32_t)sum;"),
+    ("packed row stride", "const uint8_t *src = packed + r * (K / 2);",
+     "const uint8_t *src = packed + r * K / 2 + (r > 0);"),
+    ("range check removed", "if (sum < INT32_MIN || sum > INT32_MAX) bad = 1;", ";"),
+]
+
+
+@pytest.mark.parametrize("what,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, what, old, new):
+    for d in ("oracle", "tests", "precision_integer_gemm_amd"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("*.so", "__pycache__", "*.hip", "*.o"))
+    shutil.copy(os.path.join(ROOT, "pytest.ini"), tmp_path)
+    src = tmp_path / "oracle" / "lpgemm_oracle.c"
+    text = src.read_text()
+    assert old in text, f"mutation site for '{what}' not found"
+    src.write_text(text.replace(old, new, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-q", "-x",
+                        "-p", "no:cacheprovider"], cwd=tmp_path, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 0, f"pins did not catch: {what}\n{r.stdout[-2000:]}"
