@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the low-precision integer GEMM on one MI355X.
+
+One step = one call of every workload (the whole hot path: the block-tiled
+MFMA kernel for the square and ragged shapes, the narrow-M kernel for the
+decode-like W4A8 shapes):
+
+    i4i4 256^3, i4i4 1024^3, W4A8 4096^3, W4A8 16x28672x8192,
+    W4A8 1x28672x8192 (same B values, own copy), i4i4 8192^3,
+    i4i4 3000x5120x6144
+
+value = sum of 2*M*N*K over the step / wall time per step, in TOP/s.  Inputs
+are seeded synthetic bytes already resident in HBM when timing starts; each
+call writes its own int32 C.  Every launch is bracketed by HIP events on the
+stream it runs on; the per-launch averages give each workload's TOP/s and
+roofline fraction (`per_config`) and the dominant kernel's `roofline`.
+
+The CPU baseline times the oracle (plain C, OpenMP over rows) on the first
+rows of every workload, and those rows double as a bit-exact parity check of
+the GPU output.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--case NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks (dense): int8 MFMA 5.0 POP/s, HBM3E 8 TB/s.
+PEAK_INT8_TOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+# Step order: each W4A8 skinny call reads a B that no call has touched for
+# >= 300 MB of other traffic, so it streams from HBM, not the 256 MB MALL.
+STEP_ORDER = ["w4a8_skinny_m16", "i4i4_8192", "w4a8_skinny_m1", "w4a8_4096", "i4i4_ragged",
+              "i4i4_256", "i4i4_1024"]
+
+KERNEL_SYMBOL = {"tiled": "gemm_tiled_kernel", "skinny": "gemm_w4a8_skinny_kernel",
+                 "general": "gemm_general_kernel"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--case", action="append", default=None,
+                    help="restrict the step to these workloads (profiling)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline and parity rows")
+    ap.add_argument("--cpu-macs", type=float, default=2.5e10,
+                    help="multiply-accumulates per workload in the CPU baseline sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def roofline_time_s(case) -> tuple[float, str]:
+    t_mfma = case.ops / (PEAK_INT8_TOPS * 1e12)
+    t_hbm = case.alg_bytes / (PEAK_HBM_GBS * 1e9)
+    return (t_mfma, "mfma") if t_mfma >= t_hbm else (t_hbm, "hbm")
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the GEMM shards by N or M with no exchange, and this build runs and reports a "
+              "single GPU.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import precision_integer_gemm_amd as L
+    from precision_integer_gemm_amd.inputs import CASES, operands
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    L.lib()
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return 0
+
+    names = [n for n in STEP_ORDER if args.case is None or n in args.case]
+    work = []
+    for name in names:
+        c = CASES[name]
+        A, B = operands(c)
+        a = torch.from_numpy(np.ascontiguousarray(A).view(np.uint8)).to(dev)
+        b = torch.from_numpy(B).to(dev)  # each workload owns its B copy
+        C = torch.empty((c.M, c.N), dtype=torch.int32, device=dev)
+        fn = L.lib().lpgemm_int4_int4 if c.variant == "i4i4" else L.lib().lpgemm_w4a8
+        variant = L.VARIANT_I4I4 if c.variant == "i4i4" else L.VARIANT_W4A8
+        plan = L.lpgemm_plan(variant, c.M, c.N, c.K, a.data_ptr(), b.data_ptr(), C.data_ptr())
+        work.append(dict(case=c, A=A, B=B, a=a, b=b, C=C, fn=fn, plan=plan))
+        print(f"# {name}: {c.variant} {c.M}x{c.N}x{c.K} plan {plan}", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+
+    def call(w):
+        c = w["case"]
+        st = w["fn"](w["a"].data_ptr(), w["b"].data_ptr(), w["C"].data_ptr(), c.M, c.N, c.K, handle)
+        if st != L.OK:
+            raise RuntimeError(f"{c.name}: {L.lpgemm_status_string(st)}")
+
+    for _ in range(args.warmup):
+        for w in work:
+            call(w)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in work] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, w in enumerate(work):
+            events[s][i][0].record(stream)
+            call(w)
+            events[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"# timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    ops_step = sum(w["case"].ops for w in work)
+    per_config = {}
+    dominant = None
+    for i, w in enumerate(work):
+        c = w["case"]
+        us = np.array([events[s][i][0].elapsed_time(events[s][i][1]) * 1e3
+                       for s in range(args.steps)])
+        avg = float(us.mean())
+        t_roof, bound = roofline_time_s(c)
+        rec = {"kernel": w["plan"]["kernel"], "avg_us": round(avg, 3),
+               "median_us": round(float(np.median(us)), 3), "min_us": round(float(us.min()), 3),
+               "tops": round(c.ops / (avg * 1e-6) / 1e12, 2),
+               "gbs": round(c.alg_bytes / (avg * 1e-6) / 1e9, 1),
+               "bound": bound, "roofline_frac": round(t_roof / (avg * 1e-6), 4)}
+        per_config[c.name] = rec
+        total = avg * args.steps
+        if dominant is None or total > dominant[0]:
+            dominant = (total, c, rec, avg)
+
+    _, dc, drec, davg = dominant
+    if drec["bound"] == "mfma":
+        achieved = dc.ops / (davg * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
+    else:
+        achieved = dc.alg_bytes / (davg * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof.update({"traffic": None, "kernel": KERNEL_SYMBOL[drec["kernel"]], "workload": dc.name,
+                 "avg_us": round(davg, 3)})
+
+    result = {
+        "metric": "int4/W4A8 GEMM TOPS (2MNK/s) and % of int8 MFMA or HBM roofline, 1 GPU",
+        "value": round(ops_step * args.steps / wall / 1e12, 2),
+        "unit": "TOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8-mfma/int32 (int4 and int8 operands)",
+        "data": "synthetic (seeded SplitMix64 bytes: uniform int8, uniform int4 nibbles)",
+        "config": {"workload": "lpgemm suite: " + ", ".join(w["case"].name for w in work),
+                   "cases": {w["case"].name: [w["case"].variant, w["case"].M, w["case"].N,
+                                              w["case"].K] for w in work},
+                   "ops_per_step": ops_step, "parallelism": "single GPU"},
+        "roofline": roof,
+        "per_config": per_config,
+    }
+
+    if not args.no_cpu:
+        import oracle
+
+        total_ops, total_t, parity_ok, sample = 0.0, 0.0, True, []
+        for w in work:
+            c = w["case"]
+            rows = int(max(1, min(c.M, args.cpu_macs // (c.N * c.K))))
+            a_rows = w["A"][:rows]
+            t = time.perf_counter()
+            if c.variant == "i4i4":
+                ref = oracle.gemm_i4i4(a_rows, w["B"], rows, c.N, c.K)
+            else:
+                ref = oracle.gemm_w4a8(a_rows, w["B"], rows, c.N, c.K)
+            dt = time.perf_counter() - t
+            total_ops += 2.0 * rows * c.N * c.K
+            total_t += dt
+            got = w["C"][:rows].cpu().numpy()
+            parity_ok &= bool(np.array_equal(got, ref))
+            sample.append(f"{c.name}[:{rows}]")
+            print(f"# cpu oracle {c.name} rows {rows}: {dt:.2f} s, parity "
+                  f"{np.array_equal(got, ref)}", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = {
+            "value": round(total_ops / total_t / 1e12, 5), "unit": "TOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "first rows of every workload (" + ", ".join(sample) +
+                      f"), {total_t:.1f} s of CPU time"}
+        result["parity_sampled_rows"] = parity_ok
+
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,163 @@
+/*
+ * lpgemm.h -- low-precision integer GEMM for AMD Instinct MI355X (gfx950)
+ *
+ *     C[M,N] = A[M,K] . B[N,K]^T     exact, int32 result
+ *
+ * Two operand formats, both "NT" (every operand row is contiguous along K):
+ *
+ *   int4 x int4  both A and B are signed 4-bit values packed two per byte.
+ *   W4A8         A is int8, B is packed signed 4-bit.
+ *
+ * Packing (both pages that define it agree): logical element k of a row lives
+ * in byte k/2 of that row; even k in the low nibble, odd k in the high nibble;
+ * each nibble is a two's-complement value in [-8, 7].  A packed row of K
+ * logical elements therefore occupies K/2 bytes, and K must be even.
+ *   - TileLang tutorial, ch. 14 sec. 5 "low_precision_gemm.py": pack_int4
+ *     (byte = (x[2j] & 0xF) | ((x[2j+1] & 0xF) << 4); odd last dim rejected)
+ *     and matmul_int4 (int4 operands, int32 accumulator).
+ *   - tilelang PR "[Example] add w4a8 gemm kernel" (#815): torch_convert
+ *     (byte j//2, nibble j%2, sign-extended) and ref_program (C = A . B^T of
+ *     int8 A and the unpacked int4 B); K given to the kernel is the logical,
+ *     unpacked length.
+ *   - tilelang PR "[CUDA] Support int4 T.gemm" (#2063), example gemm_int4:
+ *     matmul_nt_int4, A[M,K] and B[N,K] int4, C[M,N] int32,
+ *     T.gemm(A, B, C, transpose_B=True).
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no memory and keeps no pointer after the call returns.
+ *   - Matrices are dense and row-major with no padding: A row stride is K/2
+ *     bytes (packed) or K bytes (int8), B row stride K/2 bytes, C row stride
+ *     N int32.
+ *   - C is overwritten (no alpha/beta) and must not overlap A or B.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  A return of
+ *     LPGEMM_OK means the work was validated and enqueued; faults during
+ *     execution surface at the caller's next synchronisation.
+ *   - Argument checks happen on the host before any HIP call, so an invalid
+ *     call touches no device state.
+ *   - Calls are thread-safe.  Any alignment is accepted; 16-byte aligned
+ *     bases with K a multiple of 32 take the fast kernels, anything else a
+ *     slower general kernel with the same results.
+ *   - Exactness: the kernels pre-scale 4-bit values by 16 inside int32, which
+ *     is exact while 16384*K < 2^31, i.e. K <= 131070.  Larger K returns
+ *     LPGEMM_ERR_UNSUPPORTED.  Within that range every result fits int32
+ *     (|C| <= 64*K for int4 x int4, <= 1024*K for W4A8).
+ */
+#ifndef LPGEMM_H
+#define LPGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lpgemm_status {
+    LPGEMM_OK = 0,
+    LPGEMM_ERR_INVALID_ARG = 1, /* negative size, odd K, null pointer, bad enum  */
+    LPGEMM_ERR_UNSUPPORTED = 2, /* valid request the library cannot serve        */
+    LPGEMM_ERR_HIP = 3          /* the HIP runtime reported an error at launch   */
+} lpgemm_status;
+
+/* Largest supported K (logical elements); see "Exactness" above. */
+#define LPGEMM_MAX_K 131070
+
+/*
+ * int4 x int4:  C[m][n] = sum_k a(m,k) * b(n,k)
+ *   A_packed  device, bytes [M][K/2] (int8 or uint8 storage, same bits)
+ *   B_packed  device, bytes [N][K/2]
+ *   C         device, int32 [M][N], written
+ *   M, N, K   logical sizes; K even, 0 <= K <= LPGEMM_MAX_K
+ * Returns LPGEMM_OK (also for M == 0 or N == 0: nothing is done; K == 0
+ * writes zeros), LPGEMM_ERR_INVALID_ARG for negative sizes, odd K or a null
+ * pointer that would be dereferenced, LPGEMM_ERR_UNSUPPORTED for K above the
+ * limit, LPGEMM_ERR_HIP if the launch failed.
+ * Defined by the int4 GEMM example of "[CUDA] Support int4 T.gemm" and the
+ * tutorial's matmul_int4 with its pack_int4 layout.
+ */
+lpgemm_status lpgemm_int4_int4(const void *A_packed, const void *B_packed, int32_t *C,
+                               int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * W4A8:  C[m][n] = sum_k A[m][k] * b(n,k)
+ *   A         device, int8 [M][K]
+ *   B_packed  device, bytes [N][K/2], nibbles sign-extended on unpack
+ *   C         device, int32 [M][N], written
+ * Sizes, return codes and behaviour as for lpgemm_int4_int4.
+ * Defined by "[Example] add w4a8 gemm kernel": ref_program and the kernel's
+ * in_dtype int8 / accum_dtype int32 with the u8 -> i4 -> i8 unpack of B.
+ */
+lpgemm_status lpgemm_w4a8(const int8_t *A, const uint8_t *B_packed, int32_t *C,
+                          int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Pack logical int4 values (held one per int8) into bytes, on the device:
+ *   logical  device, int8 [rows][K], each value in [-8, 7] (only the low four
+ *            bits of each value are kept, as the tutorial's pack_int4 does)
+ *   packed   device, bytes [rows][K/2], written
+ * K must be even (LPGEMM_ERR_INVALID_ARG otherwise, as pack_int4 raises on an
+ * odd last dimension).  The tutorial's pack_int4 defines the layout.
+ */
+lpgemm_status lpgemm_pack_int4(const int8_t *logical, uint8_t *packed, int64_t rows, int64_t K,
+                               hipStream_t stream);
+
+/*
+ * Unpack bytes into logical int4 values, one per int8, sign-extended:
+ *   packed   device, bytes [rows][K/2]
+ *   logical  device, int8 [rows][K], written
+ * The dequantise-only test kernel of "[Example] add w4a8 gemm kernel"
+ * (u8 -> i4 -> i8 of byte j//2, nibble j%2) defines the operation.
+ */
+lpgemm_status lpgemm_unpack_int4(const uint8_t *packed, int8_t *logical, int64_t rows, int64_t K,
+                                 hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *lpgemm_status_string(lpgemm_status status);
+
+/* ---- kernel selection: host-only, for tests and measurement -------------- */
+
+typedef enum lpgemm_kernel {
+    LPGEMM_KERNEL_AUTO = 0,    /* choose by shape and alignment (default)        */
+    LPGEMM_KERNEL_GENERAL = 1, /* any shape and alignment; slow                  */
+    LPGEMM_KERNEL_TILED = 2,   /* block-tiled MFMA kernel for large M             */
+    LPGEMM_KERNEL_SKINNY = 3   /* W4A8 narrow-M kernel streaming B once          */
+} lpgemm_kernel;
+
+typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
+
+/* How a call would be executed. */
+typedef struct lpgemm_plan_info {
+    int32_t kernel;        /* lpgemm_kernel actually used                        */
+    int32_t tile_m;        /* output rows per workgroup                          */
+    int32_t tile_n;        /* output columns per workgroup                       */
+    int32_t k_split;       /* waves that split K inside one workgroup (skinny)   */
+    int64_t workgroups;    /* workgroups launched                                */
+    int32_t threads;       /* threads per workgroup                              */
+    int32_t reserved;
+} lpgemm_plan_info;
+
+/*
+ * Fill *info with the kernel and launch shape a call with these arguments
+ * would use, without touching the device (pointers are only inspected for
+ * alignment).  `cu_count` is the number of compute units to plan for (0 =
+ * 256, an MI355X).  Returns what the call would return for argument errors,
+ * LPGEMM_ERR_UNSUPPORTED if a forced kernel cannot run this shape.
+ */
+lpgemm_status lpgemm_plan(lpgemm_variant variant, const void *A, const void *B, const void *C,
+                          int64_t M, int64_t N, int64_t K, int32_t cu_count,
+                          lpgemm_plan_info *info);
+
+/*
+ * Force a kernel for every later call in this process (LPGEMM_KERNEL_AUTO
+ * restores the default).  A forced kernel that cannot serve a shape makes the
+ * call return LPGEMM_ERR_UNSUPPORTED.  Returns LPGEMM_ERR_INVALID_ARG for an
+ * unknown value.  Meant for tests and benchmarks.
+ */
+lpgemm_status lpgemm_set_kernel_override(lpgemm_kernel kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LPGEMM_H */

@@ -1,0 +1,15 @@
+"""lpgemm -- exact low-precision integer GEMM for AMD MI355X (gfx950).
+
+    C[M,N] = A[M,K] . B[N,K]^T   (int32), A and B int4 packed two per byte
+                                  (int4 x int4) or A int8 with B packed (W4A8).
+
+The computation runs in hand-written HIP kernels behind a C ABI
+(include/lpgemm.h, built into _lpgemm.so); this package is the thin Python
+binding with the same entry-point names.  PyTorch provides device memory and
+streams only.
+"""
+from ._binding import (  # noqa: F401
+    ERR_HIP, ERR_INVALID_ARG, ERR_UNSUPPORTED, EXPORTS, KERNEL_AUTO, KERNEL_GENERAL,
+    KERNEL_NAMES, KERNEL_SKINNY, KERNEL_TILED, LIB_PATH, MAX_K, OK, VARIANT_I4I4,
+    VARIANT_W4A8, LpgemmError, lib, lpgemm_int4_int4, lpgemm_pack_int4, lpgemm_plan,
+    lpgemm_set_kernel_override, lpgemm_status_string, lpgemm_unpack_int4, lpgemm_w4a8)

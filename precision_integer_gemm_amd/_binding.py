@@ -1,0 +1,199 @@
+"""ctypes binding of the lpgemm C-ABI (include/lpgemm.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their device pointers and the current HIP stream are handed
+to the library.  Every step of the computation runs in the HIP kernels; there
+is no fallback of any kind, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lpgemm.so")
+
+# lpgemm_status
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+# lpgemm_kernel
+KERNEL_AUTO, KERNEL_GENERAL, KERNEL_TILED, KERNEL_SKINNY = 0, 1, 2, 3
+KERNEL_NAMES = {KERNEL_AUTO: "auto", KERNEL_GENERAL: "general", KERNEL_TILED: "tiled",
+                KERNEL_SKINNY: "skinny"}
+# lpgemm_variant
+VARIANT_I4I4, VARIANT_W4A8 = 0, 1
+MAX_K = 131070
+
+EXPORTS = ("lpgemm_int4_int4", "lpgemm_w4a8", "lpgemm_pack_int4", "lpgemm_unpack_int4",
+           "lpgemm_status_string", "lpgemm_plan", "lpgemm_set_kernel_override")
+
+
+class LpgemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lpgemm_status_string(status)} (status {status})")
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("k_split", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64), ("threads", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {"kernel": KERNEL_NAMES.get(self.kernel, self.kernel), "tile_m": self.tile_m,
+                "tile_n": self.tile_n, "k_split": self.k_split,
+                "workgroups": self.workgroups, "threads": self.threads}
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"the HIP library {LIB_PATH} is not built; run "
+                          "`python -m precision_integer_gemm_amd.build` (or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    for name in ("lpgemm_int4_int4", "lpgemm_w4a8"):
+        f = getattr(L, name)
+        f.argtypes = [p, p, p, i64, i64, i64, p]
+        f.restype = ctypes.c_int
+    for name in ("lpgemm_pack_int4", "lpgemm_unpack_int4"):
+        f = getattr(L, name)
+        f.argtypes = [p, p, i64, i64, p]
+        f.restype = ctypes.c_int
+    L.lpgemm_status_string.argtypes = [ctypes.c_int]
+    L.lpgemm_status_string.restype = ctypes.c_char_p
+    L.lpgemm_plan.argtypes = [ctypes.c_int, p, p, p, i64, i64, i64, i32, ctypes.POINTER(PlanInfo)]
+    L.lpgemm_plan.restype = ctypes.c_int
+    L.lpgemm_set_kernel_override.argtypes = [ctypes.c_int]
+    L.lpgemm_set_kernel_override.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def lpgemm_status_string(status: int) -> str:
+    return lib().lpgemm_status_string(int(status)).decode()
+
+
+def _raise(status: int, what: str) -> None:
+    if status != OK:
+        raise LpgemmError(status, what)
+
+
+def lpgemm_plan(variant: int, M: int, N: int, K: int, A: int = 256, B: int = 256, C: int = 256,
+                cu_count: int = 0) -> dict:
+    """Kernel and launch shape a call would use (host only; pointers are plain
+    integers, inspected only for alignment)."""
+    info = PlanInfo()
+    _raise(lib().lpgemm_plan(variant, A, B, C, M, N, K, cu_count, ctypes.byref(info)),
+           "lpgemm_plan")
+    return info.as_dict()
+
+
+def lpgemm_set_kernel_override(kernel: int) -> None:
+    _raise(lib().lpgemm_set_kernel_override(int(kernel)), "lpgemm_set_kernel_override")
+
+
+# ---- tensor-level calls ------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_dev(t, name: str, dtypes):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _out(out, M, N, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty((M, N), dtype=torch.int32, device=device)
+    _check_dev(out, "out", (torch.int32,))
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must have shape ({M}, {N}), got {tuple(out.shape)}")
+    return out
+
+
+def lpgemm_int4_int4(A_packed, B_packed, *, out=None, stream=None):
+    """C[M,N] int32 = A . B^T with both operands packed int4 ([M,K/2], [N,K/2])."""
+    torch = _torch()
+    _check_dev(A_packed, "A_packed", (torch.int8, torch.uint8))
+    _check_dev(B_packed, "B_packed", (torch.int8, torch.uint8))
+    M, half = A_packed.shape
+    N, half_b = B_packed.shape
+    if half != half_b:
+        raise ValueError(f"packed K mismatch: A has {half} bytes per row, B {half_b}")
+    C = _out(out, M, N, A_packed.device)
+    _raise(lib().lpgemm_int4_int4(A_packed.data_ptr(), B_packed.data_ptr(), C.data_ptr(),
+                                  M, N, 2 * half, _stream_handle(stream)), "lpgemm_int4_int4")
+    return C
+
+
+def lpgemm_w4a8(A, B_packed, *, out=None, stream=None):
+    """C[M,N] int32 = A . B^T with A int8 [M,K] and B packed int4 [N,K/2]."""
+    torch = _torch()
+    _check_dev(A, "A", (torch.int8,))
+    _check_dev(B_packed, "B_packed", (torch.uint8, torch.int8))
+    M, K = A.shape
+    N, half = B_packed.shape
+    if K != 2 * half:
+        raise ValueError(f"K mismatch: A has K={K}, B_packed holds {2 * half}")
+    C = _out(out, M, N, A.device)
+    _raise(lib().lpgemm_w4a8(A.data_ptr(), B_packed.data_ptr(), C.data_ptr(), M, N, K,
+                             _stream_handle(stream)), "lpgemm_w4a8")
+    return C
+
+
+def lpgemm_pack_int4(logical, *, out=None, stream=None):
+    """Logical int4 values held as int8 [rows, K] -> packed uint8 [rows, K/2]."""
+    torch = _torch()
+    _check_dev(logical, "logical", (torch.int8,))
+    rows, K = logical.shape
+    if K % 2:
+        raise ValueError("the last dimension of a logical int4 tensor must be even")
+    if out is None:
+        out = torch.empty((rows, K // 2), dtype=torch.uint8, device=logical.device)
+    else:
+        _check_dev(out, "out", (torch.uint8, torch.int8))
+        if tuple(out.shape) != (rows, K // 2):
+            raise ValueError("out has the wrong shape")
+    _raise(lib().lpgemm_pack_int4(logical.data_ptr(), out.data_ptr(), rows, K,
+                                  _stream_handle(stream)), "lpgemm_pack_int4")
+    return out
+
+
+def lpgemm_unpack_int4(packed, *, out=None, stream=None):
+    """Packed bytes [rows, K/2] -> logical int4 values as int8 [rows, K]."""
+    torch = _torch()
+    _check_dev(packed, "packed", (torch.uint8, torch.int8))
+    rows, half = packed.shape
+    if out is None:
+        out = torch.empty((rows, 2 * half), dtype=torch.int8, device=packed.device)
+    else:
+        _check_dev(out, "out", (torch.int8,))
+        if tuple(out.shape) != (rows, 2 * half):
+            raise ValueError("out has the wrong shape")
+    _raise(lib().lpgemm_unpack_int4(packed.data_ptr(), out.data_ptr(), rows, 2 * half,
+                                    _stream_handle(stream)), "lpgemm_unpack_int4")
+    return out

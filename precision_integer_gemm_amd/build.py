@@ -1,0 +1,54 @@
+"""Ahead-of-time build of the HIP library for gfx950 (MI355X).
+
+    python -m precision_integer_gemm_amd.build
+
+compiles csrc/lpgemm_api.hip (which includes every kernel) with hipcc into
+precision_integer_gemm_amd/_lpgemm.so, next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "lpgemm_api.hip")
+LIB = os.path.join(PKG, "_lpgemm.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the HIP library needs ROCm's hipcc")
+
+
+def command(out: str) -> list[str]:
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+        # packed fp32 VALU forms are kept out of the generated code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+        "-o", out, SRC,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    proc = subprocess.run(command(tmp), capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [l for l in (proc.stdout + proc.stderr).splitlines() if noise not in l]
+    if proc.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    sys.exit(0)

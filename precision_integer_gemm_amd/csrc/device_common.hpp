@@ -1,0 +1,96 @@
+// device_common.hpp -- register-level building blocks shared by the gfx950
+// GEMM kernels: int8 MFMA wrappers and the 4-bit -> int8 unpack.
+//
+// Unpack.  A packed byte holds logical element 2j in its low nibble and 2j+1
+// in its high nibble, each a two's-complement 4-bit value (the tutorial's
+// pack_int4; the w4a8 PR's torch_convert).  Instead of sign-extending each
+// nibble (the w4a8 PR's _tir_u8_to_i4_to_i8 shifts the field to the top of an
+// int8 and back), the kernels keep every nibble in the TOP half of its byte:
+//     byte & 0xF0         == 16 * (high nibble as signed int4)   (as an int8)
+//     (byte << 4) & 0xF0  == 16 * (low nibble as signed int4)
+// so a packed dword becomes two dwords of int8 operands in three or five VALU
+// operations, and every product carries an exact factor 16 (one 4-bit
+// operand) or 256 (two), removed by an arithmetic right shift in the
+// epilogue.  Each term is then at most 128*128 = 16384 in magnitude, so the
+// int32 accumulator is exact for K <= 131070.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lpgemm {
+
+// Operand formats: int4 x int4, or int8 A with packed int4 B.
+enum Variant { I4I4 = 0, W4A8 = 1 };
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+
+// D(32x32) += S0(32x32 rows, 32 k) * S1(32 k, 32 cols); S0 lane l: row l%32,
+// S1 lane l: column l%32, both the same 16 k chosen by l/32.  D lane l,
+// register r: row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+__device__ __forceinline__ i32x16 mfma_32x32x32(i32x4 s0, i32x4 s1, i32x16 acc)
+{
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(s0, s1, acc, 0, 0, 0);
+}
+
+// D(16x16) += S0(16 rows, 64 k) * S1(64 k, 16 cols); S0 lane l: row l%16,
+// S1 lane l: column l%16, both the same 16 k chosen by l/16.  D lane l,
+// register r: row 4*(l/16) + r, column l%16.
+__device__ __forceinline__ i32x4 mfma_16x16x64(i32x4 s0, i32x4 s1, i32x4 acc)
+{
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(s0, s1, acc, 0, 0, 0);
+}
+
+// Split order: 8 nibbles of `d` -> the 4 even-k values (x16) then the 4 odd-k
+// values (x16).  Used where both MFMA operands are 4-bit and so share the
+// same permutation of k, which leaves every dot product unchanged.
+__device__ __forceinline__ void unpack_x16_split(uint32_t d, uint32_t &even, uint32_t &odd)
+{
+    even = (d << 4) & 0xF0F0F0F0u;
+    odd = d & 0xF0F0F0F0u;
+}
+
+// Natural order: 8 nibbles of `d` (k0..k7) -> dword [k0 k1 k2 k3] and dword
+// [k4 k5 k6 k7], each value x16, matching an int8 operand read in k order.
+// v_perm_b32 picks bytes from the pair {hi: d, lo: d << 4}; selector values
+// 0-3 name bytes of the low dword, 4-7 bytes of the high dword.
+__device__ __forceinline__ void unpack_x16_natural(uint32_t d, uint32_t &k0123, uint32_t &k4567)
+{
+    const uint32_t y = d << 4;
+    k0123 = __builtin_amdgcn_perm(d, y, 0x05010400u) & 0xF0F0F0F0u;
+    k4567 = __builtin_amdgcn_perm(d, y, 0x07030602u) & 0xF0F0F0F0u;
+}
+
+// 16 packed bytes (32 logical k) -> two MFMA operands of 16 k each.
+template <bool NATURAL>
+__device__ __forceinline__ void unpack_chunk(const i32x4 q, i32x4 &lo16, i32x4 &hi16)
+{
+    uint32_t a, b, c, d, e, f, g, h;
+    if (NATURAL) {
+        unpack_x16_natural((uint32_t)q.x, a, b);
+        unpack_x16_natural((uint32_t)q.y, c, d);
+        unpack_x16_natural((uint32_t)q.z, e, f);
+        unpack_x16_natural((uint32_t)q.w, g, h);
+    } else {
+        unpack_x16_split((uint32_t)q.x, a, b);
+        unpack_x16_split((uint32_t)q.y, c, d);
+        unpack_x16_split((uint32_t)q.z, e, f);
+        unpack_x16_split((uint32_t)q.w, g, h);
+    }
+    lo16 = i32x4{(int32_t)a, (int32_t)b, (int32_t)c, (int32_t)d};
+    hi16 = i32x4{(int32_t)e, (int32_t)f, (int32_t)g, (int32_t)h};
+}
+
+// Sign-extended value of nibble `pos` (0 low, 1 high) of `byte`.
+__device__ __forceinline__ int32_t int4_at(uint32_t byte, uint32_t pos)
+{
+    return ((int32_t)(byte << (28 - 4 * pos))) >> 28;
+}
+
+__device__ __forceinline__ i32x4 load16(const void *p)
+{
+    return *reinterpret_cast<const i32x4 *>(p);
+}
+
+}  // namespace lpgemm

@@ -1,0 +1,76 @@
+// gemm_general.hpp -- kernels for shapes and layouts the fast paths do not
+// take (K not a multiple of 32, unaligned bases), the K == 0 fill, and the
+// device pack / unpack of 4-bit operands.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace lpgemm {
+
+// One thread per output element, bytes read one at a time: correct for any
+// even K and any alignment.  Sums fit int32 exactly (|C| <= 1024*K).
+template <int VAR>
+__global__ __launch_bounds__(256) void gemm_general_kernel(const uint8_t *__restrict__ A,
+                                                           const uint8_t *__restrict__ B,
+                                                           int32_t *__restrict__ C, int64_t M,
+                                                           int64_t N, int64_t K)
+{
+    const int64_t n = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
+    const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
+    if (m >= M || n >= N) return;
+    const int64_t half = K / 2;
+    const uint8_t *brow = B + n * half;
+    int32_t sum = 0;
+    if (VAR == I4I4) {
+        const uint8_t *arow = A + m * half;
+        for (int64_t j = 0; j < half; ++j) {
+            const uint32_t a = arow[j], b = brow[j];
+            sum += int4_at(a, 0) * int4_at(b, 0) + int4_at(a, 1) * int4_at(b, 1);
+        }
+    } else {
+        const int8_t *arow = reinterpret_cast<const int8_t *>(A) + m * K;
+        for (int64_t j = 0; j < half; ++j) {
+            const uint32_t b = brow[j];
+            sum += (int32_t)arow[2 * j] * int4_at(b, 0) + (int32_t)arow[2 * j + 1] * int4_at(b, 1);
+        }
+    }
+    C[m * N + n] = sum;
+}
+
+// C[0 .. count) = 0: the empty sum (K == 0).  A kernel, not a memset, so the
+// call stays capturable in a graph.
+__global__ __launch_bounds__(256) void fill_zero_kernel(int32_t *__restrict__ C, int64_t count)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
+        C[i] = 0;
+}
+
+// packed[r][j] = (x[r][2j] & 0xF) | ((x[r][2j+1] & 0xF) << 4), one thread per
+// output byte (grid-stride over rows * K/2).
+__global__ __launch_bounds__(256) void pack_int4_kernel(const int8_t *__restrict__ logical,
+                                                        uint8_t *__restrict__ packed,
+                                                        int64_t total_bytes)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_bytes; i += stride) {
+        const uint32_t even = (uint32_t)(uint8_t)logical[2 * i] & 0xFu;
+        const uint32_t odd = (uint32_t)(uint8_t)logical[2 * i + 1] & 0xFu;
+        packed[i] = (uint8_t)(even | (odd << 4));
+    }
+}
+
+// logical[r][2j + p] = sign-extended nibble p of packed[r][j].
+__global__ __launch_bounds__(256) void unpack_int4_kernel(const uint8_t *__restrict__ packed,
+                                                          int8_t *__restrict__ logical,
+                                                          int64_t total_bytes)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_bytes; i += stride) {
+        const uint32_t b = packed[i];
+        logical[2 * i] = (int8_t)int4_at(b, 0);
+        logical[2 * i + 1] = (int8_t)int4_at(b, 1);
+    }
+}
+
+}  // namespace lpgemm

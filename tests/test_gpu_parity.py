@@ -1,0 +1,210 @@
+"""Bit-exact parity of the HIP kernels with the CPU oracle (needs an MI355X).
+
+Every case feeds the same seeded bytes to the GPU (through the C-ABI binding)
+and to the oracle, and compares every output element; the largest shape is
+compared on sampled elements plus full rows and columns, and through row sums.
+C sits between guard bands pre-filled with a sentinel, so a write outside
+[0, M) x [0, N) or an element left unwritten fails the test.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import precision_integer_gemm_amd as L
+from precision_integer_gemm_amd.inputs import CASES, custom_operands, operands
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7EADBEEF
+GUARD = 1024  # int32 elements on each side of C (a multiple of 4: keeps C 16-byte aligned)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    L.lib()  # the HIP library must load; there is no fallback
+    return t
+
+
+@pytest.fixture(autouse=True)
+def _auto_kernel():
+    yield
+    L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
+
+
+def run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_AUTO, a_offset=0):
+    """Run one call through the C ABI; returns C as numpy and checks guards."""
+    dev = torch.device("cuda:0")
+    a_t = torch.from_numpy(np.ascontiguousarray(A).view(np.uint8).reshape(-1)).to(dev)
+    if a_offset:  # shift A to an unaligned address
+        buf = torch.zeros(a_t.numel() + a_offset, dtype=torch.uint8, device=dev)
+        buf[a_offset:] = a_t
+        a_t = buf[a_offset:]
+    b_t = torch.from_numpy(np.ascontiguousarray(B).reshape(-1)).to(dev)
+    cbuf = torch.full((M * N + 2 * GUARD,), SENTINEL, dtype=torch.int32, device=dev)
+    c_t = cbuf[GUARD:GUARD + M * N]
+    L.lpgemm_set_kernel_override(kernel)
+    fn = L.lib().lpgemm_int4_int4 if variant == "i4i4" else L.lib().lpgemm_w4a8
+    st = fn(a_t.data_ptr(), b_t.data_ptr(), c_t.data_ptr(), M, N, K,
+            torch.cuda.current_stream().cuda_stream)
+    assert st == L.OK, L.lpgemm_status_string(st)
+    torch.cuda.synchronize()
+    host = cbuf.cpu().numpy()
+    assert (host[:GUARD] == SENTINEL).all(), "write before C"
+    assert (host[GUARD + M * N:] == SENTINEL).all(), "write after C"
+    return host[GUARD:GUARD + M * N].reshape(M, N)
+
+
+def oracle_full(variant, A, B, M, N, K):
+    return (oracle.gemm_i4i4 if variant == "i4i4" else oracle.gemm_w4a8)(A, B, M, N, K)
+
+
+# ---- small and ragged shapes, every kernel that accepts them --------------------
+RAGGED = [(1, 1, 2), (3, 5, 2), (17, 33, 34), (37, 53, 86), (129, 255, 510), (5, 7, 66)]
+ALIGNED = [(1, 1, 32), (16, 64, 128), (17, 33, 64), (37, 53, 96), (129, 255, 512),
+           (130, 200, 160), (256, 256, 256), (300, 260, 1056), (255, 129, 4096)]
+SKINNY = [(1, 1, 32), (1, 31, 96), (2, 33, 160), (7, 100, 1056), (16, 1000, 4096),
+          (16, 64, 128), (13, 257, 8192)]
+
+
+@pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
+@pytest.mark.parametrize("M,N,K", RAGGED + ALIGNED)
+def test_general_kernel(torch, variant, M, N, K):
+    say(f"general {variant} {M}x{N}x{K}")
+    A, B = custom_operands(variant, M, N, K, seed=M * 7 + N)
+    got = run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_GENERAL)
+    assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
+
+
+@pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
+@pytest.mark.parametrize("M,N,K", ALIGNED)
+def test_tiled_kernel(torch, variant, M, N, K):
+    say(f"tiled {variant} {M}x{N}x{K}")
+    A, B = custom_operands(variant, M, N, K, seed=M * 5 + K)
+    got = run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_TILED)
+    assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY)
+def test_skinny_kernel(torch, M, N, K):
+    say(f"skinny w4a8 {M}x{N}x{K}")
+    A, B = custom_operands("w4a8", M, N, K, seed=M * 3 + N)
+    got = run_gpu(torch, "w4a8", A, B, M, N, K, kernel=L.KERNEL_SKINNY)
+    assert np.array_equal(got, oracle_full("w4a8", A, B, M, N, K))
+
+
+@pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
+def test_unaligned_operand_takes_general_path(torch, variant):
+    M, N, K = 40, 72, 256
+    say(f"unaligned {variant}")
+    A, B = custom_operands(variant, M, N, K, seed=77)
+    got = run_gpu(torch, variant, A, B, M, N, K, a_offset=3)
+    assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
+
+
+@pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
+def test_closed_form_extremes(torch, variant):
+    # all -8 (and A = -128): C = 64 K (i4i4) or 1024 K (w4a8) everywhere
+    M, N, K = 160, 144, 4096
+    say(f"extremes {variant}")
+    B = np.full((N, K // 2), 0x88, dtype=np.uint8)
+    if variant == "i4i4":
+        A, want = np.full((M, K // 2), 0x88, dtype=np.uint8), 64 * K
+    else:
+        A, want = np.full((M, K), -128, dtype=np.int8), 1024 * K
+    assert (run_gpu(torch, variant, A, B, M, N, K) == want).all()
+
+
+@pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
+def test_k_zero_writes_zeros_and_empty_is_noop(torch, variant):
+    say(f"k0 {variant}")
+    empty = np.zeros((5, 0), dtype=np.uint8 if variant == "i4i4" else np.int8)
+    got = run_gpu(torch, variant, empty, np.zeros((7, 0), np.uint8), 5, 7, 0)
+    assert not got.any()
+    dev = torch.device("cuda:0")
+    C = torch.full((0, 9), 1, dtype=torch.int32, device=dev)
+    fn = L.lpgemm_int4_int4 if variant == "i4i4" else L.lpgemm_w4a8
+    A = torch.zeros((0, 16), dtype=torch.int8, device=dev)
+    assert fn(A, torch.zeros((9, 16 if variant == "i4i4" else 8), dtype=torch.int8 if variant == "i4i4" else torch.uint8,
+                             device=dev), out=C).shape == (0, 9)
+
+
+def test_deterministic_repeats(torch):
+    M, N, K = 300, 260, 1056
+    say("determinism")
+    A, B = custom_operands("w4a8", M, N, K, seed=5)
+    first = run_gpu(torch, "w4a8", A, B, M, N, K)
+    for _ in range(9):
+        assert np.array_equal(run_gpu(torch, "w4a8", A, B, M, N, K), first)
+
+
+# ---- the named workloads at full size, in the launch configuration the ----------
+# ---- benchmark times (automatic kernel selection) -------------------------------
+FULL = ["i4i4_256", "i4i4_1024", "w4a8_4096", "w4a8_skinny_m16", "w4a8_skinny_m1",
+        "i4i4_ragged"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_named_case_full_parity(torch, name):
+    c = CASES[name]
+    say(f"case {name}: {c.variant} {c.M}x{c.N}x{c.K} plan={L.lpgemm_plan(L.VARIANT_I4I4 if c.variant == 'i4i4' else L.VARIANT_W4A8, c.M, c.N, c.K)}")
+    A, B = operands(c)
+    got = run_gpu(torch, c.variant, A, B, c.M, c.N, c.K)
+    want = oracle_full(c.variant, A, B, c.M, c.N, c.K)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+
+
+def _np_unpack(packed):
+    b = np.ascontiguousarray(packed).view(np.uint8)
+    lo = ((b << 4).astype(np.uint8)).view(np.int8) >> 4
+    hi = b.view(np.int8) >> 4
+    return np.stack([lo, hi], axis=-1).reshape(b.shape[0], -1)
+
+
+def test_largest_case_sampled_rows_columns_and_row_sums(torch):
+    c = CASES["i4i4_8192"]
+    say(f"case {c.name}: sampled")
+    A, B = operands(c)
+    got = run_gpu(torch, c.variant, A, B, c.M, c.N, c.K)
+    rng = np.random.default_rng(2024)
+    # 8192 random elements, plus 8 whole rows and 8 whole columns (edges included)
+    ms = rng.integers(0, c.M, 8192)
+    ns = rng.integers(0, c.N, 8192)
+    rows = np.array([0, 1, 127, 128, 4095, 4096, c.M - 2, c.M - 1])
+    cols = np.array([0, 3, 255, 256, 5000, 8000, c.N - 4, c.N - 1])
+    ms = np.concatenate([ms, np.repeat(rows, c.N), np.tile(np.arange(c.M), len(cols))])
+    ns = np.concatenate([ns, np.tile(np.arange(c.N), len(rows)), np.repeat(cols, c.M)])
+    want = oracle.gemm_i4i4_at(A, B, c.M, c.N, c.K, ms, ns)
+    assert np.array_equal(got[ms, ns], want)
+    # every element through its row sum: sum_n C[m,n] = sum_k a(m,k) * sum_n b(n,k)
+    colsum_b = _np_unpack(B).astype(np.int64).sum(axis=0)
+    want_rows = _np_unpack(A).astype(np.int64) @ colsum_b
+    assert np.array_equal(got.astype(np.int64).sum(axis=1), want_rows)
+
+
+# ---- device pack / unpack ---------------------------------------------------------
+def test_device_pack_unpack_match_oracle(torch):
+    say("pack/unpack")
+    dev = torch.device("cuda:0")
+    rows, K = 333, 1030
+    packed = custom_operands("i4i4", rows, 1, K, seed=3)[0]
+    t = torch.from_numpy(packed).to(dev)
+    logical = L.lpgemm_unpack_int4(t)
+    torch.cuda.synchronize()
+    assert np.array_equal(logical.cpu().numpy(), oracle.unpack_int4(packed, K))
+    repacked = L.lpgemm_pack_int4(logical)
+    torch.cuda.synchronize()
+    assert np.array_equal(repacked.cpu().numpy(), packed)
+    allb = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    out = L.lpgemm_unpack_int4(torch.from_numpy(allb).to(dev)).cpu().numpy()
+    assert np.array_equal(out, oracle.unpack_int4(allb, 512))

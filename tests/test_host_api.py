@@ -1,0 +1,128 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every entry point include/lpgemm.h declares, rejects bad arguments before any
+HIP call, and plans the expected kernel for each shape."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_integer_gemm_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "lpgemm.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lpgemm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS), names
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), name
+
+
+def test_status_strings():
+    assert L.lpgemm_status_string(L.OK) == "ok"
+    assert L.lpgemm_status_string(L.ERR_INVALID_ARG) == "invalid argument"
+    assert L.lpgemm_status_string(L.ERR_UNSUPPORTED) == "unsupported"
+    assert L.lpgemm_status_string(L.ERR_HIP) == "HIP runtime error"
+    assert L.lpgemm_status_string(99) == "unknown status"
+
+
+# Arguments rejected on the host: none of these reaches the HIP runtime.
+P = 4096  # a fake, 16-byte aligned device address (never dereferenced here)
+BAD = [
+    ("negative M", (P, P, P, -1, 4, 32), L.ERR_INVALID_ARG),
+    ("negative N", (P, P, P, 4, -1, 32), L.ERR_INVALID_ARG),
+    ("negative K", (P, P, P, 4, 4, -2), L.ERR_INVALID_ARG),
+    ("odd K", (P, P, P, 4, 4, 33), L.ERR_INVALID_ARG),
+    ("K above the exact range", (P, P, P, 4, 4, L.MAX_K + 2), L.ERR_UNSUPPORTED),
+    ("null C", (P, P, None, 4, 4, 32), L.ERR_INVALID_ARG),
+    ("null A", (None, P, P, 4, 4, 32), L.ERR_INVALID_ARG),
+    ("null B", (P, None, P, 4, 4, 32), L.ERR_INVALID_ARG),
+    ("null C with K = 0", (None, None, None, 4, 4, 0), L.ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("fn", ["lpgemm_int4_int4", "lpgemm_w4a8"])
+@pytest.mark.parametrize("what,args,want", BAD, ids=[b[0] for b in BAD])
+def test_argument_errors(fn, what, args, want):
+    a, b, c, M, N, K = args
+    assert getattr(L.lib(), fn)(a, b, c, M, N, K, None) == want
+
+
+@pytest.mark.parametrize("fn", ["lpgemm_int4_int4", "lpgemm_w4a8"])
+def test_empty_outputs_are_a_no_op(fn):
+    f = getattr(L.lib(), fn)
+    assert f(None, None, None, 0, 5, 32, None) == L.OK
+    assert f(None, None, None, 5, 0, 32, None) == L.OK
+
+
+def test_max_k_is_the_exact_range_of_the_prescale():
+    # every x16-scaled term is at most 128*128 = 16384 in magnitude
+    assert 16384 * L.MAX_K <= 2**31 - 1 < 16384 * (L.MAX_K + 2)
+    assert L.MAX_K % 2 == 0
+
+
+def test_pack_unpack_argument_errors():
+    lib = L.lib()
+    assert lib.lpgemm_pack_int4(P, P, 2, 3, None) == L.ERR_INVALID_ARG
+    assert lib.lpgemm_pack_int4(P, P, -1, 4, None) == L.ERR_INVALID_ARG
+    assert lib.lpgemm_unpack_int4(None, P, 2, 4, None) == L.ERR_INVALID_ARG
+    assert lib.lpgemm_unpack_int4(None, None, 0, 4, None) == L.OK
+
+
+def test_kernel_override_rejects_unknown_values():
+    with pytest.raises(L.LpgemmError):
+        L.lpgemm_set_kernel_override(7)
+    L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
+
+
+# ---- planning -----------------------------------------------------------------
+@pytest.mark.parametrize("variant,M,N,K,kernel", [
+    (L.VARIANT_W4A8, 16, 28672, 8192, "skinny"),
+    (L.VARIANT_W4A8, 1, 28672, 8192, "skinny"),
+    (L.VARIANT_W4A8, 4096, 4096, 4096, "tiled"),
+    (L.VARIANT_I4I4, 8192, 8192, 8192, "tiled"),
+    (L.VARIANT_I4I4, 3000, 5120, 6144, "tiled"),
+    (L.VARIANT_I4I4, 256, 256, 256, "tiled"),
+    (L.VARIANT_I4I4, 17, 33, 34, "general"),     # K % 32 != 0
+    (L.VARIANT_W4A8, 16, 100, 34, "general"),
+])
+def test_auto_plan(variant, M, N, K, kernel):
+    assert L.lpgemm_plan(variant, M, N, K)["kernel"] == kernel
+
+
+def test_unaligned_pointers_take_the_general_kernel():
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 256, 256, 256, A=P + 1)["kernel"] == "general"
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 8, 256, 256, C=P + 4)["kernel"] == "general"
+
+
+def test_forced_kernel_that_cannot_run_is_unsupported():
+    try:
+        L.lpgemm_set_kernel_override(L.KERNEL_SKINNY)
+        with pytest.raises(L.LpgemmError) as e:
+            L.lpgemm_plan(L.VARIANT_I4I4, 8, 256, 256)
+        assert e.value.status == L.ERR_UNSUPPORTED
+        assert L.lpgemm_plan(L.VARIANT_W4A8, 8, 256, 256)["kernel"] == "skinny"
+        L.lpgemm_set_kernel_override(L.KERNEL_TILED)
+        with pytest.raises(L.LpgemmError):
+            L.lpgemm_plan(L.VARIANT_W4A8, 8, 256, 34)
+        L.lpgemm_set_kernel_override(L.KERNEL_GENERAL)
+        assert L.lpgemm_plan(L.VARIANT_W4A8, 4096, 4096, 4096)["kernel"] == "general"
+    finally:
+        L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
+
+
+def test_plan_grid_covers_the_output():
+    for variant, M, N, K in [(L.VARIANT_I4I4, 3000, 5120, 6144), (L.VARIANT_W4A8, 16, 28672, 8192),
+                             (L.VARIANT_W4A8, 1, 1000, 96)]:
+        p = L.lpgemm_plan(variant, M, N, K)
+        tiles = -(-M // p["tile_m"]) * -(-N // p["tile_n"])
+        assert p["workgroups"] == tiles, p
