@@ -43,7 +43,7 @@ PEAK_HBM_GBS = 8000.0
 STEP_ORDER = ["w4a8_skinny_m16", "i4i4_8192", "w4a8_skinny_m1", "w4a8_4096", "i4i4_ragged",
               "i4i4_256", "i4i4_1024"]
 
-KERNEL_SYMBOL = {"tiled": "gemm_tiled_kernel", "skinny": "gemm_w4a8_skinny_kernel",
+KERNEL_SYMBOL = {"tiled": "gemm_pipelined_kernel", "skinny": "gemm_w4a8_skinny_kernel",
                  "general": "gemm_general_kernel"}
 
 

@@ -10,6 +10,6 @@ streams only.
 """
 from ._binding import (  # noqa: F401
     ERR_HIP, ERR_INVALID_ARG, ERR_UNSUPPORTED, EXPORTS, KERNEL_AUTO, KERNEL_GENERAL,
-    KERNEL_NAMES, KERNEL_SKINNY, KERNEL_TILED, LIB_PATH, MAX_K, OK, VARIANT_I4I4,
+    KERNEL_NAMES, KERNEL_SKINNY, KERNEL_TILED, KERNEL_TILED_128, KERNEL_TILED_256, LIB_PATH, MAX_K, OK, VARIANT_I4I4,
     VARIANT_W4A8, LpgemmError, lib, lpgemm_int4_int4, lpgemm_pack_int4, lpgemm_plan,
     lpgemm_set_kernel_override, lpgemm_status_string, lpgemm_unpack_int4, lpgemm_w4a8)

@@ -8,7 +8,7 @@
 
 #include "gemm_general.hpp"
 #include "gemm_skinny.hpp"
-#include "gemm_tiled.hpp"
+#include "gemm_pipelined.hpp"
 
 using namespace lpgemm;
 
@@ -39,10 +39,22 @@ int device_cu_count()
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---- kernel configurations -------------------------------------------------
-// Tiled: 4 waves in 2 x 2, each wave 64 x 64 (2 x 2 blocks of 32 x 32), BK = 128.
-template <int VAR>
-using Tiled = TiledCfg<VAR, 2, 2, 2, 2, 128>;
-#define TILED_KERNEL(VAR) gemm_tiled_kernel<VAR, 2, 2, 2, 2, 128>
+// Tiled kernels (gemm_pipelined.hpp), chosen by measurement on MI355X:
+//   large: 256 x 256 tiles, 8 waves (2 x 4), each wave 128 (m) x 64 (n);
+//          int4 x int4 stages 256 logical k per LDS slot (2 slots, 128 KB),
+//          W4A8 128 k per slot (3 slots, 144 KB).
+//   small: 128 x 128 tiles, 4 waves, for shapes with too few large tiles to
+//          fill the GPU.
+template <int VAR, int FM, int FN, int WM, int WN, int BK, int ST>
+struct TiledKernel {
+    using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, ST>;
+    static void *fn() { return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, BK, ST, false>); }
+};
+using I4Large = TiledKernel<I4I4, 4, 2, 2, 4, 256, 2>;
+using W8Large = TiledKernel<W4A8, 4, 2, 2, 4, 128, 3>;
+using I4Small = TiledKernel<I4I4, 2, 2, 2, 2, 128, 3>;
+using W8Small = TiledKernel<W4A8, 2, 2, 2, 2, 128, 3>;
+constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 // Skinny: strips of 32 rows of B, K split over 8 waves.
 constexpr int kSkinnyFN = 2;
@@ -54,7 +66,8 @@ struct Plan {
     int tile_m = 0, tile_n = 0, k_split = 1, threads = 0;
     int64_t workgroups = 0;
     int k_per_wave = 0;
-    int tiles_n = 0;
+    int tiles_m = 0, tiles_n = 0;
+    bool large = false;
 };
 
 lpgemm_status check_args(const void *A, const void *B, const void *C, int64_t M, int64_t N,
@@ -74,7 +87,6 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
                         int64_t M, int64_t N, int64_t K, int cu_count, lpgemm_kernel forced,
                         Plan *plan)
 {
-    (void)cu_count;
     const bool fast_ok = (K % 32 == 0) && aligned16(A) && aligned16(B) && aligned16(C);
     const bool skinny_ok = fast_ok && variant == LPGEMM_VARIANT_W4A8 && M <= kSkinnyMaxM;
 
@@ -87,7 +99,9 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         else
             k = LPGEMM_KERNEL_TILED;
     }
-    if ((k == LPGEMM_KERNEL_TILED && !fast_ok) || (k == LPGEMM_KERNEL_SKINNY && !skinny_ok))
+    const bool tiled = k == LPGEMM_KERNEL_TILED || k == LPGEMM_KERNEL_TILED_128 ||
+                       k == LPGEMM_KERNEL_TILED_256;
+    if ((tiled && !fast_ok) || (k == LPGEMM_KERNEL_SKINNY && !skinny_ok))
         return LPGEMM_ERR_UNSUPPORTED;
 
     Plan p;
@@ -100,14 +114,20 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         p.workgroups = ceil_div(M, 16) * ceil_div(N, 16);
         if (ceil_div(M, 16) > 65535 || ceil_div(N, 16) > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
         break;
-    case LPGEMM_KERNEL_TILED: {
-        const int bm = (variant == LPGEMM_VARIANT_I4I4) ? Tiled<I4I4>::BM : Tiled<W4A8>::BM;
-        const int bn = (variant == LPGEMM_VARIANT_I4I4) ? Tiled<I4I4>::BN : Tiled<W4A8>::BN;
-        p.tile_m = bm;
-        p.tile_n = bn;
-        p.threads = Tiled<I4I4>::kThreads;
-        p.tiles_n = (int)ceil_div(N, bn);
-        p.workgroups = ceil_div(M, bm) * p.tiles_n;
+    case LPGEMM_KERNEL_TILED:
+    case LPGEMM_KERNEL_TILED_128:
+    case LPGEMM_KERNEL_TILED_256: {
+        // Large tiles when they give at least 3/4 of a tile per compute unit.
+        const int64_t large_tiles = ceil_div(M, 256) * ceil_div(N, 256);
+        p.large = (k == LPGEMM_KERNEL_TILED) ? large_tiles * 4 >= (int64_t)cu_count * 3
+                                              : k == LPGEMM_KERNEL_TILED_256;
+        p.kernel = LPGEMM_KERNEL_TILED;
+        p.tile_m = p.large ? 256 : 128;
+        p.tile_n = p.large ? 256 : 128;
+        p.threads = p.large ? I4Large::Cfg::kThreads : I4Small::Cfg::kThreads;
+        p.tiles_m = (int)ceil_div(M, p.tile_m);
+        p.tiles_n = (int)ceil_div(N, p.tile_n);
+        p.workgroups = (int64_t)p.tiles_m * p.tiles_n;
         if (p.workgroups > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
         break;
     }
@@ -130,6 +150,29 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
 lpgemm_status launched()
 {
     return hipGetLastError() == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
+}
+
+// Launch a tiled configuration; the first launch on each device raises the
+// kernel's dynamic-LDS limit to the ring size (above the 64 KB default).
+template <class TK>
+lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, int32_t *C, int m,
+                           int n, int k, hipStream_t stream)
+{
+    static std::once_flag once[kMaxDevices];
+    static hipError_t attr_err[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERR_HIP;
+    std::call_once(once[dev], [dev] {
+        attr_err[dev] = hipFuncSetAttribute(TK::fn(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            TK::Cfg::LDS_BYTES);
+    });
+    if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
+    int tiles_m = p.tiles_m, tiles_n = p.tiles_n, xcds = kXcds;
+    void *args[] = {(void *)&a, (void *)&b, (void *)&C, (void *)&m,       (void *)&n,
+                    (void *)&k, (void *)&tiles_m,      (void *)&tiles_n, (void *)&xcds};
+    const hipError_t e = hipLaunchKernel(TK::fn(), dim3((unsigned)p.workgroups),
+                                         dim3(TK::Cfg::kThreads), args, TK::Cfg::LDS_BYTES, stream);
+    return e == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
 }
 
 lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, int32_t *C,
@@ -161,16 +204,13 @@ lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, int
             hipLaunchKernelGGL(gemm_general_kernel<W4A8>, grid, dim3(256), 0, stream, a, b, C, M, N, K);
         break;
     }
-    case LPGEMM_KERNEL_TILED:
+    case LPGEMM_KERNEL_TILED: {
         if (variant == LPGEMM_VARIANT_I4I4)
-            hipLaunchKernelGGL(TILED_KERNEL(I4I4), dim3((unsigned)p.workgroups),
-                               dim3(Tiled<I4I4>::kThreads), Tiled<I4I4>::LDS_BYTES, stream, a, b, C,
-                               m, n, k, p.tiles_n);
-        else
-            hipLaunchKernelGGL(TILED_KERNEL(W4A8), dim3((unsigned)p.workgroups),
-                               dim3(Tiled<W4A8>::kThreads), Tiled<W4A8>::LDS_BYTES, stream, a, b, C,
-                               m, n, k, p.tiles_n);
-        break;
+            return p.large ? launch_tiled<I4Large>(p, a, b, C, m, n, k, stream)
+                           : launch_tiled<I4Small>(p, a, b, C, m, n, k, stream);
+        return p.large ? launch_tiled<W8Large>(p, a, b, C, m, n, k, stream)
+                       : launch_tiled<W8Small>(p, a, b, C, m, n, k, stream);
+    }
     case LPGEMM_KERNEL_SKINNY:
         hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyFN, kSkinnyKW>),
                            dim3((unsigned)p.workgroups), dim3(p.threads), 0, stream,
@@ -264,7 +304,7 @@ lpgemm_status lpgemm_plan(lpgemm_variant variant, const void *A, const void *B, 
 
 lpgemm_status lpgemm_set_kernel_override(lpgemm_kernel kernel)
 {
-    if (kernel < LPGEMM_KERNEL_AUTO || kernel > LPGEMM_KERNEL_SKINNY) return LPGEMM_ERR_INVALID_ARG;
+    if (kernel < LPGEMM_KERNEL_AUTO || kernel > LPGEMM_KERNEL_TILED_256) return LPGEMM_ERR_INVALID_ARG;
     g_override.store(kernel, std::memory_order_relaxed);
     return LPGEMM_OK;
 }

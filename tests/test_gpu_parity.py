@@ -71,7 +71,8 @@ def oracle_full(variant, A, B, M, N, K):
 # ---- small and ragged shapes, every kernel that accepts them --------------------
 RAGGED = [(1, 1, 2), (3, 5, 2), (17, 33, 34), (37, 53, 86), (129, 255, 510), (5, 7, 66)]
 ALIGNED = [(1, 1, 32), (16, 64, 128), (17, 33, 64), (37, 53, 96), (129, 255, 512),
-           (130, 200, 160), (256, 256, 256), (300, 260, 1056), (255, 129, 4096)]
+           (130, 200, 160), (256, 256, 256), (300, 260, 1056), (255, 129, 4096),
+           (600, 700, 2080), (513, 257, 288)]
 SKINNY = [(1, 1, 32), (1, 31, 96), (2, 33, 160), (7, 100, 1056), (16, 1000, 4096),
           (16, 64, 128), (13, 257, 8192)]
 
@@ -85,12 +86,13 @@ def test_general_kernel(torch, variant, M, N, K):
     assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
 
 
+@pytest.mark.parametrize("tile", [L.KERNEL_TILED_128, L.KERNEL_TILED_256], ids=["t128", "t256"])
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
 @pytest.mark.parametrize("M,N,K", ALIGNED)
-def test_tiled_kernel(torch, variant, M, N, K):
-    say(f"tiled {variant} {M}x{N}x{K}")
+def test_tiled_kernel(torch, variant, M, N, K, tile):
+    say(f"tiled {tile} {variant} {M}x{N}x{K}")
     A, B = custom_operands(variant, M, N, K, seed=M * 5 + K)
-    got = run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_TILED)
+    got = run_gpu(torch, variant, A, B, M, N, K, kernel=tile)
     assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
 
 

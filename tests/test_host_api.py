@@ -99,6 +99,14 @@ def test_auto_plan(variant, M, N, K, kernel):
     assert L.lpgemm_plan(variant, M, N, K)["kernel"] == kernel
 
 
+def test_tile_size_follows_the_number_of_tiles():
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192)["tile_m"] == 256
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 4096, 4096, 4096)["tile_m"] == 256
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 3000, 5120, 6144)["tile_m"] == 256  # 240 tiles
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 1024, 1024, 1024)["tile_m"] == 128
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 3000, 5120, 6144, cu_count=512)["tile_m"] == 128
+
+
 def test_unaligned_pointers_take_the_general_kernel():
     assert L.lpgemm_plan(L.VARIANT_I4I4, 256, 256, 256, A=P + 1)["kernel"] == "general"
     assert L.lpgemm_plan(L.VARIANT_W4A8, 8, 256, 256, C=P + 4)["kernel"] == "general"
@@ -116,6 +124,12 @@ def test_forced_kernel_that_cannot_run_is_unsupported():
             L.lpgemm_plan(L.VARIANT_W4A8, 8, 256, 34)
         L.lpgemm_set_kernel_override(L.KERNEL_GENERAL)
         assert L.lpgemm_plan(L.VARIANT_W4A8, 4096, 4096, 4096)["kernel"] == "general"
+        L.lpgemm_set_kernel_override(L.KERNEL_TILED_256)
+        p = L.lpgemm_plan(L.VARIANT_I4I4, 100, 100, 64)
+        assert (p["kernel"], p["tile_m"], p["workgroups"]) == ("tiled", 256, 1)
+        L.lpgemm_set_kernel_override(L.KERNEL_TILED_128)
+        p = L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192)
+        assert (p["kernel"], p["tile_m"], p["workgroups"]) == ("tiled", 128, 4096)
     finally:
         L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
 
