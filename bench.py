@@ -14,6 +14,9 @@ are seeded synthetic bytes already resident in HBM when timing starts; each
 call writes its own int32 C.  Every launch is bracketed by HIP events on the
 stream it runs on; the per-launch averages give each workload's TOP/s and
 roofline fraction (`per_config`) and the dominant kernel's `roofline`.
+`per_config_isolated` times each workload alone (back-to-back launches, the
+decode-shape B rotated over copies larger than the MALL together), free of the
+write-back a previous workload leaves behind.
 
 The CPU baseline times the oracle (plain C, OpenMP over rows) on the first
 rows of every workload, and those rows double as a bit-exact parity check of
@@ -57,6 +60,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline and parity rows")
     ap.add_argument("--cpu-macs", type=float, default=2.5e10,
                     help="multiply-accumulates per workload in the CPU baseline sample")
+    ap.add_argument("--isolated-reps", type=int, default=20,
+                    help="back-to-back launches per workload for the isolated per-kernel times")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -159,6 +164,35 @@ def main() -> int:
         if dominant is None or total > dominant[0]:
             dominant = (total, c, rec, avg)
 
+    # Each workload alone: back-to-back launches, B rotated over enough copies
+    # that every launch streams B from HBM (three copies exceed the 256 MB
+    # MALL for the decode shape), so no launch pays for another workload's
+    # write-back and none reads a cache-warm B.
+    isolated = {}
+    if args.isolated_reps > 0:
+        for w in work:
+            c = w["case"]
+            copies = [w["b"]] + [w["b"].clone() for _ in range(2 if c.b_bytes > (64 << 20) else 0)]
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.isolated_reps)]
+            call(w)
+            for j, (e0, e1) in enumerate(evs):
+                e0.record(stream)
+                st = w["fn"](w["a"].data_ptr(), copies[j % len(copies)].data_ptr(),
+                             w["C"].data_ptr(), c.M, c.N, c.K, handle)
+                e1.record(stream)
+                if st != L.OK:
+                    raise RuntimeError(f"{c.name}: {L.lpgemm_status_string(st)}")
+            torch.cuda.synchronize()
+            us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+            med = float(np.median(us))
+            t_roof, bound = roofline_time_s(c)
+            isolated[c.name] = {"median_us": round(med, 3), "min_us": round(float(us.min()), 3),
+                                "tops": round(c.ops / (med * 1e-6) / 1e12, 2),
+                                "gbs": round(c.alg_bytes / (med * 1e-6) / 1e9, 1),
+                                "bound": bound, "roofline_frac": round(t_roof / (med * 1e-6), 4)}
+            del copies
+
     _, dc, drec, davg = dominant
     if drec["bound"] == "mfma":
         achieved = dc.ops / (davg * 1e-6) / 1e12
@@ -190,6 +224,7 @@ def main() -> int:
                    "ops_per_step": ops_step, "parallelism": "single GPU"},
         "roofline": roof,
         "per_config": per_config,
+        "per_config_isolated": isolated,
     }
 
     if not args.no_cpu:

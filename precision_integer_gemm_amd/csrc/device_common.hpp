@@ -93,4 +93,25 @@ __device__ __forceinline__ i32x4 load16(const void *p)
     return *reinterpret_cast<const i32x4 *>(p);
 }
 
+// Workgroup barrier for LDS traffic only: drains this wave's LDS operations
+// and waits for the other waves, without the vector-memory drain that a full
+// __syncthreads() fence adds (prefetched global loads stay in flight).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Raw buffer resource over `bytes` bytes at `base`: loads at offsets at or
+// past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t offset)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(rsrc, offset, 0, 0);
+}
+
 }  // namespace lpgemm

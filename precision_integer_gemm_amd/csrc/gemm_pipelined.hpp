@@ -107,12 +107,6 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N < 63 ? N : 63) : "memory");
 }
 
-// Workgroup barrier that first drains this wave's LDS reads.
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, bool SCHED>

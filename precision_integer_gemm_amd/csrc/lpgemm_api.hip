@@ -56,16 +56,17 @@ using I4Small = TiledKernel<I4I4, 2, 2, 2, 2, 128, 3>;
 using W8Small = TiledKernel<W4A8, 2, 2, 2, 2, 128, 3>;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
-// Skinny: strips of 32 rows of B, K split over 8 waves.
-constexpr int kSkinnyFN = 2;
+// Skinny: 8 waves split K (up to 8 steps of 128 k each, A held in registers);
+// one workgroup per compute unit walks strips of 16 rows of B.
 constexpr int kSkinnyKW = 8;
 constexpr int kSkinnyMaxM = 16;
+constexpr int kSkinnyMaxK = kSkinnyKW * 8 * 128;
 
 struct Plan {
     lpgemm_kernel kernel = LPGEMM_KERNEL_AUTO;
     int tile_m = 0, tile_n = 0, k_split = 1, threads = 0;
     int64_t workgroups = 0;
-    int k_per_wave = 0;
+    int k_steps = 0;
     int tiles_m = 0, tiles_n = 0;
     bool large = false;
 };
@@ -88,7 +89,8 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
                         Plan *plan)
 {
     const bool fast_ok = (K % 32 == 0) && aligned16(A) && aligned16(B) && aligned16(C);
-    const bool skinny_ok = fast_ok && variant == LPGEMM_VARIANT_W4A8 && M <= kSkinnyMaxM;
+    const bool skinny_ok = fast_ok && variant == LPGEMM_VARIANT_W4A8 && M <= kSkinnyMaxM &&
+                           K <= kSkinnyMaxK && N * (K / 2) < INT32_MAX;
 
     lpgemm_kernel k = forced;
     if (k == LPGEMM_KERNEL_AUTO) {
@@ -133,11 +135,12 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
     }
     case LPGEMM_KERNEL_SKINNY: {
         p.tile_m = kSkinnyMaxM;
-        p.tile_n = kSkinnyFN * 16;
+        p.tile_n = 16;
         p.k_split = kSkinnyKW;
         p.threads = 64 * kSkinnyKW;
-        p.k_per_wave = (int)(ceil_div(ceil_div(K, kSkinnyKW), 128) * 128);
-        p.workgroups = ceil_div(N, p.tile_n);
+        p.k_steps = (int)ceil_div(ceil_div(K, kSkinnyKW), 128);  // 1..8
+        while (p.k_steps & (p.k_steps - 1)) ++p.k_steps;          // 1, 2, 4 or 8
+        p.workgroups = std::min<int64_t>(ceil_div(N, 16), std::min(cu_count, 256));
         break;
     }
     default:
@@ -211,11 +214,17 @@ lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, int
         return p.large ? launch_tiled<W8Large>(p, a, b, C, m, n, k, stream)
                        : launch_tiled<W8Small>(p, a, b, C, m, n, k, stream);
     }
-    case LPGEMM_KERNEL_SKINNY:
-        hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyFN, kSkinnyKW>),
-                           dim3((unsigned)p.workgroups), dim3(p.threads), 0, stream,
-                           static_cast<const int8_t *>(A), b, C, m, n, k, p.k_per_wave);
+    case LPGEMM_KERNEL_SKINNY: {
+        const int8_t *a8 = static_cast<const int8_t *>(A);
+        const dim3 grid((unsigned)p.workgroups), block(p.threads);
+        switch (p.k_steps) {
+        case 1: hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, 1>), grid, block, 0, stream, a8, b, C, m, n, k); break;
+        case 2: hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, 2>), grid, block, 0, stream, a8, b, C, m, n, k); break;
+        case 4: hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, 4>), grid, block, 0, stream, a8, b, C, m, n, k); break;
+        default: hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, 8>), grid, block, 0, stream, a8, b, C, m, n, k); break;
+        }
         break;
+    }
     default:
         return LPGEMM_ERR_INVALID_ARG;
     }

@@ -135,8 +135,18 @@ def test_forced_kernel_that_cannot_run_is_unsupported():
 
 
 def test_plan_grid_covers_the_output():
-    for variant, M, N, K in [(L.VARIANT_I4I4, 3000, 5120, 6144), (L.VARIANT_W4A8, 16, 28672, 8192),
-                             (L.VARIANT_W4A8, 1, 1000, 96)]:
+    for variant, M, N, K in [(L.VARIANT_I4I4, 3000, 5120, 6144), (L.VARIANT_I4I4, 1024, 1000, 64)]:
         p = L.lpgemm_plan(variant, M, N, K)
         tiles = -(-M // p["tile_m"]) * -(-N // p["tile_n"])
         assert p["workgroups"] == tiles, p
+    # the narrow-M kernel: one workgroup per compute unit walks the 16-row strips
+    p = L.lpgemm_plan(L.VARIANT_W4A8, 16, 28672, 8192)
+    assert (p["workgroups"], p["tile_n"], p["k_split"]) == (256, 16, 8)
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 1, 1000, 96)["workgroups"] == 63
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 28672, 8192, cu_count=304)["workgroups"] == 304
+
+
+def test_narrow_m_limits():
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 4096, 8192)["kernel"] == "skinny"
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 4096, 8224)["kernel"] == "tiled"   # K above 8192
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 17, 4096, 4096)["kernel"] == "tiled"   # M above 16
