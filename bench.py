@@ -49,6 +49,36 @@ STEP_ORDER = ["w4a8_skinny_m16", "i4i4_8192", "w4a8_skinny_m1", "w4a8_4096", "i4
 KERNEL_SYMBOL = {"tiled": "gemm_pipelined_kernel", "skinny": "gemm_w4a8_skinny_kernel",
                  "general": "gemm_general_kernel"}
 
+# HBM traffic of the dominant kernel, from two rocprofv3 --pmc runs (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+# reads for a plain 256 MiB device copy (bench.py --copy-calibration 256):
+# FETCH_SIZE reads 131072 KiB for 256 MiB read (x2.0), WRITE_SIZE 262144 KiB
+# for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
+# on (their SHA-256 below); any change reports null until re-measured.
+TRAFFIC = {
+    "i4i4_8192": {"fetch_kib": 197382.0, "fetch_scale": 2.0, "write_kib": 266789.0,
+                  "write_scale": 1.0, "sources_sha256": "fc995a336eee255726e89cf4796612be0a02e0eb5ada7f536db2620003d5e8d7"},
+}
+TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
+                   "precision_integer_gemm_amd/csrc/device_common.hpp",
+                   "precision_integer_gemm_amd/csrc/lpgemm_api.hip"]
+
+
+def sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    t = TRAFFIC.get(workload)
+    if t is None or t["sources_sha256"] != sources_sha256():
+        return None
+    return int(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -64,7 +94,29 @@ def parse():
                     help="back-to-back launches per workload for the isolated per-kernel times")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarise a rocprofv3 kernel_trace.csv per kernel and grid (no GPU use)")
     return ap.parse_args()
+
+
+def trace_summary(path: str) -> int:
+    """Average duration per (kernel, grid) of a rocprofv3 kernel trace, so one
+    kernel template used by several workloads is split by launch shape."""
+    import csv
+    from collections import defaultdict
+    groups = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0]
+            grid = int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0)
+            wg = int(r.get("Workgroup_Size", r.get("Workgroup_Size_X", 0)) or 0)
+            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            groups[(name, grid, wg)].append(dur)
+    print("| kernel | grid (threads) | workgroup | calls | avg ns | min ns | max ns |")
+    print("|---|---|---|---|---|---|---|")
+    for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {name} | {grid} | {wg} | {len(d)} | {sum(d) / len(d):.0f} | {min(d)} | {max(d)} |")
+    return 0
 
 
 def roofline_time_s(case) -> tuple[float, str]:
@@ -75,6 +127,8 @@ def roofline_time_s(case) -> tuple[float, str]:
 
 def main() -> int:
     args = parse()
+    if args.trace_summary:
+        return trace_summary(args.trace_summary)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -202,7 +256,8 @@ def main() -> int:
         achieved = dc.alg_bytes / (davg * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof.update({"traffic": None, "kernel": KERNEL_SYMBOL[drec["kernel"]], "workload": dc.name,
+    roof.update({"traffic": measured_traffic(dc.name), "traffic_unit": "bytes per launch",
+                 "kernel": KERNEL_SYMBOL[drec["kernel"]], "workload": dc.name,
                  "avg_us": round(davg, 3)})
 
     result = {

@@ -26,8 +26,10 @@
 //
 // Epilogue (a5): exact >> 8 (int4 x int4) or >> 4 (W4A8), masked stores.
 //
-// Tile order: workgroup b runs on XCD b % 8; the kernel renumbers blocks so
-// each XCD walks a compact band of C (shared A rows and B columns in its L2).
+// Tile order: persistent workgroups loop over tiles (stores of one tile drain
+// under the next tile's work); workgroup b runs on XCD b % 8 and tiles are
+// renumbered so each XCD walks a compact band of C (shared A rows and B
+// columns in its L2).
 //
 // Requirements (checked on the host): K % 32 == 0, 16-byte aligned bases,
 // M, N < 2^31, K <= 131070.
@@ -126,27 +128,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipelined_kernel(
     const int wm = wave / WN;
     const int wn = wave % WN;
 
-    // ---- tile of this workgroup: XCD-contiguous ranges, then bands of 4 tile rows
-    const int nblocks = tiles_m * tiles_n;
-    int id = blockIdx.x;
-    const int whole = nblocks - nblocks % xcds;
-    if (id < whole) id = (id % xcds) * (whole / xcds) + id / xcds;
-    constexpr int kBand = 4;
-    const int band = id / (kBand * tiles_n);
-    const int band_m0 = band * kBand;
-    const int band_rows = min(kBand, tiles_m - band_m0);
-    const int in_band = id - band * kBand * tiles_n;
-    const int tile_m = band_m0 + in_band % band_rows;
-    const int tile_n = in_band / band_rows;
-    const int m0 = tile_m * Cfg::BM;
-    const int n0 = tile_n * Cfg::BN;
-
     const uint32_t lda = (VAR == I4I4) ? (uint32_t)K / 2 : (uint32_t)K;  // global row bytes
     const uint32_t ldb = (uint32_t)K / 2;
     const int ktiles = (K + BK - 1) / BK;
-
-    const i32x4 rsrc_a = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)min(Cfg::BM, M - m0) * lda);
-    const i32x4 rsrc_b = make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)min(Cfg::BN, N - n0) * ldb);
 
     // Per-lane source of each DMA instruction: tile row and 16-byte column.
     uint32_t a_off[NA], a_col[NA], b_off[NB], b_col[NB];
@@ -168,187 +152,213 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipelined_kernel(
     }
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
-    auto issue_stage = [&](int kt) {
-        const uint32_t base = lds0 + (uint32_t)(kt % STAGES) * Cfg::STAGE_BYTES;
-        const uint32_t ka = (uint32_t)kt * RA, kb = (uint32_t)kt * RB;
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const uint32_t off = (ka + a_col[i] < lda) ? a_off[i] + ka : kOutOfRange;
-            dma16(rsrc_a, off, base + (uint32_t)(wave * NA + i) * 1024u);
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const uint32_t off = (kb + b_col[i] < ldb) ? b_off[i] + kb : kOutOfRange;
-            dma16(rsrc_b, off, base + Cfg::A_BYTES + (uint32_t)(wave * NB + i) * 1024u);
-        }
-    };
+    // Persistent tile loop: workgroup b takes tiles b, b + G, b + 2G, ... (G =
+    // number of workgroups).  Each tile's C stores are issued and left to
+    // drain while the next tile's loads and MFMAs proceed.  Tiles are
+    // renumbered so that each XCD (workgroup b runs on XCD b % xcds) walks a
+    // contiguous range of tile ids, taken in bands of 4 tile rows, which keeps
+    // the A rows and B columns its workgroups share in that XCD's L2.
+    const int nblocks = tiles_m * tiles_n;
+    const int whole = nblocks - nblocks % xcds;
+    for (int v = blockIdx.x; v < nblocks; v += gridDim.x) {
+        int id = v;
+        if (id < whole) id = (id % xcds) * (whole / xcds) + id / xcds;
+        constexpr int kBand = 4;
+        const int band = id / (kBand * tiles_n);
+        const int band_m0 = band * kBand;
+        const int band_rows = min(kBand, tiles_m - band_m0);
+        const int in_band = id - band * kBand * tiles_n;
+        const int tile_m = band_m0 + in_band % band_rows;
+        const int tile_n = in_band / band_rows;
+        const int m0 = tile_m * Cfg::BM;
+        const int n0 = tile_n * Cfg::BN;
+        const i32x4 rsrc_a = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)min(Cfg::BM, M - m0) * lda);
+        const i32x4 rsrc_b = make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)min(Cfg::BN, N - n0) * ldb);
+        lds_barrier();  // every wave is done with the previous tile's LDS slots
 
-    i32x16 acc[FN][FM];
+        auto issue_stage = [&](int kt) {
+            const uint32_t base = lds0 + (uint32_t)(kt % STAGES) * Cfg::STAGE_BYTES;
+            const uint32_t ka = (uint32_t)kt * RA, kb = (uint32_t)kt * RB;
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = i32x16{};
-
-    const int h = lane >> 5;    // which 16-k half of an MFMA operand this lane feeds
-    const int r32 = lane & 31;  // operand row inside a 32-row block
-
-    // Raw (still packed / int8) fragments of one 64-k step, as read from LDS.
-    constexpr int AV = (VAR == I4I4) ? 1 : 2;  // 16-byte vectors per A block row
-    struct Frags {
-        i32x4 b[FN];
-        i32x4 a[FM][AV];
-    };
-    auto read_frags = [&](int slot, int step, Frags &f) {
-        const uint8_t *sa = smem + slot * Cfg::STAGE_BYTES;
-        const uint8_t *sb = sa + Cfg::A_BYTES;
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int row = (wn * FN + fn) * 32 + r32;
-            f.b[fn] = *reinterpret_cast<const i32x4 *>(sb + 16 * lds_chunk<CPR_B>(row, 2 * step + h));
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int row = (wm * FM + fm) * 32 + r32;
-#pragma unroll
-            for (int v = 0; v < AV; ++v) {
-                const int col = (VAR == I4I4) ? 2 * step + h : 4 * step + 2 * h + v;
-                f.a[fm][v] = *reinterpret_cast<const i32x4 *>(sa + 16 * lds_chunk<CPR_A>(row, col));
+            for (int i = 0; i < NA; ++i) {
+                const uint32_t off = (ka + a_col[i] < lda) ? a_off[i] + ka : kOutOfRange;
+                dma16(rsrc_a, off, base + (uint32_t)(wave * NA + i) * 1024u);
             }
-        }
-    };
-    // Unpack and contract one 64-k step: per block two 32x32x32 MFMAs.
-    auto compute = [&](const Frags &f) {
-        i32x4 a_lo[FM], a_hi[FM];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            i32x4 b_lo, b_hi;
-            unpack_chunk<VAR == W4A8>(f.b[fn], b_lo, b_hi);
+            for (int i = 0; i < NB; ++i) {
+                const uint32_t off = (kb + b_col[i] < ldb) ? b_off[i] + kb : kOutOfRange;
+                dma16(rsrc_b, off, base + Cfg::A_BYTES + (uint32_t)(wave * NB + i) * 1024u);
+            }
+        };
+
+        i32x16 acc[FN][FM];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = i32x16{};
+
+        const int h = lane >> 5;    // which 16-k half of an MFMA operand this lane feeds
+        const int r32 = lane & 31;  // operand row inside a 32-row block
+
+        // Raw (still packed / int8) fragments of one 64-k step, as read from LDS.
+        constexpr int AV = (VAR == I4I4) ? 1 : 2;  // 16-byte vectors per A block row
+        struct Frags {
+            i32x4 b[FN];
+            i32x4 a[FM][AV];
+        };
+        auto read_frags = [&](int slot, int step, Frags &f) {
+            const uint8_t *sa = smem + slot * Cfg::STAGE_BYTES;
+            const uint8_t *sb = sa + Cfg::A_BYTES;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int row = (wn * FN + fn) * 32 + r32;
+                f.b[fn] = *reinterpret_cast<const i32x4 *>(sb + 16 * lds_chunk<CPR_B>(row, 2 * step + h));
+            }
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                if (fn == 0) {
-                    if (VAR == I4I4) {
-                        unpack_chunk<false>(f.a[fm][0], a_lo[fm], a_hi[fm]);
+                const int row = (wm * FM + fm) * 32 + r32;
+#pragma unroll
+                for (int v = 0; v < AV; ++v) {
+                    const int col = (VAR == I4I4) ? 2 * step + h : 4 * step + 2 * h + v;
+                    f.a[fm][v] = *reinterpret_cast<const i32x4 *>(sa + 16 * lds_chunk<CPR_A>(row, col));
+                }
+            }
+        };
+        // Unpack and contract one 64-k step: per block two 32x32x32 MFMAs.
+        auto compute = [&](const Frags &f) {
+            i32x4 a_lo[FM], a_hi[FM];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                i32x4 b_lo, b_hi;
+                unpack_chunk<VAR == W4A8>(f.b[fn], b_lo, b_hi);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    if (fn == 0) {
+                        if (VAR == I4I4) {
+                            unpack_chunk<false>(f.a[fm][0], a_lo[fm], a_hi[fm]);
+                        } else {
+                            a_lo[fm] = f.a[fm][0];
+                            a_hi[fm] = f.a[fm][AV - 1];
+                        }
+                    }
+                    acc[fn][fm] = mfma_32x32x32(b_lo, a_lo[fm], acc[fn][fm]);
+                    acc[fn][fm] = mfma_32x32x32(b_hi, a_hi[fm], acc[fn][fm]);
+                }
+            }
+        };
+
+        // Scheduling pattern of one 64-k step: the first operands' unpack, then
+        // each MFMA followed by its share of the remaining unpack work, with the
+        // next step's LDS reads spread in between, so that one wave per SIMD
+        // keeps both the MFMA pipe and the VALU busy (instructions issue in
+        // order, so VALU work overlaps an MFMA only when placed after it).
+        auto interleave = [&]() {
+            if constexpr (SCHED) {
+                constexpr int kMfma = 2 * FM * FN;
+                constexpr int kValuPerDword = (VAR == I4I4) ? 3 : 5;
+                constexpr int kValu = 8 * kValuPerDword * FN + (VAR == I4I4 ? 8 * 3 * FM : 0);
+                constexpr int kFirst = 8 * kValuPerDword + (VAR == I4I4 ? 8 * 3 : 0);
+                constexpr int kRest = kValu - kFirst;
+                constexpr int kPer = (kRest + kMfma - 1) / kMfma;
+                constexpr int kReads = FN + FM * AV;
+                constexpr int kReadEvery = (kMfma + kReads - 1) / kReads;
+                __builtin_amdgcn_sched_group_barrier(0x002, kFirst, 0);
+#pragma unroll
+                for (int i = 0; i < kMfma; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);
+                    if (i % kReadEvery == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+        };
+
+        constexpr int STEPS = BK / 64;
+        constexpr int kPerStage = NA + NB;
+        // Wait until this wave's loads of the tile issued `after` tiles before the
+        // newest one have landed.
+        auto wait_tiles_after = [&](int after) {
+            if (after >= 4)
+                wait_vmcnt<4 * kPerStage>();
+            else if (after >= 3)
+                wait_vmcnt<3 * kPerStage>();
+            else if (after == 2)
+                wait_vmcnt<2 * kPerStage>();
+            else if (after == 1)
+                wait_vmcnt<kPerStage>();
+            else
+                wait_vmcnt<0>();
+        };
+
+        // Prologue: fill every ring slot, then read step 0 of tile 0.  Slots past
+        // the last tile are filled too (with zeros: every offset is out of range),
+        // which keeps the number of loads in flight the same in every iteration.
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s) issue_stage(s);
+        wait_tiles_after(STAGES - 1);
+        lds_barrier();
+        Frags cur, nxt;
+        read_frags(0, 0, cur);
+
+        // Steady state: every tile but the last.  The tile's last step waits for
+        // tile kt+1, passes the barrier (every wave is done reading tile kt),
+        // refills tile kt's slot with tile kt+STAGES and reads step 0 of tile kt+1.
+        for (int kt = 0; kt + 1 < ktiles; ++kt) {
+            const int slot = kt % STAGES;
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) {
+                if (st + 1 < STEPS) {
+                    read_frags(slot, st + 1, nxt);
+                } else {
+                    wait_tiles_after(STAGES - 2);
+                    lds_barrier();
+                    issue_stage(kt + STAGES);
+                    read_frags((kt + 1) % STAGES, 0, nxt);
+                }
+                compute(cur);
+                interleave();
+                cur = nxt;
+            }
+        }
+        // Last tile.
+        {
+            const int slot = (ktiles - 1) % STAGES;
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) {
+                if (st + 1 < STEPS) read_frags(slot, st + 1, nxt);
+                compute(cur);
+                interleave();
+                cur = nxt;
+            }
+        }
+        wait_vmcnt<0>();  // the zero-fill loads past the end
+
+        // Epilogue: lane holds C[m][n .. n+3] for m = l%32 of each column block.
+        const bool vec_ok = (N % 4) == 0;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int m = m0 + (wm * FM + fm) * 32 + r32;
+                if (m >= M) continue;
+                int32_t *crow = C + (int64_t)m * N;
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int n = n0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h;
+                    const i32x4 v = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
+                                          acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
+                                    Cfg::SHIFT;
+                    if (vec_ok && n + 3 < N) {
+                        *reinterpret_cast<i32x4 *>(crow + n) = v;
                     } else {
-                        a_lo[fm] = f.a[fm][0];
-                        a_hi[fm] = f.a[fm][AV - 1];
+                        if (n + 0 < N) crow[n + 0] = v.x;
+                        if (n + 1 < N) crow[n + 1] = v.y;
+                        if (n + 2 < N) crow[n + 2] = v.z;
+                        if (n + 3 < N) crow[n + 3] = v.w;
                     }
                 }
-                acc[fn][fm] = mfma_32x32x32(b_lo, a_lo[fm], acc[fn][fm]);
-                acc[fn][fm] = mfma_32x32x32(b_hi, a_hi[fm], acc[fn][fm]);
             }
-        }
-    };
+    }  // tile loop
 
-    // Scheduling pattern of one 64-k step: the first operands' unpack, then
-    // each MFMA followed by its share of the remaining unpack work, with the
-    // next step's LDS reads spread in between, so that one wave per SIMD
-    // keeps both the MFMA pipe and the VALU busy (instructions issue in
-    // order, so VALU work overlaps an MFMA only when placed after it).
-    auto interleave = [&]() {
-        if constexpr (SCHED) {
-            constexpr int kMfma = 2 * FM * FN;
-            constexpr int kValuPerDword = (VAR == I4I4) ? 3 : 5;
-            constexpr int kValu = 8 * kValuPerDword * FN + (VAR == I4I4 ? 8 * 3 * FM : 0);
-            constexpr int kFirst = 8 * kValuPerDword + (VAR == I4I4 ? 8 * 3 : 0);
-            constexpr int kRest = kValu - kFirst;
-            constexpr int kPer = (kRest + kMfma - 1) / kMfma;
-            constexpr int kReads = FN + FM * AV;
-            constexpr int kReadEvery = (kMfma + kReads - 1) / kReads;
-            __builtin_amdgcn_sched_group_barrier(0x002, kFirst, 0);
-#pragma unroll
-            for (int i = 0; i < kMfma; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);
-                if (i % kReadEvery == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        }
-    };
-
-    constexpr int STEPS = BK / 64;
-    constexpr int kPerStage = NA + NB;
-    // Wait until this wave's loads of the tile issued `after` tiles before the
-    // newest one have landed.
-    auto wait_tiles_after = [&](int after) {
-        if (after >= 4)
-            wait_vmcnt<4 * kPerStage>();
-        else if (after >= 3)
-            wait_vmcnt<3 * kPerStage>();
-        else if (after == 2)
-            wait_vmcnt<2 * kPerStage>();
-        else if (after == 1)
-            wait_vmcnt<kPerStage>();
-        else
-            wait_vmcnt<0>();
-    };
-
-    // Prologue: fill every ring slot, then read step 0 of tile 0.  Slots past
-    // the last tile are filled too (with zeros: every offset is out of range),
-    // which keeps the number of loads in flight the same in every iteration.
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s) issue_stage(s);
-    wait_tiles_after(STAGES - 1);
-    lds_barrier();
-    Frags cur, nxt;
-    read_frags(0, 0, cur);
-
-    // Steady state: every tile but the last.  The tile's last step waits for
-    // tile kt+1, passes the barrier (every wave is done reading tile kt),
-    // refills tile kt's slot with tile kt+STAGES and reads step 0 of tile kt+1.
-    for (int kt = 0; kt + 1 < ktiles; ++kt) {
-        const int slot = kt % STAGES;
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            if (st + 1 < STEPS) {
-                read_frags(slot, st + 1, nxt);
-            } else {
-                wait_tiles_after(STAGES - 2);
-                lds_barrier();
-                issue_stage(kt + STAGES);
-                read_frags((kt + 1) % STAGES, 0, nxt);
-            }
-            compute(cur);
-            interleave();
-            cur = nxt;
-        }
-    }
-    // Last tile.
-    {
-        const int slot = (ktiles - 1) % STAGES;
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            if (st + 1 < STEPS) read_frags(slot, st + 1, nxt);
-            compute(cur);
-            interleave();
-            cur = nxt;
-        }
-    }
-    wait_vmcnt<0>();  // the zero-fill loads past the end
-
-    // Epilogue: lane holds C[m][n .. n+3] for m = l%32 of each column block.
-    const bool vec_ok = (N % 4) == 0;
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int m = m0 + (wm * FM + fm) * 32 + r32;
-            if (m >= M) continue;
-            int32_t *crow = C + (int64_t)m * N;
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int n = n0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h;
-                const i32x4 v = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
-                                      acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
-                                Cfg::SHIFT;
-                if (vec_ok && n + 3 < N) {
-                    *reinterpret_cast<i32x4 *>(crow + n) = v;
-                } else {
-                    if (n + 0 < N) crow[n + 0] = v.x;
-                    if (n + 1 < N) crow[n + 1] = v.y;
-                    if (n + 2 < N) crow[n + 2] = v.z;
-                    if (n + 3 < N) crow[n + 3] = v.w;
-                }
-            }
-        }
 }
 
 }  // namespace lpgemm

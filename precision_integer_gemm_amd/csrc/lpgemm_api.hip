@@ -131,6 +131,9 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         p.tiles_n = (int)ceil_div(N, p.tile_n);
         p.workgroups = (int64_t)p.tiles_m * p.tiles_n;
         if (p.workgroups > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+        // Large tiles run one persistent workgroup per compute unit (their LDS
+        // ring leaves room for one), each looping over tiles.
+        if (p.large) p.workgroups = std::min<int64_t>(p.workgroups, cu_count);
         break;
     }
     case LPGEMM_KERNEL_SKINNY: {

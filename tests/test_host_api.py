@@ -139,11 +139,16 @@ def test_plan_grid_covers_the_output():
         p = L.lpgemm_plan(variant, M, N, K)
         tiles = -(-M // p["tile_m"]) * -(-N // p["tile_n"])
         assert p["workgroups"] == tiles, p
+    # 256 x 256 tiles: one persistent workgroup per compute unit loops over tiles
+    p = L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192)
+    assert (p["tile_m"], p["workgroups"]) == (256, 256)
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=304)["workgroups"] == 304
     # the narrow-M kernel: one workgroup per compute unit walks the 16-row strips
     p = L.lpgemm_plan(L.VARIANT_W4A8, 16, 28672, 8192)
     assert (p["workgroups"], p["tile_n"], p["k_split"]) == (256, 16, 8)
     assert L.lpgemm_plan(L.VARIANT_W4A8, 1, 1000, 96)["workgroups"] == 63
-    assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 28672, 8192, cu_count=304)["workgroups"] == 304
+    # capped at 256 workgroups (prefetch offsets past the end stay within 32 bits)
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 28672, 8192, cu_count=304)["workgroups"] == 256
 
 
 def test_narrow_m_limits():
