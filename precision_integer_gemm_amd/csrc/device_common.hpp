@@ -114,4 +114,45 @@ __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint
     return __builtin_amdgcn_raw_buffer_load_b128(rsrc, offset, 0, 0);
 }
 
+// ---- direct-to-LDS loads ---------------------------------------------------
+// Buffer resource for `bytes` bytes at `base` (raw buffer, no stride).
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)p);
+    r.y = __builtin_amdgcn_readfirstlane((int32_t)((p >> 32) & 0xFFFFu));
+    r.z = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+    r.w = 0x00020000;  // 32-bit data format: raw byte-addressed loads
+    return r;
+}
+
+// 16 bytes per lane from rsrc[voffset] into LDS at lds_base + 16 * lane.  An
+// offset at or beyond the resource size reads zeros.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voffset, uint32_t lds_base)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"  // one wait state between an M0 write and an LDS DMA
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voffset), "s"(rsrc), "s"(lds_base)
+        : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (the counter holds 0..63; a larger N waits for 63, which is only stricter).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N < 63 ? N : 63) : "memory");
+}
+
+// A buffer offset that no resource here reaches: such a load returns zeros.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 }  // namespace lpgemm

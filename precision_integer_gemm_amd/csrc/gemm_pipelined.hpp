@@ -73,53 +73,24 @@ __device__ __forceinline__ int lds_chunk(int row, int col)
     return row * CPR + (col ^ ((row / rows_per_256) % CPR));
 }
 
-// Buffer resource for `bytes` bytes at `base` (raw buffer, no stride).
-__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)
-{
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    i32x4 r;
-    r.x = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)p);
-    r.y = __builtin_amdgcn_readfirstlane((int32_t)((p >> 32) & 0xFFFFu));
-    r.z = __builtin_amdgcn_readfirstlane((int32_t)bytes);
-    r.w = 0x00020000;  // 32-bit data format: raw byte-addressed loads
-    return r;
-}
-
-// 16 bytes per lane from rsrc[voffset] into LDS at lds_base + 16 * lane.  An
-// offset at or beyond the resource size reads zeros.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voffset, uint32_t lds_base)
-{
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voffset), "s"(rsrc), "s"(lds_base)
-        : "memory");
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight
-// (the counter holds 0..63; a larger N waits for 63, which is only stricter).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N < 63 ? N : 63) : "memory");
-}
-
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
-template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, bool SCHED>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_pipelined_kernel(
+template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, int SCHED, bool SPREAD = false>
+__global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pipelined_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int32_t *__restrict__ C, int M,
     int N, int K, int tiles_m, int tiles_n, int xcds)
 {
     using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, STAGES>;
     static_assert(Cfg::kFits, "LDS ring does not fit in 160 KB");
+    static_assert(!SPREAD || STAGES >= 3, "spread issue needs a slot of slack");
     constexpr int RA = Cfg::RA, RB = Cfg::RB, CPR_A = Cfg::CPR_A, CPR_B = Cfg::CPR_B;
     constexpr int NA = Cfg::NA, NB = Cfg::NB;
+    constexpr int STEPS = BK / 64;
+    constexpr int kPerStage = NA + NB;  // DMA instructions per wave per stage
+    // Stages loaded before a tile's first step: all of them, or all but the
+    // one that the first tile's steps issue piece by piece.
+    constexpr int kPrologue = SPREAD ? STAGES - 1 : STAGES;
+    // 16-byte stores per wave for a tile with no edge (a lower bound on the
+    // vector-memory instructions its epilogue issues).
+    constexpr int kStores = FN * FM * 4;
     extern __shared__ __align__(1024) uint8_t smem[];
 
     const int tid = threadIdx.x;
@@ -153,14 +124,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipelined_kernel(
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
     // Persistent tile loop: workgroup b takes tiles b, b + G, b + 2G, ... (G =
-    // number of workgroups).  Each tile's C stores are issued and left to
-    // drain while the next tile's loads and MFMAs proceed.  Tiles are
-    // renumbered so that each XCD (workgroup b runs on XCD b % xcds) walks a
-    // contiguous range of tile ids, taken in bands of 4 tile rows, which keeps
-    // the A rows and B columns its workgroups share in that XCD's L2.
+    // number of workgroups).  Tiles are renumbered so that each XCD
+    // (workgroup b runs on XCD b % xcds) walks a contiguous range of tile
+    // ids, taken in bands of 4 tile rows, which keeps the A rows and B columns
+    // its workgroups share in that XCD's L2.
     const int nblocks = tiles_m * tiles_n;
     const int whole = nblocks - nblocks % xcds;
-    for (int v = blockIdx.x; v < nblocks; v += gridDim.x) {
+    auto tile_origin = [&](int v, int &m0, int &n0) {
         int id = v;
         if (id < whole) id = (id % xcds) * (whole / xcds) + id / xcds;
         constexpr int kBand = 4;
@@ -168,150 +138,192 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipelined_kernel(
         const int band_m0 = band * kBand;
         const int band_rows = min(kBand, tiles_m - band_m0);
         const int in_band = id - band * kBand * tiles_n;
-        const int tile_m = band_m0 + in_band % band_rows;
-        const int tile_n = in_band / band_rows;
-        const int m0 = tile_m * Cfg::BM;
-        const int n0 = tile_n * Cfg::BN;
-        const i32x4 rsrc_a = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)min(Cfg::BM, M - m0) * lda);
-        const i32x4 rsrc_b = make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)min(Cfg::BN, N - n0) * ldb);
-        lds_barrier();  // every wave is done with the previous tile's LDS slots
+        m0 = (band_m0 + in_band % band_rows) * Cfg::BM;
+        n0 = (in_band / band_rows) * Cfg::BN;
+    };
 
-        auto issue_stage = [&](int kt) {
-            const uint32_t base = lds0 + (uint32_t)(kt % STAGES) * Cfg::STAGE_BYTES;
-            const uint32_t ka = (uint32_t)kt * RA, kb = (uint32_t)kt * RB;
-#pragma unroll
-            for (int i = 0; i < NA; ++i) {
-                const uint32_t off = (ka + a_col[i] < lda) ? a_off[i] + ka : kOutOfRange;
-                dma16(rsrc_a, off, base + (uint32_t)(wave * NA + i) * 1024u);
-            }
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const uint32_t off = (kb + b_col[i] < ldb) ? b_off[i] + kb : kOutOfRange;
-                dma16(rsrc_b, off, base + Cfg::A_BYTES + (uint32_t)(wave * NB + i) * 1024u);
-            }
-        };
+    int v = blockIdx.x;
+    int m0, n0;
+    tile_origin(v, m0, n0);
+    i32x4 rsrc_a, rsrc_b;
+    auto set_rsrc = [&]() {
+        rsrc_a = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)min(Cfg::BM, M - m0) * lda);
+        rsrc_b = make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)min(Cfg::BN, N - n0) * ldb);
+    };
+    set_rsrc();
 
-        i32x16 acc[FN][FM];
+    // DMA instructions [lo, hi) of stage kt (A's first, then B's) into its
+    // ring slot.  Past K every offset is out of range: the slot fills with
+    // zeros.
+    auto issue_range = [&](int kt, int lo, int hi) {
+        const uint32_t base = lds0 + (uint32_t)(kt % STAGES) * Cfg::STAGE_BYTES;
+        const uint32_t ka = (uint32_t)kt * RA, kb = (uint32_t)kt * RB;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            if (i < lo || i >= hi) continue;
+            const uint32_t off = (ka + a_col[i] < lda) ? a_off[i] + ka : kOutOfRange;
+            dma16(rsrc_a, off, base + (uint32_t)(wave * NA + i) * 1024u);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (NA + i < lo || NA + i >= hi) continue;
+            const uint32_t off = (kb + b_col[i] < ldb) ? b_off[i] + kb : kOutOfRange;
+            dma16(rsrc_b, off, base + Cfg::A_BYTES + (uint32_t)(wave * NB + i) * 1024u);
+        }
+    };
+    auto issue_stage = [&](int kt) { issue_range(kt, 0, NA + NB); };
+
+    const int h = lane >> 5;    // which 16-k half of an MFMA operand this lane feeds
+    const int r32 = lane & 31;  // operand row inside a 32-row block
+
+    // Raw (still packed / int8) fragments of one 64-k step, as read from LDS.
+    constexpr int AV = (VAR == I4I4) ? 1 : 2;  // 16-byte vectors per A block row
+    struct Frags {
+        i32x4 b[FN];
+        i32x4 a[FM][AV];
+    };
+    auto read_frags = [&](int slot, int step, Frags &f) {
+        const uint8_t *sa = smem + slot * Cfg::STAGE_BYTES;
+        const uint8_t *sb = sa + Cfg::A_BYTES;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int row = (wn * FN + fn) * 32 + r32;
+            f.b[fn] = *reinterpret_cast<const i32x4 *>(sb + 16 * lds_chunk<CPR_B>(row, 2 * step + h));
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int row = (wm * FM + fm) * 32 + r32;
+#pragma unroll
+            for (int v = 0; v < AV; ++v) {
+                const int col = (VAR == I4I4) ? 2 * step + h : 4 * step + 2 * h + v;
+                f.a[fm][v] = *reinterpret_cast<const i32x4 *>(sa + 16 * lds_chunk<CPR_A>(row, col));
+            }
+        }
+    };
+
+    i32x16 acc[FN][FM];
+    // Unpack and contract one 64-k step: per block two 32x32x32 MFMAs.
+    auto compute = [&](const Frags &f) {
+        i32x4 a_lo[FM], a_hi[FM];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            i32x4 b_lo, b_hi;
+            unpack_chunk<VAR == W4A8>(f.b[fn], b_lo, b_hi);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                if (fn == 0) {
+                    if (VAR == I4I4) {
+                        unpack_chunk<false>(f.a[fm][0], a_lo[fm], a_hi[fm]);
+                    } else {
+                        a_lo[fm] = f.a[fm][0];
+                        a_hi[fm] = f.a[fm][AV - 1];
+                    }
+                }
+                acc[fn][fm] = mfma_32x32x32(b_lo, a_lo[fm], acc[fn][fm]);
+                acc[fn][fm] = mfma_32x32x32(b_hi, a_hi[fm], acc[fn][fm]);
+            }
+        }
+    };
+
+    // Scheduling pattern of one 64-k step: the first operands' unpack, then
+    // each MFMA followed by its share of the remaining unpack work, with the
+    // next step's LDS reads spread in between, so that one wave per SIMD
+    // keeps both the MFMA pipe and the VALU busy (instructions issue in
+    // order, so VALU work overlaps an MFMA only when placed after it).
+    auto interleave = [&]() {
+        if constexpr (SCHED == 2) {
+            // The next step's LDS reads first (the longest latency), then the
+            // first operands' unpack, then each MFMA followed by its share of
+            // the remaining unpack.
+            constexpr int kMfma = 2 * FM * FN;
+            constexpr int kValuPerDword = (VAR == I4I4) ? 3 : 5;
+            constexpr int kValu = 8 * kValuPerDword * FN + (VAR == I4I4 ? 8 * 3 * FM : 0);
+            constexpr int kFirst = 8 * kValuPerDword + (VAR == I4I4 ? 8 * 3 : 0);
+            constexpr int kRest = kValu - kFirst;
+            constexpr int kPer = (kRest + kMfma - 1) / kMfma;
+            constexpr int kReads = FN + FM * AV;
+            __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kFirst, 0);
+#pragma unroll
+            for (int i = 0; i < kMfma; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);
+            }
+        } else if constexpr (SCHED == 1) {
+            constexpr int kMfma = 2 * FM * FN;
+            constexpr int kValuPerDword = (VAR == I4I4) ? 3 : 5;
+            constexpr int kValu = 8 * kValuPerDword * FN + (VAR == I4I4 ? 8 * 3 * FM : 0);
+            constexpr int kFirst = 8 * kValuPerDword + (VAR == I4I4 ? 8 * 3 : 0);
+            constexpr int kRest = kValu - kFirst;
+            constexpr int kPer = (kRest + kMfma - 1) / kMfma;
+            constexpr int kReads = FN + FM * AV;
+            constexpr int kReadEvery = (kMfma + kReads - 1) / kReads;
+            __builtin_amdgcn_sched_group_barrier(0x002, kFirst, 0);
+#pragma unroll
+            for (int i = 0; i < kMfma; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);
+                if (i % kReadEvery == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+    };
+
+    // Wait until this wave's loads of the stage issued `after` stages before
+    // the newest one have landed (loads complete in issue order).
+    auto wait_tiles_after = [&](int after) {
+        if (after >= 4)
+            wait_vmcnt<4 * kPerStage>();
+        else if (after >= 3)
+            wait_vmcnt<3 * kPerStage>();
+        else if (after == 2)
+            wait_vmcnt<2 * kPerStage>();
+        else if (after == 1)
+            wait_vmcnt<kPerStage>();
+        else
+            wait_vmcnt<0>();
+    };
+
+    // Stages 0 .. kPrologue-1 of the first tile.  Slots past the last K tile
+    // are filled too (with zeros: every offset is out of range), which keeps
+    // the number of loads in flight the same in every iteration.
+#pragma unroll
+    for (int s = 0; s < kPrologue; ++s) issue_stage(s);
+    bool stores_pending = false;  // a full tile's stores were issued after the prologue
+
+    for (;;) {
+        // Stage 0 of this tile has landed.  The previous tile's stores were
+        // issued after this tile's prologue loads, so they may stay in flight.
+        if (stores_pending)
+            wait_vmcnt<(kPrologue - 1) * kPerStage + kStores>();
+        else
+            wait_vmcnt<(kPrologue - 1) * kPerStage>();
+        lds_barrier();
+
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j) acc[i][j] = i32x16{};
-
-        const int h = lane >> 5;    // which 16-k half of an MFMA operand this lane feeds
-        const int r32 = lane & 31;  // operand row inside a 32-row block
-
-        // Raw (still packed / int8) fragments of one 64-k step, as read from LDS.
-        constexpr int AV = (VAR == I4I4) ? 1 : 2;  // 16-byte vectors per A block row
-        struct Frags {
-            i32x4 b[FN];
-            i32x4 a[FM][AV];
-        };
-        auto read_frags = [&](int slot, int step, Frags &f) {
-            const uint8_t *sa = smem + slot * Cfg::STAGE_BYTES;
-            const uint8_t *sb = sa + Cfg::A_BYTES;
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int row = (wn * FN + fn) * 32 + r32;
-                f.b[fn] = *reinterpret_cast<const i32x4 *>(sb + 16 * lds_chunk<CPR_B>(row, 2 * step + h));
-            }
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int row = (wm * FM + fm) * 32 + r32;
-#pragma unroll
-                for (int v = 0; v < AV; ++v) {
-                    const int col = (VAR == I4I4) ? 2 * step + h : 4 * step + 2 * h + v;
-                    f.a[fm][v] = *reinterpret_cast<const i32x4 *>(sa + 16 * lds_chunk<CPR_A>(row, col));
-                }
-            }
-        };
-        // Unpack and contract one 64-k step: per block two 32x32x32 MFMAs.
-        auto compute = [&](const Frags &f) {
-            i32x4 a_lo[FM], a_hi[FM];
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                i32x4 b_lo, b_hi;
-                unpack_chunk<VAR == W4A8>(f.b[fn], b_lo, b_hi);
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    if (fn == 0) {
-                        if (VAR == I4I4) {
-                            unpack_chunk<false>(f.a[fm][0], a_lo[fm], a_hi[fm]);
-                        } else {
-                            a_lo[fm] = f.a[fm][0];
-                            a_hi[fm] = f.a[fm][AV - 1];
-                        }
-                    }
-                    acc[fn][fm] = mfma_32x32x32(b_lo, a_lo[fm], acc[fn][fm]);
-                    acc[fn][fm] = mfma_32x32x32(b_hi, a_hi[fm], acc[fn][fm]);
-                }
-            }
-        };
-
-        // Scheduling pattern of one 64-k step: the first operands' unpack, then
-        // each MFMA followed by its share of the remaining unpack work, with the
-        // next step's LDS reads spread in between, so that one wave per SIMD
-        // keeps both the MFMA pipe and the VALU busy (instructions issue in
-        // order, so VALU work overlaps an MFMA only when placed after it).
-        auto interleave = [&]() {
-            if constexpr (SCHED) {
-                constexpr int kMfma = 2 * FM * FN;
-                constexpr int kValuPerDword = (VAR == I4I4) ? 3 : 5;
-                constexpr int kValu = 8 * kValuPerDword * FN + (VAR == I4I4 ? 8 * 3 * FM : 0);
-                constexpr int kFirst = 8 * kValuPerDword + (VAR == I4I4 ? 8 * 3 : 0);
-                constexpr int kRest = kValu - kFirst;
-                constexpr int kPer = (kRest + kMfma - 1) / kMfma;
-                constexpr int kReads = FN + FM * AV;
-                constexpr int kReadEvery = (kMfma + kReads - 1) / kReads;
-                __builtin_amdgcn_sched_group_barrier(0x002, kFirst, 0);
-#pragma unroll
-                for (int i = 0; i < kMfma; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);
-                    if (i % kReadEvery == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            }
-        };
-
-        constexpr int STEPS = BK / 64;
-        constexpr int kPerStage = NA + NB;
-        // Wait until this wave's loads of the tile issued `after` tiles before the
-        // newest one have landed.
-        auto wait_tiles_after = [&](int after) {
-            if (after >= 4)
-                wait_vmcnt<4 * kPerStage>();
-            else if (after >= 3)
-                wait_vmcnt<3 * kPerStage>();
-            else if (after == 2)
-                wait_vmcnt<2 * kPerStage>();
-            else if (after == 1)
-                wait_vmcnt<kPerStage>();
-            else
-                wait_vmcnt<0>();
-        };
-
-        // Prologue: fill every ring slot, then read step 0 of tile 0.  Slots past
-        // the last tile are filled too (with zeros: every offset is out of range),
-        // which keeps the number of loads in flight the same in every iteration.
-#pragma unroll
-        for (int s = 0; s < STAGES; ++s) issue_stage(s);
-        wait_tiles_after(STAGES - 1);
-        lds_barrier();
         Frags cur, nxt;
         read_frags(0, 0, cur);
 
-        // Steady state: every tile but the last.  The tile's last step waits for
-        // tile kt+1, passes the barrier (every wave is done reading tile kt),
-        // refills tile kt's slot with tile kt+STAGES and reads step 0 of tile kt+1.
+        // Steady state: every K tile but the last.  The tile's last step waits
+        // for tile kt+1, passes the barrier (every wave is done reading tile
+        // kt) and reads step 0 of tile kt+1.  Tile kt's slot is refilled with
+        // tile kt+STAGES right after that barrier, or (spread issue) in a share
+        // per step of tile kt+1, so that DMA requests reach the memory
+        // pipeline a few at a time between MFMAs.
+        constexpr int kShare = (kPerStage + STEPS - 1) / STEPS;
         for (int kt = 0; kt + 1 < ktiles; ++kt) {
             const int slot = kt % STAGES;
 #pragma unroll
             for (int st = 0; st < STEPS; ++st) {
+                if constexpr (SPREAD) issue_range(kt + STAGES - 1, st * kShare, (st + 1) * kShare);
                 if (st + 1 < STEPS) {
                     read_frags(slot, st + 1, nxt);
                 } else {
                     wait_tiles_after(STAGES - 2);
                     lds_barrier();
-                    issue_stage(kt + STAGES);
+                    if constexpr (!SPREAD) issue_stage(kt + STAGES);
                     read_frags((kt + 1) % STAGES, 0, nxt);
                 }
                 compute(cur);
@@ -319,7 +331,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipelined_kernel(
                 cur = nxt;
             }
         }
-        // Last tile.
+        // Last K tile.
         {
             const int slot = (ktiles - 1) % STAGES;
 #pragma unroll
@@ -332,18 +344,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipelined_kernel(
         }
         wait_vmcnt<0>();  // the zero-fill loads past the end
 
+        // Start the next tile's loads before this tile's stores, so that the
+        // first wait of the next tile does not also wait for the stores.
+        const int tm0 = m0, tn0 = n0;
+        const int vn = v + (int)gridDim.x;
+        lds_barrier();  // every wave is done reading this tile's slots
+        if (vn < nblocks) {
+            tile_origin(vn, m0, n0);
+            set_rsrc();
+#pragma unroll
+            for (int s = 0; s < kPrologue; ++s) issue_stage(s);
+        }
+
         // Epilogue: lane holds C[m][n .. n+3] for m = l%32 of each column block.
         const bool vec_ok = (N % 4) == 0;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                const int m = m0 + (wm * FM + fm) * 32 + r32;
+                const int m = tm0 + (wm * FM + fm) * 32 + r32;
                 if (m >= M) continue;
                 int32_t *crow = C + (int64_t)m * N;
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    const int n = n0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h;
+                    const int n = tn0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h;
                     const i32x4 v = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
                                           acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
                                     Cfg::SHIFT;
@@ -357,8 +381,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipelined_kernel(
                     }
                 }
             }
-    }  // tile loop
-
+        if (vn >= nblocks) break;
+        stores_pending = vec_ok && tm0 + Cfg::BM <= M && tn0 + Cfg::BN <= N;
+        v = vn;
+    }
 }
 
 }  // namespace lpgemm

@@ -1,95 +1,128 @@
 // gemm_skinny.hpp -- narrow-M W4A8 kernel for gfx950 (decode-like shapes).
 //
 // For M <= 16 the product is bound by reading the packed weights B once from
-// HBM.  Design:
-//   * workgroup = KW waves; wave w owns the w-th slice of K (KSTEPS steps of
-//     128 logical k) for the whole kernel and keeps the matching fragments of
-//     A (rows zero-padded to 16) in registers, loaded once;
-//   * the workgroup walks strips of 16 rows of B (grid-stride); for each strip
-//     a wave issues all KSTEPS of its 16-byte-per-lane loads at once, two
-//     strips ahead of the strip it computes (three register sets used in
-//     turn: no copy ever waits on a prefetch), so about 128 KB per compute
-//     unit stay in flight;
-//   * loads are raw buffer loads: rows past N come back as zeros from the
-//     range check, steps past K use an out-of-range offset -- no branches;
-//   * nibbles are unpacked in registers and contracted with
-//     v_mfma_i32_16x16x64_i8, B as the MFMA's 16-row operand and A as its
-//     16-column operand (the w4a8 page's kernel also puts the dequantised B
-//     first and produces C^T), so each lane ends with four consecutive n of
-//     one m;
-//   * the KW partial tiles are summed in LDS in a fixed order (exact; no
-//     atomics, no memset) and wave 0 stores the strip of C.
-//
-// Requirements (checked on the host): M <= 16, K % 32 == 0, 16-byte aligned
-// bases, N * K / 2 < 2^31, KW * KSTEPS * 128 >= K, at most 256 workgroups
-// (so offsets of the strips prefetched past the end still fit 32 bits).
+// HBM, so the kernel is built around streaming B at full bandwidth.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace lpgemm {
 
+// B reaches LDS through direct-to-LDS buffer loads in which every instruction
+// reads 1 KB of one row, so HBM sees long row-linear bursts (a lane-per-row
+// register load, 16 rows x 64 bytes per instruction, streams markedly slower).
+//
+//   * workgroup = KW waves, one per compute unit, walking strips of 16 rows
+//     of B (grid-stride); two LDS strip buffers, the next strip's loads in
+//     flight while the current strip is contracted;
+//   * strip layout in LDS: row-major, 16-byte chunks, chunk c of row r stored
+//     at position c ^ (r % 16) when a row holds a multiple of 16 chunks (the
+//     MFMA fragment reads of 16 rows at one k then hit 16 distinct bank
+//     groups); each DMA instruction still covers one contiguous 1 KB span;
+//   * wave w owns the w-th slice of K (KSTEPS steps of 128 logical k) for the
+//     whole kernel and keeps the matching A fragments (rows zero-padded to
+//     16, read once) in registers; fragments of B come from LDS with
+//     ds_read_b128, are unpacked in registers and contracted with
+//     v_mfma_i32_16x16x64_i8, B as the MFMA's 16-row operand and A as its
+//     16-column operand (the w4a8 page's kernel also puts the dequantised B
+//     first and produces C^T), so each lane ends with four consecutive n of
+//     one m;
+//   * the KW partial tiles of a strip are summed in LDS in a fixed order by
+//     one wave (rotating) after the next iteration's barrier, so one barrier
+//     per strip suffices and C stores overlap the next strip's work.
+//
+// Requirements (checked on the host): M <= 16, K % 32 == 0, 16-byte aligned
+// bases, N * K / 2 < 2^31, KW * KSTEPS * 128 >= K, at most 256 workgroups.
+template <int KW, int KSTEPS>
+struct SkinnyCfg {
+    static constexpr int kBufBytes = KW * KSTEPS * 1024;  // one strip (16 rows x K/2 bytes, padded)
+    static constexpr int kRedBytes = 2 * KW * 64 * 16;
+    static constexpr int kLdsBytes = 2 * kBufBytes + kRedBytes;
+    static_assert(kLdsBytes <= 160 * 1024, "strip buffers exceed the LDS");
+};
+
 template <int KW, int KSTEPS>
 __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B, int32_t *__restrict__ C, int M,
     int N, int K)
 {
-    constexpr uint32_t kOut = 0x80000000u;  // an offset no resource here reaches
-    __shared__ i32x4 red[2][KW][64];
+    using Cfg = SkinnyCfg<KW, KSTEPS>;
+    extern __shared__ __align__(1024) uint8_t smem[];
+    i32x4 *red = reinterpret_cast<i32x4 *>(smem + 2 * Cfg::kBufBytes);  // [2][KW][64]
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int g = lane >> 4;    // k group this lane feeds
-    const int r16 = lane & 15;  // operand row (n for B, m for A)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
     const int strips = (N + 15) / 16;
     const uint32_t ldb = (uint32_t)K / 2;
+    const int cpr = (int)(ldb / 16);               // 16-byte chunks per row
+    const int swz_mask = (cpr % 16 == 0) ? 15 : 0;  // XOR swizzle only when it stays in the row
     const int k_begin = wave * (KSTEPS * 128);
 
     const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(A, (uint32_t)M * (uint32_t)K);
-    const __amdgpu_buffer_rsrc_t rsrc_b = buffer_rsrc(B, (uint32_t)N * ldb);
+    const i32x4 rsrc_b = make_rsrc(B, (uint32_t)N * ldb);
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
-    // A fragments of this wave's K slice: step j covers logical k
-    // k_begin + 128 j + [32 g, 32 g + 32) of row r16, as two 16-byte halves.
-    // Rows past M lie past the resource and read as zeros.
+    // A fragments of this wave's K slice (zeros past K and past M).
     i32x4 a_lo[KSTEPS], a_hi[KSTEPS];
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
         const int kl = k_begin + 128 * j + 32 * g;
-        const uint32_t off = kl < K ? (uint32_t)r16 * (uint32_t)K + (uint32_t)kl : kOut;
+        const uint32_t off = kl < K ? (uint32_t)r16 * (uint32_t)K + (uint32_t)kl : kOutOfRange;
         a_lo[j] = buffer_load16(rsrc_a, off);
-        a_hi[j] = buffer_load16(rsrc_a, off == kOut ? kOut : off + 16);
+        a_hi[j] = buffer_load16(rsrc_a, off == kOutOfRange ? kOutOfRange : off + 16);
     }
 
-    // Packed B of strip s for every step of this wave's slice (16 bytes per
-    // lane per step: logical k k_begin + 128 j + [32 g, 32 g + 32) of row n).
-    auto load_strip = [&](int s, i32x4(&q)[KSTEPS]) {
-        const uint32_t row_off = (uint32_t)(s * 16 + r16) * ldb;
+    // DMA of strip s into buffer b: this wave's instructions are KSTEPS
+    // consecutive 1 KB pieces of the buffer; lane l of piece j fetches the
+    // global chunk stored at buffer position q = 64 j + l.
+    uint32_t dma_row_off[KSTEPS];
+    bool dma_live[KSTEPS];
 #pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) {
-            const int kl = k_begin + 128 * j + 32 * g;
-            q[j] = buffer_load16(rsrc_b, kl < K ? row_off + (uint32_t)kl / 2 : kOut);
-        }
+    for (int t = 0; t < KSTEPS; ++t) {
+        const int q = (wave * KSTEPS + t) * 64 + lane;
+        const int row = q / cpr, slot = q % cpr;
+        dma_live[t] = row < 16;
+        dma_row_off[t] = (uint32_t)row * ldb + 16u * (uint32_t)(slot ^ (row & swz_mask));
+    }
+    auto issue_strip = [&](int s, int b) {
+        const uint32_t base = (uint32_t)s * 16u * ldb;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t)
+            dma16(rsrc_b, dma_live[t] ? base + dma_row_off[t] : kOutOfRange,
+                  lds0 + (uint32_t)b * Cfg::kBufBytes + (uint32_t)(wave * KSTEPS + t) * 1024u);
     };
 
-    int buf = 0;
-    auto do_strip = [&](int s, const i32x4(&q)[KSTEPS]) {
-        i32x4 acc = {0, 0, 0, 0};
+    // Fragment addresses in a strip buffer: step t reads chunk kc of row r16.
+    uint32_t frag_off[KSTEPS];
 #pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) {
-            i32x4 b_lo, b_hi;
-            unpack_chunk<true>(q[j], b_lo, b_hi);
-            acc = mfma_16x16x64(b_lo, a_lo[j], acc);
-            acc = mfma_16x16x64(b_hi, a_hi[j], acc);
-        }
-        red[buf][wave][lane] = acc;
-        lds_barrier();
-        if (wave == 0) {
-            i32x4 sum = red[buf][0][lane];
+    for (int t = 0; t < KSTEPS; ++t) {
+        int kc = (k_begin + 128 * t) / 32 + g;
+        kc = kc < cpr ? kc : cpr - 1;  // past K: A is zero there, any in-strip data will do
+        frag_off[t] = 16u * (uint32_t)(r16 * cpr + (kc ^ (r16 & swz_mask)));
+    }
+
+    const int G = gridDim.x;
+    int s = blockIdx.x;
+    if (s >= strips) return;
+    issue_strip(s, 0);
+    int it = 0;
+    int prev = -1;  // strip whose partial tiles await reduction
+    for (;;) {
+        const int b = it & 1;
+        wait_vmcnt<0>();
+        lds_barrier();  // strip s is in buffer b; partial tiles of `prev` are in red[b ^ 1]
+
+        // Reduce and store the previous strip (one wave, rotating).
+        if (prev >= 0 && wave == (it - 1) % KW) {
+            const i32x4 *rp = red + (b ^ 1) * KW * 64;
+            i32x4 sum = rp[lane];
 #pragma unroll
-            for (int w = 1; w < KW; ++w) sum += red[buf][w][lane];
+            for (int w = 1; w < KW; ++w) sum += rp[w * 64 + lane];
             sum >>= 4;  // B carried a factor 16
             const int m = r16;
-            const int n = s * 16 + 4 * g;
+            const int n = prev * 16 + 4 * g;
             if (m < M) {
                 int32_t *crow = C + (int64_t)m * N;
                 if ((N % 4) == 0 && n + 3 < N) {
@@ -102,33 +135,49 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
                 }
             }
         }
-        // The next strip writes the other half of `red`, so one barrier per
-        // strip suffices: wave 0 has finished reading this half before any
-        // wave passes the next strip's barrier.
-        buf ^= 1;
-    };
+        // Next strip's loads into the other buffer (its last readers passed
+        // the barrier above).
+        const int sn = s + G;
+        if (sn < strips) issue_strip(sn, b ^ 1);
 
-    // Strips are prefetched two ahead into three register sets used in turn.
-    // The prefetch is unconditional: a strip past the end reads zeros (its
-    // offsets lie past the resource), which keeps the number of loads in
-    // flight fixed so the compiler waits only for the strip being computed.
-    const int G = gridDim.x;
-    int s = blockIdx.x;
-    i32x4 q0[KSTEPS], q1[KSTEPS], q2[KSTEPS];
-    load_strip(s, q0);
-    load_strip(s + G, q1);
-    while (s < strips) {
-        load_strip(s + 2 * G, q2);
-        do_strip(s, q0);
-        s += G;
-        if (s >= strips) break;
-        load_strip(s + 2 * G, q0);
-        do_strip(s, q1);
-        s += G;
-        if (s >= strips) break;
-        load_strip(s + 2 * G, q1);
-        do_strip(s, q2);
-        s += G;
+        // Contract this wave's K slice of strip s.
+        const uint8_t *buf = smem + b * Cfg::kBufBytes;
+        i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            const i32x4 q = *reinterpret_cast<const i32x4 *>(buf + frag_off[t]);
+            i32x4 b_lo, b_hi;
+            unpack_chunk<true>(q, b_lo, b_hi);
+            acc = mfma_16x16x64(b_lo, a_lo[t], acc);
+            acc = mfma_16x16x64(b_hi, a_hi[t], acc);
+        }
+        red[b * KW * 64 + wave * 64 + lane] = acc;
+        prev = s;
+        ++it;
+        if (sn >= strips) break;
+        s = sn;
+    }
+    // The last strip: every partial tile written, then one wave reduces it.
+    lds_barrier();
+    if (wave == (it - 1) % KW) {
+        const i32x4 *rp = red + ((it - 1) & 1) * KW * 64;
+        i32x4 sum = rp[lane];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) sum += rp[w * 64 + lane];
+        sum >>= 4;
+        const int m = r16;
+        const int n = prev * 16 + 4 * g;
+        if (m < M) {
+            int32_t *crow = C + (int64_t)m * N;
+            if ((N % 4) == 0 && n + 3 < N) {
+                *reinterpret_cast<i32x4 *>(crow + n) = sum;
+            } else {
+                if (n + 0 < N) crow[n + 0] = sum.x;
+                if (n + 1 < N) crow[n + 1] = sum.y;
+                if (n + 2 < N) crow[n + 2] = sum.z;
+                if (n + 3 < N) crow[n + 3] = sum.w;
+            }
+        }
     }
 }
 

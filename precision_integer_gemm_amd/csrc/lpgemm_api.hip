@@ -48,7 +48,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 template <int VAR, int FM, int FN, int WM, int WN, int BK, int ST>
 struct TiledKernel {
     using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, ST>;
-    static void *fn() { return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, BK, ST, false>); }
+    static void *fn() { return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, BK, ST, 0>); }
 };
 using I4Large = TiledKernel<I4I4, 4, 2, 2, 4, 256, 2>;
 using W8Large = TiledKernel<W4A8, 4, 2, 2, 4, 128, 3>;
@@ -57,7 +57,7 @@ using W8Small = TiledKernel<W4A8, 2, 2, 2, 2, 128, 3>;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 // Skinny: 8 waves split K (up to 8 steps of 128 k each, A held in registers);
-// one workgroup per compute unit walks strips of 16 rows of B.
+// one workgroup per compute unit walks strips of 16 rows of B, staged in LDS.
 constexpr int kSkinnyKW = 8;
 constexpr int kSkinnyMaxM = 16;
 constexpr int kSkinnyMaxK = kSkinnyKW * 8 * 128;
@@ -181,6 +181,28 @@ lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, in
     return e == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
 }
 
+// Launch the narrow-M kernel for K up to KSTEPS * 1024; the first launch on
+// each device raises its dynamic-LDS limit to the two strip buffers.
+template <int KSTEPS>
+lpgemm_status launch_skinny(const Plan &p, const int8_t *a, const uint8_t *b, int32_t *C, int m,
+                            int n, int k, hipStream_t stream)
+{
+    using Cfg = SkinnyCfg<kSkinnyKW, KSTEPS>;
+    static std::once_flag once[kMaxDevices];
+    static hipError_t attr_err[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERR_HIP;
+    std::call_once(once[dev], [dev] {
+        attr_err[dev] = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&gemm_w4a8_skinny_kernel<kSkinnyKW, KSTEPS>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
+    });
+    if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
+    hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, KSTEPS>), dim3((unsigned)p.workgroups),
+                       dim3(p.threads), Cfg::kLdsBytes, stream, a, b, C, m, n, k);
+    return launched();
+}
+
 lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, int32_t *C,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {
@@ -219,14 +241,12 @@ lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, int
     }
     case LPGEMM_KERNEL_SKINNY: {
         const int8_t *a8 = static_cast<const int8_t *>(A);
-        const dim3 grid((unsigned)p.workgroups), block(p.threads);
         switch (p.k_steps) {
-        case 1: hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, 1>), grid, block, 0, stream, a8, b, C, m, n, k); break;
-        case 2: hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, 2>), grid, block, 0, stream, a8, b, C, m, n, k); break;
-        case 4: hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, 4>), grid, block, 0, stream, a8, b, C, m, n, k); break;
-        default: hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, 8>), grid, block, 0, stream, a8, b, C, m, n, k); break;
+        case 1: return launch_skinny<1>(p, a8, b, C, m, n, k, stream);
+        case 2: return launch_skinny<2>(p, a8, b, C, m, n, k, stream);
+        case 4: return launch_skinny<4>(p, a8, b, C, m, n, k, stream);
+        default: return launch_skinny<8>(p, a8, b, C, m, n, k, stream);
         }
-        break;
     }
     default:
         return LPGEMM_ERR_INVALID_ARG;
