@@ -26,8 +26,9 @@
 //
 // Epilogue (a5): exact >> 8 (int4 x int4) or >> 4 (W4A8), masked stores.
 //
-// Tile order: persistent workgroups loop over tiles (stores of one tile drain
-// under the next tile's work); workgroup b runs on XCD b % 8 and tiles are
+// Tile order: persistent workgroups loop over tiles; the next tile's first
+// loads are issued before the current tile's stores, so the stores drain
+// under the next tile's work.  Workgroup b runs on XCD b % 8 and tiles are
 // renumbered so each XCD walks a compact band of C (shared A rows and B
 // columns in its L2).
 //
@@ -73,21 +74,18 @@ __device__ __forceinline__ int lds_chunk(int row, int col)
     return row * CPR + (col ^ ((row / rows_per_256) % CPR));
 }
 
-template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, int SCHED, bool SPREAD = false>
+template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pipelined_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int32_t *__restrict__ C, int M,
     int N, int K, int tiles_m, int tiles_n, int xcds)
 {
     using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, STAGES>;
     static_assert(Cfg::kFits, "LDS ring does not fit in 160 KB");
-    static_assert(!SPREAD || STAGES >= 3, "spread issue needs a slot of slack");
     constexpr int RA = Cfg::RA, RB = Cfg::RB, CPR_A = Cfg::CPR_A, CPR_B = Cfg::CPR_B;
     constexpr int NA = Cfg::NA, NB = Cfg::NB;
     constexpr int STEPS = BK / 64;
     constexpr int kPerStage = NA + NB;  // DMA instructions per wave per stage
-    // Stages loaded before a tile's first step: all of them, or all but the
-    // one that the first tile's steps issue piece by piece.
-    constexpr int kPrologue = SPREAD ? STAGES - 1 : STAGES;
+    constexpr int kPrologue = STAGES;  // stages loaded before a tile's first step
     // 16-byte stores per wave for a tile with no edge (a lower bound on the
     // vector-memory instructions its epilogue issues).
     constexpr int kStores = FN * FM * 4;
@@ -152,26 +150,22 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     };
     set_rsrc();
 
-    // DMA instructions [lo, hi) of stage kt (A's first, then B's) into its
-    // ring slot.  Past K every offset is out of range: the slot fills with
-    // zeros.
-    auto issue_range = [&](int kt, int lo, int hi) {
+    // DMA of stage kt (A's rows, then B's) into its ring slot.  Past K every
+    // offset is out of range: the slot fills with zeros.
+    auto issue_stage = [&](int kt) {
         const uint32_t base = lds0 + (uint32_t)(kt % STAGES) * Cfg::STAGE_BYTES;
         const uint32_t ka = (uint32_t)kt * RA, kb = (uint32_t)kt * RB;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            if (i < lo || i >= hi) continue;
             const uint32_t off = (ka + a_col[i] < lda) ? a_off[i] + ka : kOutOfRange;
             dma16(rsrc_a, off, base + (uint32_t)(wave * NA + i) * 1024u);
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            if (NA + i < lo || NA + i >= hi) continue;
             const uint32_t off = (kb + b_col[i] < ldb) ? b_off[i] + kb : kOutOfRange;
             dma16(rsrc_b, off, base + Cfg::A_BYTES + (uint32_t)(wave * NB + i) * 1024u);
         }
     };
-    auto issue_stage = [&](int kt) { issue_range(kt, 0, NA + NB); };
 
     const int h = lane >> 5;    // which 16-k half of an MFMA operand this lane feeds
     const int r32 = lane & 31;  // operand row inside a 32-row block
@@ -225,49 +219,6 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
         }
     };
 
-    // Scheduling pattern of one 64-k step: the first operands' unpack, then
-    // each MFMA followed by its share of the remaining unpack work, with the
-    // next step's LDS reads spread in between, so that one wave per SIMD
-    // keeps both the MFMA pipe and the VALU busy (instructions issue in
-    // order, so VALU work overlaps an MFMA only when placed after it).
-    auto interleave = [&]() {
-        if constexpr (SCHED == 2) {
-            // The next step's LDS reads first (the longest latency), then the
-            // first operands' unpack, then each MFMA followed by its share of
-            // the remaining unpack.
-            constexpr int kMfma = 2 * FM * FN;
-            constexpr int kValuPerDword = (VAR == I4I4) ? 3 : 5;
-            constexpr int kValu = 8 * kValuPerDword * FN + (VAR == I4I4 ? 8 * 3 * FM : 0);
-            constexpr int kFirst = 8 * kValuPerDword + (VAR == I4I4 ? 8 * 3 : 0);
-            constexpr int kRest = kValu - kFirst;
-            constexpr int kPer = (kRest + kMfma - 1) / kMfma;
-            constexpr int kReads = FN + FM * AV;
-            __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, kFirst, 0);
-#pragma unroll
-            for (int i = 0; i < kMfma; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);
-            }
-        } else if constexpr (SCHED == 1) {
-            constexpr int kMfma = 2 * FM * FN;
-            constexpr int kValuPerDword = (VAR == I4I4) ? 3 : 5;
-            constexpr int kValu = 8 * kValuPerDword * FN + (VAR == I4I4 ? 8 * 3 * FM : 0);
-            constexpr int kFirst = 8 * kValuPerDword + (VAR == I4I4 ? 8 * 3 : 0);
-            constexpr int kRest = kValu - kFirst;
-            constexpr int kPer = (kRest + kMfma - 1) / kMfma;
-            constexpr int kReads = FN + FM * AV;
-            constexpr int kReadEvery = (kMfma + kReads - 1) / kReads;
-            __builtin_amdgcn_sched_group_barrier(0x002, kFirst, 0);
-#pragma unroll
-            for (int i = 0; i < kMfma; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);
-                if (i % kReadEvery == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        }
-    };
-
     // Wait until this wave's loads of the stage issued `after` stages before
     // the newest one have landed (loads complete in issue order).
     auto wait_tiles_after = [&](int after) {
@@ -308,26 +259,21 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
 
         // Steady state: every K tile but the last.  The tile's last step waits
         // for tile kt+1, passes the barrier (every wave is done reading tile
-        // kt) and reads step 0 of tile kt+1.  Tile kt's slot is refilled with
-        // tile kt+STAGES right after that barrier, or (spread issue) in a share
-        // per step of tile kt+1, so that DMA requests reach the memory
-        // pipeline a few at a time between MFMAs.
-        constexpr int kShare = (kPerStage + STEPS - 1) / STEPS;
+        // kt), refills tile kt's slot with tile kt+STAGES and reads step 0 of
+        // tile kt+1.
         for (int kt = 0; kt + 1 < ktiles; ++kt) {
             const int slot = kt % STAGES;
 #pragma unroll
             for (int st = 0; st < STEPS; ++st) {
-                if constexpr (SPREAD) issue_range(kt + STAGES - 1, st * kShare, (st + 1) * kShare);
                 if (st + 1 < STEPS) {
                     read_frags(slot, st + 1, nxt);
                 } else {
                     wait_tiles_after(STAGES - 2);
                     lds_barrier();
-                    if constexpr (!SPREAD) issue_stage(kt + STAGES);
+                    issue_stage(kt + STAGES);
                     read_frags((kt + 1) % STAGES, 0, nxt);
                 }
                 compute(cur);
-                interleave();
                 cur = nxt;
             }
         }
@@ -338,7 +284,6 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
             for (int st = 0; st < STEPS; ++st) {
                 if (st + 1 < STEPS) read_frags(slot, st + 1, nxt);
                 compute(cur);
-                interleave();
                 cur = nxt;
             }
         }

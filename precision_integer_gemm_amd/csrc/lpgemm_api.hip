@@ -48,7 +48,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 template <int VAR, int FM, int FN, int WM, int WN, int BK, int ST>
 struct TiledKernel {
     using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, ST>;
-    static void *fn() { return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, BK, ST, 0>); }
+    static void *fn() { return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, BK, ST>); }
 };
 using I4Large = TiledKernel<I4I4, 4, 2, 2, 4, 256, 2>;
 using W8Large = TiledKernel<W4A8, 4, 2, 2, 4, 128, 3>;
