@@ -16,7 +16,8 @@ stream it runs on; the per-launch averages give each workload's TOP/s and
 roofline fraction (`per_config`) and the dominant kernel's `roofline`.
 `per_config_isolated` times each workload alone (back-to-back launches, the
 decode-shape B rotated over copies larger than the MALL together), free of the
-write-back a previous workload leaves behind.
+write-back a previous workload leaves behind; `per_config_cold` times each
+workload after a 512 MiB write that evicts its operands from L2 and MALL.
 
 The CPU baseline times the oracle (plain C, OpenMP over rows) on the first
 rows of every workload, and those rows double as a bit-exact parity check of
@@ -92,6 +93,8 @@ def parse():
                     help="multiply-accumulates per workload in the CPU baseline sample")
     ap.add_argument("--isolated-reps", type=int, default=20,
                     help="back-to-back launches per workload for the isolated per-kernel times")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="launches per workload, each after a 512 MiB write that evicts L2 and MALL")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--trace-summary", metavar="CSV",
@@ -210,6 +213,7 @@ def main() -> int:
         t_roof, bound = roofline_time_s(c)
         rec = {"kernel": w["plan"]["kernel"], "avg_us": round(avg, 3),
                "median_us": round(float(np.median(us)), 3), "min_us": round(float(us.min()), 3),
+               "p90_us": round(float(np.percentile(us, 90)), 3),
                "tops": round(c.ops / (avg * 1e-6) / 1e12, 2),
                "gbs": round(c.alg_bytes / (avg * 1e-6) / 1e9, 1),
                "bound": bound, "roofline_frac": round(t_roof / (avg * 1e-6), 4)}
@@ -242,10 +246,37 @@ def main() -> int:
             med = float(np.median(us))
             t_roof, bound = roofline_time_s(c)
             isolated[c.name] = {"median_us": round(med, 3), "min_us": round(float(us.min()), 3),
+                                "p90_us": round(float(np.percentile(us, 90)), 3),
                                 "tops": round(c.ops / (med * 1e-6) / 1e12, 2),
                                 "gbs": round(c.alg_bytes / (med * 1e-6) / 1e9, 1),
                                 "bound": bound, "roofline_frac": round(t_roof / (med * 1e-6), 4)}
             del copies
+
+    # Each workload cold: before every timed launch a 512 MiB buffer is written
+    # (not timed), which evicts its operands from the L2s and the 256 MB MALL.
+    cold = {}
+    if args.cold_reps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for w in work:
+            c = w["case"]
+            evs = []
+            for j in range(args.cold_reps):
+                flush.fill_(j & 0xFF)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                call(w)
+                e1.record(stream)
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+            med = float(np.median(us))
+            t_roof, bound = roofline_time_s(c)
+            cold[c.name] = {"median_us": round(med, 3), "min_us": round(float(us.min()), 3),
+                            "p90_us": round(float(np.percentile(us, 90)), 3),
+                            "tops": round(c.ops / (med * 1e-6) / 1e12, 2),
+                            "gbs": round(c.alg_bytes / (med * 1e-6) / 1e9, 1),
+                            "bound": bound, "roofline_frac": round(t_roof / (med * 1e-6), 4)}
+        del flush
 
     _, dc, drec, davg = dominant
     if drec["bound"] == "mfma":
@@ -280,6 +311,7 @@ def main() -> int:
         "roofline": roof,
         "per_config": per_config,
         "per_config_isolated": isolated,
+        "per_config_cold": cold,
     }
 
     if not args.no_cpu:
