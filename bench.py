@@ -17,7 +17,9 @@ roofline fraction (`per_config`) and the dominant kernel's `roofline`.
 `per_config_isolated` times each workload alone (back-to-back launches, the
 decode-shape B rotated over copies larger than the MALL together), free of the
 write-back a previous workload leaves behind; `per_config_cold` times each
-workload after a 512 MiB write that evicts its operands from L2 and MALL.
+workload after a 512 MiB write that evicts its operands from L2 and MALL;
+`per_config_scaled_bf16` times the scaled product (per-row and per-column
+scales, bf16 output) of each workload alone.
 
 The CPU baseline times the oracle (plain C, OpenMP over rows) on the first
 rows of every workload, and those rows double as a bit-exact parity check of
@@ -252,6 +254,43 @@ def main() -> int:
                                 "bound": bound, "roofline_frac": round(t_roof / (med * 1e-6), 4)}
             del copies
 
+    # The scaled product (per-row / per-column scales, bf16 output) of every
+    # workload alone, timed like `per_config_isolated`: the same GEMM with the
+    # scaling epilogue; D is half the bytes of the int32 C.
+    scaled = {}
+    if args.isolated_reps > 0:
+        from precision_integer_gemm_amd.inputs import scale_vector
+        for w in work:
+            c = w["case"]
+            sa = torch.from_numpy(scale_vector(c.seed, 0, c.M)).to(dev)
+            sb = torch.from_numpy(scale_vector(c.seed, 1, c.N)).to(dev)
+            D = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
+            fn = L.lib().lpgemm_int4_int4_scaled if c.variant == "i4i4" else L.lib().lpgemm_w4a8_scaled
+            copies = [w["b"]] + [w["b"].clone() for _ in range(2 if c.b_bytes > (64 << 20) else 0)]
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.isolated_reps)]
+            for j in range(-1, args.isolated_reps):
+                if j >= 0:
+                    evs[j][0].record(stream)
+                st = fn(w["a"].data_ptr(), copies[max(j, 0) % len(copies)].data_ptr(), sa.data_ptr(),
+                        sb.data_ptr(), D.data_ptr(), L.OUT_BF16, c.M, c.N, c.K, handle)
+                if j >= 0:
+                    evs[j][1].record(stream)
+                if st != L.OK:
+                    raise RuntimeError(f"{c.name} scaled: {L.lpgemm_status_string(st)}")
+            torch.cuda.synchronize()
+            us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+            med = float(np.median(us))
+            d_bytes = c.a_bytes + c.b_bytes + 2 * c.M * c.N + 4 * (c.M + c.N)
+            t_mfma = c.ops / (PEAK_INT8_TOPS * 1e12)
+            t_hbm = d_bytes / (PEAK_HBM_GBS * 1e9)
+            scaled[c.name] = {"out": "bf16", "median_us": round(med, 3),
+                              "tops": round(c.ops / (med * 1e-6) / 1e12, 2),
+                              "gbs": round(d_bytes / (med * 1e-6) / 1e9, 1),
+                              "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                              "roofline_frac": round(max(t_mfma, t_hbm) / (med * 1e-6), 4)}
+            del copies, D
+
     # Each workload cold: before every timed launch a 512 MiB buffer is written
     # (not timed), which evicts its operands from the L2s and the 256 MB MALL.
     cold = {}
@@ -312,6 +351,7 @@ def main() -> int:
         "per_config": per_config,
         "per_config_isolated": isolated,
         "per_config_cold": cold,
+        "per_config_scaled_bf16": scaled,
     }
 
     if not args.no_cpu:

@@ -91,6 +91,47 @@ lpgemm_status lpgemm_int4_int4(const void *A_packed, const void *B_packed, int32
 lpgemm_status lpgemm_w4a8(const int8_t *A, const uint8_t *B_packed, int32_t *C,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/* ---- per-channel scaled output ---------------------------------------------- */
+
+/* Element type of a scaled result. */
+typedef enum lpgemm_out_dtype {
+    LPGEMM_OUT_F32 = 0,  /* IEEE binary32                                  */
+    LPGEMM_OUT_BF16 = 1, /* bfloat16 bits (upper half of a binary32)       */
+    LPGEMM_OUT_F16 = 2   /* IEEE binary16                                  */
+} lpgemm_out_dtype;
+
+/*
+ * Scaled product with one scale per row of A and one per row of B:
+ *
+ *     D[m][n] = out( ((float)C[m][n] * scale_a[m]) * scale_b[n] )
+ *
+ * where C[m][n] is the exact integer result of lpgemm_int4_int4 /
+ * lpgemm_w4a8, (float) converts it to binary32 rounding to nearest even
+ * (exact while |C| < 2^24), each * is a binary32 multiply rounding to nearest
+ * even, and out() converts the binary32 value to out_dtype rounding to
+ * nearest even (F32: unchanged; BF16: a NaN stays a quiet NaN, values past the
+ * largest finite bf16 become infinities; F16: likewise for binary16).  This is
+ * the tutorial's gemm_blockscaled (ch. 14 sec. 5, "low_precision_gemm.py":
+ * SFA / SFB scales applied per K block, fp32 accumulation, out_dtype result)
+ * with a single K block: per-row and per-column scales.  The integer sum
+ * stays exact; only the epilogue rounds.
+ *   scale_a   device, float [M] (4-byte aligned)
+ *   scale_b   device, float [N] (4-byte aligned)
+ *   D         device, [M][N] of out_dtype, row stride N elements, written;
+ *             aligned to its element size
+ * Other arguments, sizes and return codes as for the unscaled calls; also
+ * LPGEMM_ERR_INVALID_ARG for an unknown out_dtype, a null or misaligned scale
+ * vector or D.  K == 0 gives out(((float)0 * scale_a[m]) * scale_b[n]).
+ */
+lpgemm_status lpgemm_int4_int4_scaled(const void *A_packed, const void *B_packed,
+                                      const float *scale_a, const float *scale_b, void *D,
+                                      lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                                      hipStream_t stream);
+
+lpgemm_status lpgemm_w4a8_scaled(const int8_t *A, const uint8_t *B_packed, const float *scale_a,
+                                 const float *scale_b, void *D, lpgemm_out_dtype out_dtype,
+                                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 /*
  * Pack logical int4 values (held one per int8) into bytes, on the device:
  *   logical  device, int8 [rows][K], each value in [-8, 7] (only the low four

@@ -14,8 +14,8 @@ Pages cited (by title):
   * tilelang PR "[CUDA] Support int4 T.gemm" (#2063), example gemm_int4.
   * tilelang PR "[Example] add w4a8 gemm kernel" (#815), reviews of
     torch_convert / ref_program.
-  * TileLang tutorial ch. 14 sec. 5 "low_precision_gemm.py", pack_int4 and
-    matmul_int4.
+  * TileLang tutorial ch. 14 sec. 5 "low_precision_gemm.py", pack_int4,
+    matmul_int4 and gemm_blockscaled (the scaled epilogue, one K block).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 hand-worked values, closed forms, brute force and an independent numpy
@@ -42,7 +42,7 @@ def build(force: bool = True) -> str:
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp"
     cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
-           "-o", tmp, _SRC]
+           "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -68,6 +68,8 @@ def _load():
         f = getattr(lib, name)
         f.argtypes = [p, p, i64, i64, i64, p]
         f.restype = ctypes.c_int
+    lib.oracle_scaled_epilogue.argtypes = [p, p, p, i64, i64, ctypes.c_int, p]
+    lib.oracle_scaled_epilogue.restype = ctypes.c_int
     for name in ("oracle_gemm_i4i4_at", "oracle_gemm_w4a8_at"):
         f = getattr(lib, name)
         f.argtypes = [p, p, i64, i64, i64, p, p, i64, p]
@@ -176,3 +178,31 @@ def gemm_w4a8_at(A, B_packed, M: int, N: int, K: int, ms, ns) -> np.ndarray:
     a = _bytes2d(A, M, K, "A")
     b = _bytes2d(B_packed, N, K // 2, "B_packed")
     return _at(_load().oracle_gemm_w4a8_at, a, b, M, N, K, ms, ns, "gemm_w4a8_at")
+
+
+# Output formats of the scaled epilogue (lpgemm_out_dtype order).
+FMT_F32, FMT_BF16, FMT_F16 = 0, 1, 2
+
+
+def scaled_epilogue(C, scale_a, scale_b, fmt: int) -> np.ndarray:
+    """D = out(((float)C * scale_a[m]) * scale_b[n]) as the exact value of each
+    rounded result (float64 array); fmt 0 binary32, 1 bfloat16, 2 binary16."""
+    C = np.ascontiguousarray(C, dtype=np.int32)
+    if C.ndim != 2:
+        raise ValueError("C must be 2-D")
+    M, N = C.shape
+    sa = np.ascontiguousarray(scale_a, dtype=np.float32).reshape(-1)
+    sb = np.ascontiguousarray(scale_b, dtype=np.float32).reshape(-1)
+    if sa.shape[0] != M or sb.shape[0] != N:
+        raise ValueError("scale vectors must have M and N entries")
+    out = np.empty((M, N), dtype=np.float64)
+    _check(_load().oracle_scaled_epilogue(_ptr(C), _ptr(sa), _ptr(sb), M, N, int(fmt), _ptr(out)),
+           "oracle_scaled_epilogue")
+    return out
+
+
+def gemm_scaled(variant: str, A, B_packed, scale_a, scale_b, M: int, N: int, K: int,
+                fmt: int) -> np.ndarray:
+    """The scaled product: the exact integer GEMM, then the scaled epilogue."""
+    C = (gemm_i4i4 if variant == "i4i4" else gemm_w4a8)(A, B_packed, M, N, K)
+    return scaled_epilogue(C, scale_a, scale_b, fmt)

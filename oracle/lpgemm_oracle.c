@@ -32,6 +32,7 @@
  * Return codes: 0 ok, 1 bad argument (negative size, odd K, null pointer),
  * 2 a result outside int32, 3 out of host memory.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #ifdef _OPENMP
@@ -206,4 +207,59 @@ int oracle_gemm_w4a8_at(const int8_t *A, const uint8_t *Bp, int64_t M, int64_t N
     }
     if (bad & 2) return ORACLE_ERR_ARG;
     return bad ? ORACLE_ERR_RANGE : ORACLE_OK;
+}
+
+/* ---- per-row / per-column scaled output ---------------------------------------
+ * [tutorial] gemm_blockscaled: scales SFA[m][kb], SFB[n][kb] applied per block
+ * of K with fp32 accumulation and an out_dtype result.  With a single K block
+ * (one scale per row of A and per row of B) and the exact integer sum C:
+ *     D[m][n] = out( ((float)C[m][n] * scale_a[m]) * scale_b[n] )
+ * each step in IEEE binary32 with round-to-nearest-even, then out() rounds the
+ * binary32 value to the output format, nearest even.  Formats: 0 binary32,
+ * 1 bfloat16 (8 significant bits, binary32's exponent range), 2 binary16
+ * (11 significant bits, normal exponents -14..15, subnormals down to 2^-24).
+ * The result is returned as the exact value of the rounded number, in double. */
+
+/* Round x (a finite binary32 value held in a double) to a binary format with
+ * `digits` significant bits, smallest normal exponent `emin` and largest
+ * finite value `maxv`, ties to even: the written-out definition, scaling the
+ * value so the format's quantum at x becomes 1 and rounding with rint (the
+ * default rounding mode is nearest-even).  Values at or beyond the midpoint
+ * between maxv and the next power of two overflow to infinity (the tie goes
+ * to the even neighbour, which is the infinity). */
+static double round_to_format(double x, int digits, int emin, double maxv)
+{
+    if (x == 0.0 || isnan(x) || isinf(x)) return x;
+    const double ax = fabs(x);
+    int e2;
+    frexp(ax, &e2);             /* ax = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;             /* ax in [2^e, 2^(e+1)) */
+    if (e < emin) e = emin;     /* subnormal range: fixed quantum */
+    const double q = ldexp(1.0, e - (digits - 1));
+    const double r = rint(ax / q) * q;
+    const double next_pow = ldexp(1.0, (int)floor(log2(maxv)) + 1);
+    const double limit = maxv + (next_pow - maxv) / 2;
+    if (ax >= limit || r > maxv) return copysign(INFINITY, x);
+    return copysign(r, x);
+}
+
+int oracle_scaled_epilogue(const int32_t *C, const float *scale_a, const float *scale_b,
+                           int64_t M, int64_t N, int fmt, double *out)
+{
+    if (M < 0 || N < 0 || fmt < 0 || fmt > 2) return 1;
+    if (M == 0 || N == 0) return 0;
+    if (!C || !scale_a || !scale_b || !out) return 1;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            volatile float t = (float)C[m * N + n]; /* int32 -> binary32, nearest even */
+            volatile float y = t * scale_a[m];      /* binary32 multiply */
+            volatile float z = y * scale_b[n];      /* binary32 multiply */
+            double v = (double)z;
+            if (fmt == 1)
+                v = round_to_format(v, 8, -126, ldexp(255.0, 120));    /* (2 - 2^-7) * 2^127 */
+            else if (fmt == 2)
+                v = round_to_format(v, 11, -14, 65504.0);
+            out[m * N + n] = v;
+        }
+    return 0;
 }

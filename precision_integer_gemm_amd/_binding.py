@@ -22,10 +22,13 @@ KERNEL_NAMES = {KERNEL_AUTO: "auto", KERNEL_GENERAL: "general", KERNEL_TILED: "t
                 KERNEL_SKINNY: "skinny"}
 # lpgemm_variant
 VARIANT_I4I4, VARIANT_W4A8 = 0, 1
+# lpgemm_out_dtype
+OUT_F32, OUT_BF16, OUT_F16 = 0, 1, 2
 MAX_K = 131070
 
-EXPORTS = ("lpgemm_int4_int4", "lpgemm_w4a8", "lpgemm_pack_int4", "lpgemm_unpack_int4",
-           "lpgemm_status_string", "lpgemm_plan", "lpgemm_set_kernel_override")
+EXPORTS = ("lpgemm_int4_int4", "lpgemm_w4a8", "lpgemm_int4_int4_scaled", "lpgemm_w4a8_scaled",
+           "lpgemm_pack_int4", "lpgemm_unpack_int4", "lpgemm_status_string", "lpgemm_plan",
+           "lpgemm_set_kernel_override")
 
 
 class LpgemmError(RuntimeError):
@@ -62,6 +65,10 @@ def lib() -> ctypes.CDLL:
     for name in ("lpgemm_int4_int4", "lpgemm_w4a8"):
         f = getattr(L, name)
         f.argtypes = [p, p, p, i64, i64, i64, p]
+        f.restype = ctypes.c_int
+    for name in ("lpgemm_int4_int4_scaled", "lpgemm_w4a8_scaled"):
+        f = getattr(L, name)
+        f.argtypes = [p, p, p, p, p, ctypes.c_int, i64, i64, i64, p]
         f.restype = ctypes.c_int
     for name in ("lpgemm_pack_int4", "lpgemm_unpack_int4"):
         f = getattr(L, name)
@@ -164,6 +171,71 @@ def lpgemm_w4a8(A, B_packed, *, out=None, stream=None):
     _raise(lib().lpgemm_w4a8(A.data_ptr(), B_packed.data_ptr(), C.data_ptr(), M, N, K,
                              _stream_handle(stream)), "lpgemm_w4a8")
     return C
+
+
+def _out_code(dtype):
+    torch = _torch()
+    codes = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16, torch.float16: OUT_F16}
+    if dtype not in codes:
+        raise TypeError(f"out dtype must be one of {list(codes)}, got {dtype}")
+    return codes[dtype]
+
+
+def _scaled_out(out, dtype, M, N, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty((M, N), dtype=dtype, device=device)
+    _check_dev(out, "out", (dtype,))
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must have shape ({M}, {N}), got {tuple(out.shape)}")
+    return out
+
+
+def _check_scales(scale_a, scale_b, M, N):
+    torch = _torch()
+    for name, t, n in (("scale_a", scale_a, M), ("scale_b", scale_b, N)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.float32:
+            raise TypeError(f"{name} must be a float32 tensor on a GPU device")
+        if t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with shape ({n},)")
+
+
+def lpgemm_int4_int4_scaled(A_packed, B_packed, scale_a, scale_b, *, dtype=None, out=None,
+                            stream=None):
+    """D[M,N] = out(((float)C * scale_a[m]) * scale_b[n]) of the int4 x int4 product C."""
+    torch = _torch()
+    _check_dev(A_packed, "A_packed", (torch.int8, torch.uint8))
+    _check_dev(B_packed, "B_packed", (torch.int8, torch.uint8))
+    M, half = A_packed.shape
+    N, half_b = B_packed.shape
+    if half != half_b:
+        raise ValueError(f"packed K mismatch: A has {half} bytes per row, B {half_b}")
+    _check_scales(scale_a, scale_b, M, N)
+    dtype = dtype or (out.dtype if out is not None else torch.bfloat16)
+    D = _scaled_out(out, dtype, M, N, A_packed.device)
+    _raise(lib().lpgemm_int4_int4_scaled(A_packed.data_ptr(), B_packed.data_ptr(),
+                                         scale_a.data_ptr(), scale_b.data_ptr(), D.data_ptr(),
+                                         _out_code(dtype), M, N, 2 * half, _stream_handle(stream)),
+           "lpgemm_int4_int4_scaled")
+    return D
+
+
+def lpgemm_w4a8_scaled(A, B_packed, scale_a, scale_b, *, dtype=None, out=None, stream=None):
+    """D[M,N] = out(((float)C * scale_a[m]) * scale_b[n]) of the W4A8 product C."""
+    torch = _torch()
+    _check_dev(A, "A", (torch.int8,))
+    _check_dev(B_packed, "B_packed", (torch.uint8, torch.int8))
+    M, K = A.shape
+    N, half = B_packed.shape
+    if K != 2 * half:
+        raise ValueError(f"K mismatch: A has K={K}, B_packed holds {2 * half}")
+    _check_scales(scale_a, scale_b, M, N)
+    dtype = dtype or (out.dtype if out is not None else torch.bfloat16)
+    D = _scaled_out(out, dtype, M, N, A.device)
+    _raise(lib().lpgemm_w4a8_scaled(A.data_ptr(), B_packed.data_ptr(), scale_a.data_ptr(),
+                                    scale_b.data_ptr(), D.data_ptr(), _out_code(dtype), M, N, K,
+                                    _stream_handle(stream)), "lpgemm_w4a8_scaled")
+    return D
 
 
 def lpgemm_pack_int4(logical, *, out=None, stream=None):

@@ -31,6 +31,9 @@ def command(out: str) -> list[str]:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # the scaled epilogue's roundings are part of its definition: no
+        # contraction of a multiply into a fused operation
+        "-ffp-contract=off",
         "-Wall", "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
         "-o", out, SRC,
     ]

@@ -114,6 +114,116 @@ __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint
     return __builtin_amdgcn_raw_buffer_load_b128(rsrc, offset, 0, 0);
 }
 
+// ---- output epilogue -------------------------------------------------------
+// The integer result C[m][n] is stored either as int32, or scaled per row and
+// per column and converted (the one-K-block case of the tutorial's
+// gemm_blockscaled, with fp32 arithmetic):
+//     D[m][n] = out(((float)C[m][n] * scale_a[m]) * scale_b[n])
+// where (float) and both multiplies round to nearest even in fp32 and out()
+// converts to fp32 (identity), bf16 or fp16, rounding to nearest even.
+enum OutFormat { OUT_I32 = 0, OUT_F32 = 1, OUT_BF16 = 2, OUT_F16 = 3 };
+
+struct Epilogue {
+    void *out;             // D (or C), row-major [M][N]
+    const float *scale_a;  // [M], scaled formats only
+    const float *scale_b;  // [N], scaled formats only
+};
+
+// fp32 -> bf16 bits, round to nearest even; a NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t f16_bits_rne(float x)
+{
+    const _Float16 h = (_Float16)x;  // v_cvt_f16_f32: round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float scaled(int32_t c, float sa, float sb)
+{
+    const float t = (float)c;
+    const float y = t * sa;
+    float z = y * sb;
+    // Materialise the binary32 product: without this the compiler folds the
+    // last multiply and a following fp16 conversion into one fused operation
+    // (one rounding instead of two, and -0 turned into +0).
+    asm volatile("" : "+v"(z));
+    return z;
+}
+
+template <int OUT>
+__device__ __forceinline__ uint32_t out_bits(float y)
+{
+    if (OUT == OUT_BF16) return bf16_bits_rne(y);
+    return f16_bits_rne(y);
+}
+
+// Store results v[i] for columns n .. n+3 of row m (columns >= N skipped).
+// sa is scale_a[m]; sb[i] scale_b[n + i] (read only for columns < N).  The
+// 16-byte (int32 / fp32) or 8-byte (bf16 / fp16) vector store is used when
+// all four columns exist and N % 4 == 0 (aligned base assumed).
+template <int OUT>
+__device__ __forceinline__ void store_row4(const Epilogue &e, int64_t m, int N, int n, i32x4 v,
+                                           float sa, const float (&sb)[4])
+{
+    const bool vec = (N % 4) == 0 && n + 3 < N;
+    if (OUT == OUT_I32) {
+        int32_t *row = static_cast<int32_t *>(e.out) + m * N;
+        if (vec) {
+            *reinterpret_cast<i32x4 *>(row + n) = v;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (n + i < N) row[n + i] = v[i];
+        }
+    } else if (OUT == OUT_F32) {
+        float *row = static_cast<float *>(e.out) + m * N;
+        if (vec) {
+            i32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = (int32_t)__float_as_uint(scaled(v[i], sa, sb[i]));
+            *reinterpret_cast<i32x4 *>(row + n) = w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (n + i < N) row[n + i] = scaled(v[i], sa, sb[i]);
+        }
+    } else {
+        uint16_t *row = static_cast<uint16_t *>(e.out) + m * N;
+        if (vec) {
+            uint32_t h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[i] = out_bits<OUT>(scaled(v[i], sa, sb[i]));
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2 *>(row + n) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (n + i < N) row[n + i] = (uint16_t)out_bits<OUT>(scaled(v[i], sa, sb[i]));
+        }
+    }
+}
+
+// scale_a[m] and scale_b[n .. n+3] (zero where the column does not exist).
+template <int OUT>
+__device__ __forceinline__ void load_scales(const Epilogue &e, int64_t m, int N, int n, float &sa,
+                                            float (&sb)[4])
+{
+    if (OUT == OUT_I32) {
+        sa = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sb[i] = 0.f;
+        return;
+    }
+    sa = e.scale_a[m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sb[i] = (n + i < N) ? e.scale_b[n + i] : 0.f;
+}
+
 // ---- direct-to-LDS loads ---------------------------------------------------
 // Buffer resource for `bytes` bytes at `base` (raw buffer, no stride).
 __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)

@@ -8,12 +8,13 @@
 namespace lpgemm {
 
 // One thread per output element, bytes read one at a time: correct for any
-// even K and any alignment.  Sums fit int32 exactly (|C| <= 1024*K).
-template <int VAR>
+// even K and any alignment.  Sums fit int32 exactly (|C| <= 1024*K).  Also
+// serves K == 0 for the scaled formats (the empty sum, then scaled).
+template <int VAR, int OUT>
 __global__ __launch_bounds__(256) void gemm_general_kernel(const uint8_t *__restrict__ A,
                                                            const uint8_t *__restrict__ B,
-                                                           int32_t *__restrict__ C, int64_t M,
-                                                           int64_t N, int64_t K)
+                                                           Epilogue epi, int64_t M, int64_t N,
+                                                           int64_t K)
 {
     const int64_t n = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
     const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
@@ -34,7 +35,15 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(const uint8_t *__rest
             sum += (int32_t)arow[2 * j] * int4_at(b, 0) + (int32_t)arow[2 * j + 1] * int4_at(b, 1);
         }
     }
-    C[m * N + n] = sum;
+    if (OUT == OUT_I32) {
+        static_cast<int32_t *>(epi.out)[m * N + n] = sum;
+    } else {
+        const float y = scaled(sum, epi.scale_a[m], epi.scale_b[n]);
+        if (OUT == OUT_F32)
+            static_cast<float *>(epi.out)[m * N + n] = y;
+        else
+            static_cast<uint16_t *>(epi.out)[m * N + n] = (uint16_t)out_bits<OUT>(y);
+    }
 }
 
 // C[0 .. count) = 0: the empty sum (K == 0).  A kernel, not a memset, so the

@@ -24,7 +24,8 @@
 // and A its column operand, so the accumulators hold C^T and each lane ends
 // with four consecutive n of one m (16-byte stores).
 //
-// Epilogue (a5): exact >> 8 (int4 x int4) or >> 4 (W4A8), masked stores.
+// Epilogue (a5): exact >> 8 (int4 x int4) or >> 4 (W4A8), masked stores of
+// int32, or of the per-row / per-column scaled fp32, bf16 or fp16 value.
 //
 // Tile order: persistent workgroups loop over tiles; the next tile's first
 // loads are issued before the current tile's stores, so the stores drain
@@ -74,10 +75,10 @@ __device__ __forceinline__ int lds_chunk(int row, int col)
     return row * CPR + (col ^ ((row / rows_per_256) % CPR));
 }
 
-template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES>
+template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, int OUT>
 __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pipelined_kernel(
-    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int32_t *__restrict__ C, int M,
-    int N, int K, int tiles_m, int tiles_n, int xcds)
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N,
+    int K, int tiles_m, int tiles_n, int xcds)
 {
     using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, STAGES>;
     static_assert(Cfg::kFits, "LDS ring does not fit in 160 KB");
@@ -289,45 +290,51 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
         }
         wait_vmcnt<0>();  // the zero-fill loads past the end
 
-        // Start the next tile's loads before this tile's stores, so that the
-        // first wait of the next tile does not also wait for the stores.
         const int tm0 = m0, tn0 = n0;
         const int vn = v + (int)gridDim.x;
-        lds_barrier();  // every wave is done reading this tile's slots
-        if (vn < nblocks) {
-            tile_origin(vn, m0, n0);
-            set_rsrc();
-#pragma unroll
-            for (int s = 0; s < kPrologue; ++s) issue_stage(s);
-        }
-
         // Epilogue: lane holds C[m][n .. n+3] for m = l%32 of each column block.
-        const bool vec_ok = (N % 4) == 0;
+        auto store_tile = [&]() {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = tm0 + (wm * FM + fm) * 32 + r32;
-                if (m >= M) continue;
-                int32_t *crow = C + (int64_t)m * N;
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int m = tm0 + (wm * FM + fm) * 32 + r32;
+                    if (m >= M) continue;
 #pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int n = tn0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h;
-                    const i32x4 v = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
-                                          acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
-                                    Cfg::SHIFT;
-                    if (vec_ok && n + 3 < N) {
-                        *reinterpret_cast<i32x4 *>(crow + n) = v;
-                    } else {
-                        if (n + 0 < N) crow[n + 0] = v.x;
-                        if (n + 1 < N) crow[n + 1] = v.y;
-                        if (n + 2 < N) crow[n + 2] = v.z;
-                        if (n + 3 < N) crow[n + 3] = v.w;
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int n = tn0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h;
+                        const i32x4 c = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
+                                              acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
+                                        Cfg::SHIFT;
+                        float sa, sb[4];
+                        load_scales<OUT>(epi, m, N, n, sa, sb);
+                        store_row4<OUT>(epi, m, N, n, c, sa, sb);
                     }
                 }
+        };
+        auto start_next = [&]() {
+            lds_barrier();  // every wave is done reading this tile's slots
+            if (vn < nblocks) {
+                tile_origin(vn, m0, n0);
+                set_rsrc();
+#pragma unroll
+                for (int s = 0; s < kPrologue; ++s) issue_stage(s);
             }
+        };
+        if constexpr (OUT == OUT_I32) {
+            // The next tile's loads go out before this tile's stores, so the
+            // next tile's first wait does not also wait for the stores.
+            start_next();
+            store_tile();
+        } else {
+            // The scaled epilogue reads scale vectors: stores first, so that
+            // the compiler's waits for those reads never wait on the next
+            // tile's loads.
+            store_tile();
+            start_next();
+        }
         if (vn >= nblocks) break;
-        stores_pending = vec_ok && tm0 + Cfg::BM <= M && tn0 + Cfg::BN <= N;
+        stores_pending = OUT == OUT_I32 && (N % 4) == 0 && tm0 + Cfg::BM <= M && tn0 + Cfg::BN <= N;
         v = vn;
     }
 }

@@ -41,10 +41,9 @@ struct SkinnyCfg {
     static_assert(kLdsBytes <= 160 * 1024, "strip buffers exceed the LDS");
 };
 
-template <int KW, int KSTEPS>
+template <int KW, int KSTEPS, int OUT>
 __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
-    const int8_t *__restrict__ A, const uint8_t *__restrict__ B, int32_t *__restrict__ C, int M,
-    int N, int K)
+    const int8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N, int K)
 {
     using Cfg = SkinnyCfg<KW, KSTEPS>;
     extern __shared__ __align__(1024) uint8_t smem[];
@@ -124,15 +123,9 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
             const int m = r16;
             const int n = prev * 16 + 4 * g;
             if (m < M) {
-                int32_t *crow = C + (int64_t)m * N;
-                if ((N % 4) == 0 && n + 3 < N) {
-                    *reinterpret_cast<i32x4 *>(crow + n) = sum;
-                } else {
-                    if (n + 0 < N) crow[n + 0] = sum.x;
-                    if (n + 1 < N) crow[n + 1] = sum.y;
-                    if (n + 2 < N) crow[n + 2] = sum.z;
-                    if (n + 3 < N) crow[n + 3] = sum.w;
-                }
+                float sa, sb[4];
+                load_scales<OUT>(epi, m, N, n, sa, sb);
+                store_row4<OUT>(epi, m, N, n, sum, sa, sb);
             }
         }
         // Next strip's loads into the other buffer (its last readers passed
@@ -168,15 +161,9 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
         const int m = r16;
         const int n = prev * 16 + 4 * g;
         if (m < M) {
-            int32_t *crow = C + (int64_t)m * N;
-            if ((N % 4) == 0 && n + 3 < N) {
-                *reinterpret_cast<i32x4 *>(crow + n) = sum;
-            } else {
-                if (n + 0 < N) crow[n + 0] = sum.x;
-                if (n + 1 < N) crow[n + 1] = sum.y;
-                if (n + 2 < N) crow[n + 2] = sum.z;
-                if (n + 3 < N) crow[n + 3] = sum.w;
-            }
+            float sa, sb[4];
+            load_scales<OUT>(epi, m, N, n, sa, sb);
+            store_row4<OUT>(epi, m, N, n, sum, sa, sb);
         }
     }
 }

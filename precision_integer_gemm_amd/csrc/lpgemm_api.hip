@@ -48,7 +48,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 template <int VAR, int FM, int FN, int WM, int WN, int BK, int ST>
 struct TiledKernel {
     using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, ST>;
-    static void *fn() { return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, BK, ST>); }
+    template <int OUT>
+    static void *fn() { return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, BK, ST, OUT>); }
 };
 using I4Large = TiledKernel<I4I4, 4, 2, 2, 4, 256, 2>;
 using W8Large = TiledKernel<W4A8, 4, 2, 2, 4, 128, 3>;
@@ -160,8 +161,8 @@ lpgemm_status launched()
 
 // Launch a tiled configuration; the first launch on each device raises the
 // kernel's dynamic-LDS limit to the ring size (above the 64 KB default).
-template <class TK>
-lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, int32_t *C, int m,
+template <class TK, int OUT>
+lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Epilogue epi, int m,
                            int n, int k, hipStream_t stream)
 {
     static std::once_flag once[kMaxDevices];
@@ -169,22 +170,23 @@ lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, in
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERR_HIP;
     std::call_once(once[dev], [dev] {
-        attr_err[dev] = hipFuncSetAttribute(TK::fn(), hipFuncAttributeMaxDynamicSharedMemorySize,
+        attr_err[dev] = hipFuncSetAttribute(TK::template fn<OUT>(),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                             TK::Cfg::LDS_BYTES);
     });
     if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
     int tiles_m = p.tiles_m, tiles_n = p.tiles_n, xcds = kXcds;
-    void *args[] = {(void *)&a, (void *)&b, (void *)&C, (void *)&m,       (void *)&n,
-                    (void *)&k, (void *)&tiles_m,      (void *)&tiles_n, (void *)&xcds};
-    const hipError_t e = hipLaunchKernel(TK::fn(), dim3((unsigned)p.workgroups),
+    void *args[] = {(void *)&a, (void *)&b, (void *)&epi, (void *)&m,       (void *)&n,
+                    (void *)&k, (void *)&tiles_m,        (void *)&tiles_n, (void *)&xcds};
+    const hipError_t e = hipLaunchKernel(TK::template fn<OUT>(), dim3((unsigned)p.workgroups),
                                          dim3(TK::Cfg::kThreads), args, TK::Cfg::LDS_BYTES, stream);
     return e == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
 }
 
 // Launch the narrow-M kernel for K up to KSTEPS * 1024; the first launch on
 // each device raises its dynamic-LDS limit to the two strip buffers.
-template <int KSTEPS>
-lpgemm_status launch_skinny(const Plan &p, const int8_t *a, const uint8_t *b, int32_t *C, int m,
+template <int KSTEPS, int OUT>
+lpgemm_status launch_skinny(const Plan &p, const int8_t *a, const uint8_t *b, Epilogue epi, int m,
                             int n, int k, hipStream_t stream)
 {
     using Cfg = SkinnyCfg<kSkinnyKW, KSTEPS>;
@@ -194,32 +196,20 @@ lpgemm_status launch_skinny(const Plan &p, const int8_t *a, const uint8_t *b, in
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERR_HIP;
     std::call_once(once[dev], [dev] {
         attr_err[dev] = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&gemm_w4a8_skinny_kernel<kSkinnyKW, KSTEPS>),
+            reinterpret_cast<const void *>(&gemm_w4a8_skinny_kernel<kSkinnyKW, KSTEPS, OUT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
     });
     if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
-    hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, KSTEPS>), dim3((unsigned)p.workgroups),
-                       dim3(p.threads), Cfg::kLdsBytes, stream, a, b, C, m, n, k);
+    hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, KSTEPS, OUT>), dim3((unsigned)p.workgroups),
+                       dim3(p.threads), Cfg::kLdsBytes, stream, a, b, epi, m, n, k);
     return launched();
 }
 
-lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, int32_t *C,
-                       int64_t M, int64_t N, int64_t K, hipStream_t stream)
+// Launch the planned kernel for output format OUT.
+template <int OUT>
+lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, const void *B,
+                          Epilogue epi, int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {
-    lpgemm_status st = check_args(A, B, C, M, N, K);
-    if (st != LPGEMM_OK || M == 0 || N == 0) return st;
-    (void)hipGetLastError();  // clear a stale error so the check below is ours
-    if (K == 0) {
-        const int64_t count = M * N;
-        const int blocks = (int)std::min<int64_t>(ceil_div(count, 256), 65536);
-        hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream, C, count);
-        return launched();
-    }
-    Plan p;
-    st = make_plan(variant, A, B, C, M, N, K, device_cu_count(),
-                   (lpgemm_kernel)g_override.load(std::memory_order_relaxed), &p);
-    if (st != LPGEMM_OK) return st;
-
     const uint8_t *a = static_cast<const uint8_t *>(A);
     const uint8_t *b = static_cast<const uint8_t *>(B);
     const int m = (int)M, n = (int)N, k = (int)K;
@@ -227,31 +217,87 @@ lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, int
     case LPGEMM_KERNEL_GENERAL: {
         const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16));
         if (variant == LPGEMM_VARIANT_I4I4)
-            hipLaunchKernelGGL(gemm_general_kernel<I4I4>, grid, dim3(256), 0, stream, a, b, C, M, N, K);
+            hipLaunchKernelGGL((gemm_general_kernel<I4I4, OUT>), grid, dim3(256), 0, stream, a, b, epi, M, N, K);
         else
-            hipLaunchKernelGGL(gemm_general_kernel<W4A8>, grid, dim3(256), 0, stream, a, b, C, M, N, K);
-        break;
+            hipLaunchKernelGGL((gemm_general_kernel<W4A8, OUT>), grid, dim3(256), 0, stream, a, b, epi, M, N, K);
+        return launched();
     }
-    case LPGEMM_KERNEL_TILED: {
+    case LPGEMM_KERNEL_TILED:
         if (variant == LPGEMM_VARIANT_I4I4)
-            return p.large ? launch_tiled<I4Large>(p, a, b, C, m, n, k, stream)
-                           : launch_tiled<I4Small>(p, a, b, C, m, n, k, stream);
-        return p.large ? launch_tiled<W8Large>(p, a, b, C, m, n, k, stream)
-                       : launch_tiled<W8Small>(p, a, b, C, m, n, k, stream);
-    }
+            return p.large ? launch_tiled<I4Large, OUT>(p, a, b, epi, m, n, k, stream)
+                           : launch_tiled<I4Small, OUT>(p, a, b, epi, m, n, k, stream);
+        return p.large ? launch_tiled<W8Large, OUT>(p, a, b, epi, m, n, k, stream)
+                       : launch_tiled<W8Small, OUT>(p, a, b, epi, m, n, k, stream);
     case LPGEMM_KERNEL_SKINNY: {
         const int8_t *a8 = static_cast<const int8_t *>(A);
         switch (p.k_steps) {
-        case 1: return launch_skinny<1>(p, a8, b, C, m, n, k, stream);
-        case 2: return launch_skinny<2>(p, a8, b, C, m, n, k, stream);
-        case 4: return launch_skinny<4>(p, a8, b, C, m, n, k, stream);
-        default: return launch_skinny<8>(p, a8, b, C, m, n, k, stream);
+        case 1: return launch_skinny<1, OUT>(p, a8, b, epi, m, n, k, stream);
+        case 2: return launch_skinny<2, OUT>(p, a8, b, epi, m, n, k, stream);
+        case 4: return launch_skinny<4, OUT>(p, a8, b, epi, m, n, k, stream);
+        default: return launch_skinny<8, OUT>(p, a8, b, epi, m, n, k, stream);
         }
     }
     default:
         return LPGEMM_ERR_INVALID_ARG;
     }
-    return launched();
+}
+
+// out_format: OUT_I32 for the plain entry points; scale pointers are used by
+// the scaled formats only.
+lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, void *C,
+                       const float *scale_a, const float *scale_b, int out_format, int64_t M,
+                       int64_t N, int64_t K, hipStream_t stream)
+{
+    lpgemm_status st = check_args(A, B, C, M, N, K);
+    if (st != LPGEMM_OK || M == 0 || N == 0) return st;
+    if (out_format != OUT_I32) {
+        if (scale_a == nullptr || scale_b == nullptr) return LPGEMM_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(scale_a) | reinterpret_cast<uintptr_t>(scale_b)) & 3u)
+            return LPGEMM_ERR_INVALID_ARG;
+        const uintptr_t elem = out_format == OUT_F32 ? 4u : 2u;
+        if (reinterpret_cast<uintptr_t>(C) & (elem - 1)) return LPGEMM_ERR_INVALID_ARG;
+    }
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    const Epilogue epi{C, scale_a, scale_b};
+    if (K == 0) {
+        if (out_format == OUT_I32) {
+            const int64_t count = M * N;
+            const int blocks = (int)std::min<int64_t>(ceil_div(count, 256), 65536);
+            hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream,
+                               static_cast<int32_t *>(C), count);
+            return launched();
+        }
+        // The empty sum, scaled: the general kernel with no K loop.
+        if (ceil_div(M, 16) > 65535 || ceil_div(N, 16) > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+        Plan p;
+        p.kernel = LPGEMM_KERNEL_GENERAL;
+        switch (out_format) {
+        case OUT_F32: return launch_gemm<OUT_F32>(p, variant, A, B, epi, M, N, K, stream);
+        case OUT_BF16: return launch_gemm<OUT_BF16>(p, variant, A, B, epi, M, N, K, stream);
+        default: return launch_gemm<OUT_F16>(p, variant, A, B, epi, M, N, K, stream);
+        }
+    }
+    Plan p;
+    st = make_plan(variant, A, B, C, M, N, K, device_cu_count(),
+                   (lpgemm_kernel)g_override.load(std::memory_order_relaxed), &p);
+    if (st != LPGEMM_OK) return st;
+    switch (out_format) {
+    case OUT_I32: return launch_gemm<OUT_I32>(p, variant, A, B, epi, M, N, K, stream);
+    case OUT_F32: return launch_gemm<OUT_F32>(p, variant, A, B, epi, M, N, K, stream);
+    case OUT_BF16: return launch_gemm<OUT_BF16>(p, variant, A, B, epi, M, N, K, stream);
+    default: return launch_gemm<OUT_F16>(p, variant, A, B, epi, M, N, K, stream);
+    }
+}
+
+// lpgemm_out_dtype -> OutFormat; -1 for an unknown value.
+int out_format_of(lpgemm_out_dtype d)
+{
+    switch (d) {
+    case LPGEMM_OUT_F32: return OUT_F32;
+    case LPGEMM_OUT_BF16: return OUT_BF16;
+    case LPGEMM_OUT_F16: return OUT_F16;
+    }
+    return -1;
 }
 
 lpgemm_status run_elementwise(bool pack, const void *src, void *dst, int64_t rows, int64_t K,
@@ -279,13 +325,35 @@ extern "C" {
 lpgemm_status lpgemm_int4_int4(const void *A_packed, const void *B_packed, int32_t *C, int64_t M,
                                int64_t N, int64_t K, hipStream_t stream)
 {
-    return run_gemm(LPGEMM_VARIANT_I4I4, A_packed, B_packed, C, M, N, K, stream);
+    return run_gemm(LPGEMM_VARIANT_I4I4, A_packed, B_packed, C, nullptr, nullptr, OUT_I32, M, N, K,
+                    stream);
 }
 
 lpgemm_status lpgemm_w4a8(const int8_t *A, const uint8_t *B_packed, int32_t *C, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream)
 {
-    return run_gemm(LPGEMM_VARIANT_W4A8, A, B_packed, C, M, N, K, stream);
+    return run_gemm(LPGEMM_VARIANT_W4A8, A, B_packed, C, nullptr, nullptr, OUT_I32, M, N, K,
+                    stream);
+}
+
+lpgemm_status lpgemm_int4_int4_scaled(const void *A_packed, const void *B_packed,
+                                      const float *scale_a, const float *scale_b, void *D,
+                                      lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                                      hipStream_t stream)
+{
+    const int f = out_format_of(out_dtype);
+    if (f < 0) return LPGEMM_ERR_INVALID_ARG;
+    return run_gemm(LPGEMM_VARIANT_I4I4, A_packed, B_packed, D, scale_a, scale_b, f, M, N, K,
+                    stream);
+}
+
+lpgemm_status lpgemm_w4a8_scaled(const int8_t *A, const uint8_t *B_packed, const float *scale_a,
+                                 const float *scale_b, void *D, lpgemm_out_dtype out_dtype,
+                                 int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    const int f = out_format_of(out_dtype);
+    if (f < 0) return LPGEMM_ERR_INVALID_ARG;
+    return run_gemm(LPGEMM_VARIANT_W4A8, A, B_packed, D, scale_a, scale_b, f, M, N, K, stream);
 }
 
 lpgemm_status lpgemm_pack_int4(const int8_t *logical, uint8_t *packed, int64_t rows, int64_t K,

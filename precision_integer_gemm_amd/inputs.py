@@ -110,3 +110,18 @@ def operands(case: Case) -> tuple[np.ndarray, np.ndarray]:
 def custom_operands(variant: str, M: int, N: int, K: int, seed: int):
     """Operands of an ad-hoc shape (tests), drawn like the named cases."""
     return operands(Case("custom", variant, M, N, K, seed))
+
+
+def scale_vector(seed: int, which: int, n: int, lo_exp: int = -12, hi_exp: int = 0) -> np.ndarray:
+    """`n` float32 scales for the scaled product (which = 0: per row of A,
+    1: per row of B): random sign, a random binary exponent in
+    [lo_exp, hi_exp] and a random 23-bit mantissa, so the epilogue's
+    roundings are exercised.  Drawn from stream (seed << 8) | (2 + which)."""
+    words = splitmix64(operand_stream(seed, 2 + which), n)
+    sign = (words >> np.uint64(63)).astype(np.uint32)
+    span = hi_exp - lo_exp + 1
+    exp = (words >> np.uint64(32)).astype(np.uint64) % np.uint64(span)
+    biased = (exp.astype(np.int64) + lo_exp + 127).astype(np.uint32)
+    mant = (words & np.uint64(0x7FFFFF)).astype(np.uint32)
+    bits = (sign << np.uint32(31)) | (biased << np.uint32(23)) | mant
+    return bits.view(np.float32)

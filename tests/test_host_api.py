@@ -64,6 +64,20 @@ def test_empty_outputs_are_a_no_op(fn):
     assert f(None, None, None, 5, 0, 32, None) == L.OK
 
 
+@pytest.mark.parametrize("fn", ["lpgemm_int4_int4_scaled", "lpgemm_w4a8_scaled"])
+def test_scaled_argument_errors(fn):
+    f = getattr(L.lib(), fn)
+    assert f(P, P, P, P, P, 3, 4, 4, 32, None) == L.ERR_INVALID_ARG        # unknown out dtype
+    assert f(P, P, None, P, P, L.OUT_BF16, 4, 4, 32, None) == L.ERR_INVALID_ARG  # null scale_a
+    assert f(P, P, P, None, P, L.OUT_BF16, 4, 4, 32, None) == L.ERR_INVALID_ARG  # null scale_b
+    assert f(P, P, P + 2, P, P, L.OUT_F32, 4, 4, 32, None) == L.ERR_INVALID_ARG  # misaligned scale
+    assert f(P, P, P, P, P + 2, L.OUT_F32, 4, 4, 32, None) == L.ERR_INVALID_ARG  # misaligned fp32 D
+    assert f(P, P, P, P, P + 1, L.OUT_BF16, 4, 4, 32, None) == L.ERR_INVALID_ARG  # misaligned bf16 D
+    assert f(P, P, P, P, None, L.OUT_F16, 4, 4, 32, None) == L.ERR_INVALID_ARG   # null D
+    assert f(P, P, P, P, P, L.OUT_F16, 4, 4, 33, None) == L.ERR_INVALID_ARG      # odd K
+    assert f(None, None, None, None, None, L.OUT_F16, 0, 4, 32, None) == L.OK    # empty
+
+
 def test_max_k_is_the_exact_range_of_the_prescale():
     # every x16-scaled term is at most 128*128 = 16384 in magnitude
     assert 16384 * L.MAX_K <= 2**31 - 1 < 16384 * (L.MAX_K + 2)

@@ -35,9 +35,26 @@ MUTANTS = [
     ("range check removed", "if (sum < INT32_MIN || sum > INT32_MAX) bad = 1;", ";"),
 ]
 
+# Mistakes in the scaled epilogue, caught by test_oracle_scaled.py.
+SCALED_MUTANTS = [
+    ("scales multiplied first", "volatile float y = t * scale_a[m];      /* binary32 multiply */\n"
+     "            volatile float z = y * scale_b[n];",
+     "volatile float y = scale_a[m] * scale_b[n];\n            volatile float z = y * t;"),
+    ("ties away from zero", "const double r = rint(ax / q) * q;",
+     "const double r = round(ax / q) * q;"),
+    ("truncation", "const double r = rint(ax / q) * q;", "const double r = trunc(ax / q) * q;"),
+    ("bf16 keeps 7 bits", "round_to_format(v, 8, -126,", "round_to_format(v, 7, -126,"),
+    ("f16 no subnormals", "if (e < emin) e = emin;", ";"),
+    ("f16 overflow at max", "if (ax >= limit || r > maxv)", "if (ax > maxv || r > maxv)"),
+    ("scale_b index", "volatile float z = y * scale_b[n];", "volatile float z = y * scale_b[m % N];"),
+]
 
-@pytest.mark.parametrize("what,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_planted_mistake(tmp_path, what, old, new):
+
+@pytest.mark.parametrize("what,old,new,pins",
+                         [m + ("tests/test_oracle_pins.py",) for m in MUTANTS] +
+                         [m + ("tests/test_oracle_scaled.py",) for m in SCALED_MUTANTS],
+                         ids=[m[0] for m in MUTANTS + SCALED_MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, what, old, new, pins):
     for d in ("oracle", "tests", "precision_integer_gemm_amd"):
         shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
                         ignore=shutil.ignore_patterns("*.so", "__pycache__", "*.hip", "*.o"))
@@ -46,7 +63,7 @@ def test_pins_catch_planted_mistake(tmp_path, what, old, new):
     text = src.read_text()
     assert old in text, f"mutation site for '{what}' not found"
     src.write_text(text.replace(old, new, 1))
-    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-q", "-x",
+    r = subprocess.run([sys.executable, "-m", "pytest", pins, "-q", "-x",
                         "-p", "no:cacheprovider"], cwd=tmp_path, capture_output=True, text=True,
                        timeout=600)
     assert r.returncode != 0, f"pins did not catch: {what}\n{r.stdout[-2000:]}"
