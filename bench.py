@@ -17,7 +17,7 @@ roofline fraction (`per_config`) and the dominant kernel's `roofline`.
 `per_config_isolated` times each workload alone (back-to-back launches, the
 decode-shape B rotated over copies larger than the MALL together), free of the
 write-back a previous workload leaves behind; `per_config_cold` times each
-workload after a 512 MiB write that evicts its operands from L2 and MALL;
+workload after a 512 MiB read that evicts its operands from L2 and MALL;
 `per_config_scaled_bf16` times the scaled product (per-row and per-column
 scales, bf16 output) of each workload alone.
 
@@ -96,7 +96,7 @@ def parse():
     ap.add_argument("--isolated-reps", type=int, default=20,
                     help="back-to-back launches per workload for the isolated per-kernel times")
     ap.add_argument("--cold-reps", type=int, default=10,
-                    help="launches per workload, each after a 512 MiB write that evicts L2 and MALL")
+                    help="launches per workload, each after a 512 MiB read that evicts L2 and MALL")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--trace-summary", metavar="CSV",
@@ -291,16 +291,18 @@ def main() -> int:
                               "roofline_frac": round(max(t_mfma, t_hbm) / (med * 1e-6), 4)}
             del copies, D
 
-    # Each workload cold: before every timed launch a 512 MiB buffer is written
-    # (not timed), which evicts its operands from the L2s and the 256 MB MALL.
+    # Each workload cold: before every timed launch a 512 MiB buffer is read
+    # (not timed), which evicts its operands from the L2s and the 256 MB MALL
+    # with clean lines (a write would leave 512 MB of write-back competing
+    # with the timed launch).
     cold = {}
     if args.cold_reps > 0:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)  # 512 MiB
         for w in work:
             c = w["case"]
             evs = []
             for j in range(args.cold_reps):
-                flush.fill_(j & 0xFF)
+                flush.max()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 call(w)

@@ -208,20 +208,44 @@ __device__ __forceinline__ void store_row4(const Epilogue &e, int64_t m, int N, 
     }
 }
 
-// scale_a[m] and scale_b[n .. n+3] (zero where the column does not exist).
+// scale_a[m] (scaled formats; 0 otherwise).
 template <int OUT>
-__device__ __forceinline__ void load_scales(const Epilogue &e, int64_t m, int N, int n, float &sa,
-                                            float (&sb)[4])
+__device__ __forceinline__ float load_scale_a(const Epilogue &e, int64_t m)
+{
+    return OUT == OUT_I32 ? 0.f : e.scale_a[m];
+}
+
+// scale_b[n .. n+3], zero where the column does not exist: one 16-byte load
+// when the four columns exist and the address is 16-byte aligned.
+template <int OUT>
+__device__ __forceinline__ void load_scale_b4(const Epilogue &e, int N, int n, float (&sb)[4])
 {
     if (OUT == OUT_I32) {
-        sa = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) sb[i] = 0.f;
         return;
     }
-    sa = e.scale_a[m];
+    const float *p = e.scale_b + n;
+    if (n + 3 < N && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        sb[0] = v.x;
+        sb[1] = v.y;
+        sb[2] = v.z;
+        sb[3] = v.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sb[i] = (n + i < N) ? e.scale_b[n + i] : 0.f;
+        for (int i = 0; i < 4; ++i) sb[i] = (n + i < N) ? p[i] : 0.f;
+    }
+}
+
+// Both scale sets of one row segment.
+template <int OUT>
+__device__ __forceinline__ void load_scales(const Epilogue &e, int64_t m, int N, int n, float &sa,
+                                            float (&sb)[4])
+{
+    sa = load_scale_a<OUT>(e, m);
+    load_scale_b4<OUT>(e, N, n, sb);
 }
 
 // ---- direct-to-LDS loads ---------------------------------------------------

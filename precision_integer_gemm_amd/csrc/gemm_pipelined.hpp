@@ -294,6 +294,19 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
         const int vn = v + (int)gridDim.x;
         // Epilogue: lane holds C[m][n .. n+3] for m = l%32 of each column block.
         auto store_tile = [&]() {
+            // Scales first (one per row block, four per column group), then
+            // the stores: the scale reads are not reordered behind stores to D.
+            float sa[FM], sb[FN][4][4];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int m = tm0 + (wm * FM + fm) * 32 + r32;
+                sa[fm] = m < M ? load_scale_a<OUT>(epi, m) : 0.f;
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg)
+                    load_scale_b4<OUT>(epi, N, tn0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h, sb[fn][rg]);
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -306,9 +319,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
                         const i32x4 c = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
                                               acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
                                         Cfg::SHIFT;
-                        float sa, sb[4];
-                        load_scales<OUT>(epi, m, N, n, sa, sb);
-                        store_row4<OUT>(epi, m, N, n, c, sa, sb);
+                        store_row4<OUT>(epi, m, N, n, c, sa[fm], sb[fn][rg]);
                     }
                 }
         };

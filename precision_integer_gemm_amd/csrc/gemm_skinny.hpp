@@ -108,6 +108,10 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
     issue_strip(s, 0);
     int it = 0;
     int prev = -1;  // strip whose partial tiles await reduction
+    // Scales of the strip this wave will reduce next, read one iteration
+    // early (the reducing wave of strip s is the wave that reads its scales
+    // while strip s is contracted), so the reduction never waits on them.
+    float pend_sa = 0.f, pend_sb[4] = {0.f, 0.f, 0.f, 0.f};
     for (;;) {
         const int b = it & 1;
         wait_vmcnt<0>();
@@ -122,16 +126,14 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
             sum >>= 4;  // B carried a factor 16
             const int m = r16;
             const int n = prev * 16 + 4 * g;
-            if (m < M) {
-                float sa, sb[4];
-                load_scales<OUT>(epi, m, N, n, sa, sb);
-                store_row4<OUT>(epi, m, N, n, sum, sa, sb);
-            }
+            if (m < M) store_row4<OUT>(epi, m, N, n, sum, pend_sa, pend_sb);
         }
         // Next strip's loads into the other buffer (its last readers passed
         // the barrier above).
         const int sn = s + G;
         if (sn < strips) issue_strip(sn, b ^ 1);
+        if (OUT != OUT_I32 && wave == it % KW && r16 < M)
+            load_scales<OUT>(epi, r16, N, s * 16 + 4 * g, pend_sa, pend_sb);
 
         // Contract this wave's K slice of strip s.
         const uint8_t *buf = smem + b * Cfg::kBufBytes;
@@ -160,11 +162,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
         sum >>= 4;
         const int m = r16;
         const int n = prev * 16 + 4 * g;
-        if (m < M) {
-            float sa, sb[4];
-            load_scales<OUT>(epi, m, N, n, sa, sb);
-            store_row4<OUT>(epi, m, N, n, sum, sa, sb);
-        }
+        if (m < M) store_row4<OUT>(epi, m, N, n, sum, pend_sa, pend_sb);
     }
 }
 
