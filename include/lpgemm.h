@@ -164,7 +164,8 @@ typedef enum lpgemm_kernel {
     LPGEMM_KERNEL_TILED = 2,     /* block-tiled MFMA kernel, tile size by shape   */
     LPGEMM_KERNEL_SKINNY = 3,    /* W4A8 narrow-M kernel streaming B once        */
     LPGEMM_KERNEL_TILED_128 = 4, /* block-tiled, 128 x 128 output tiles          */
-    LPGEMM_KERNEL_TILED_256 = 5  /* block-tiled, 256 x 256 output tiles          */
+    LPGEMM_KERNEL_TILED_256 = 5, /* block-tiled, 256 x 256 output tiles          */
+    LPGEMM_KERNEL_TILED_64 = 6   /* block-tiled, 64 x 64 output tiles            */
 } lpgemm_kernel;
 
 typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "_lpgemm.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 # lpgemm_kernel
 KERNEL_AUTO, KERNEL_GENERAL, KERNEL_TILED, KERNEL_SKINNY = 0, 1, 2, 3
-KERNEL_TILED_128, KERNEL_TILED_256 = 4, 5
+KERNEL_TILED_128, KERNEL_TILED_256, KERNEL_TILED_64 = 4, 5, 6
 KERNEL_NAMES = {KERNEL_AUTO: "auto", KERNEL_GENERAL: "general", KERNEL_TILED: "tiled",
                 KERNEL_SKINNY: "skinny"}
 # lpgemm_variant

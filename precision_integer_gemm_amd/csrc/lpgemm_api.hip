@@ -43,6 +43,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 //   large: 256 x 256 tiles, 8 waves (2 x 4), each wave 128 (m) x 64 (n);
 //          int4 x int4 stages 256 logical k per LDS slot (2 slots, 128 KB),
 //          W4A8 128 k per slot (3 slots, 144 KB).
+//   tiny:  64 x 64 tiles, 4 waves, when even 128 x 128 tiles would leave
+//          more than half of the compute units idle (1024^3: 64 -> 256 tiles).
 //   small: 128 x 128 tiles, 4 waves, for shapes with too few large tiles to
 //          fill the GPU.
 template <int VAR, int FM, int FN, int WM, int WN, int BK, int ST>
@@ -55,6 +57,8 @@ using I4Large = TiledKernel<I4I4, 4, 2, 2, 4, 256, 2>;
 using W8Large = TiledKernel<W4A8, 4, 2, 2, 4, 128, 3>;
 using I4Small = TiledKernel<I4I4, 2, 2, 2, 2, 128, 3>;
 using W8Small = TiledKernel<W4A8, 2, 2, 2, 2, 128, 3>;
+using I4Tiny = TiledKernel<I4I4, 1, 1, 2, 2, 256, 2>;
+using W8Tiny = TiledKernel<W4A8, 1, 1, 2, 2, 256, 2>;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 // Skinny: 8 waves split K (up to 8 steps of 128 k each, A held in registers);
@@ -69,7 +73,7 @@ struct Plan {
     int64_t workgroups = 0;
     int k_steps = 0;
     int tiles_m = 0, tiles_n = 0;
-    bool large = false;
+    int tile = 0;  // tiled kernels: 256, 128 or 64 (square tiles)
 };
 
 lpgemm_status check_args(const void *A, const void *B, const void *C, int64_t M, int64_t N,
@@ -103,7 +107,7 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
             k = LPGEMM_KERNEL_TILED;
     }
     const bool tiled = k == LPGEMM_KERNEL_TILED || k == LPGEMM_KERNEL_TILED_128 ||
-                       k == LPGEMM_KERNEL_TILED_256;
+                       k == LPGEMM_KERNEL_TILED_256 || k == LPGEMM_KERNEL_TILED_64;
     if ((tiled && !fast_ok) || (k == LPGEMM_KERNEL_SKINNY && !skinny_ok))
         return LPGEMM_ERR_UNSUPPORTED;
 
@@ -119,22 +123,32 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         break;
     case LPGEMM_KERNEL_TILED:
     case LPGEMM_KERNEL_TILED_128:
-    case LPGEMM_KERNEL_TILED_256: {
-        // Large tiles when they give at least 3/4 of a tile per compute unit.
+    case LPGEMM_KERNEL_TILED_256:
+    case LPGEMM_KERNEL_TILED_64: {
+        // Large tiles when they give at least 3/4 of a tile per compute unit;
+        // else 128-tiles when they cover at least half of the compute units;
+        // else 64-tiles.
         const int64_t large_tiles = ceil_div(M, 256) * ceil_div(N, 256);
-        p.large = (k == LPGEMM_KERNEL_TILED) ? large_tiles * 4 >= (int64_t)cu_count * 3
-                                              : k == LPGEMM_KERNEL_TILED_256;
+        const int64_t small_tiles = ceil_div(M, 128) * ceil_div(N, 128);
+        if (k == LPGEMM_KERNEL_TILED)
+            p.tile = large_tiles * 4 >= (int64_t)cu_count * 3 ? 256
+                     : small_tiles * 2 >= (int64_t)cu_count   ? 128
+                                                              : 64;
+        else
+            p.tile = k == LPGEMM_KERNEL_TILED_256 ? 256 : k == LPGEMM_KERNEL_TILED_128 ? 128 : 64;
         p.kernel = LPGEMM_KERNEL_TILED;
-        p.tile_m = p.large ? 256 : 128;
-        p.tile_n = p.large ? 256 : 128;
-        p.threads = p.large ? I4Large::Cfg::kThreads : I4Small::Cfg::kThreads;
+        p.tile_m = p.tile;
+        p.tile_n = p.tile;
+        p.threads = p.tile == 256 ? I4Large::Cfg::kThreads
+                    : p.tile == 128 ? I4Small::Cfg::kThreads
+                                    : I4Tiny::Cfg::kThreads;
         p.tiles_m = (int)ceil_div(M, p.tile_m);
         p.tiles_n = (int)ceil_div(N, p.tile_n);
         p.workgroups = (int64_t)p.tiles_m * p.tiles_n;
         if (p.workgroups > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
         // Large tiles run one persistent workgroup per compute unit (their LDS
         // ring leaves room for one), each looping over tiles.
-        if (p.large) p.workgroups = std::min<int64_t>(p.workgroups, cu_count);
+        if (p.tile == 256) p.workgroups = std::min<int64_t>(p.workgroups, cu_count);
         break;
     }
     case LPGEMM_KERNEL_SKINNY: {
@@ -224,10 +238,12 @@ lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, 
     }
     case LPGEMM_KERNEL_TILED:
         if (variant == LPGEMM_VARIANT_I4I4)
-            return p.large ? launch_tiled<I4Large, OUT>(p, a, b, epi, m, n, k, stream)
-                           : launch_tiled<I4Small, OUT>(p, a, b, epi, m, n, k, stream);
-        return p.large ? launch_tiled<W8Large, OUT>(p, a, b, epi, m, n, k, stream)
-                       : launch_tiled<W8Small, OUT>(p, a, b, epi, m, n, k, stream);
+            return p.tile == 256 ? launch_tiled<I4Large, OUT>(p, a, b, epi, m, n, k, stream)
+                   : p.tile == 128 ? launch_tiled<I4Small, OUT>(p, a, b, epi, m, n, k, stream)
+                                   : launch_tiled<I4Tiny, OUT>(p, a, b, epi, m, n, k, stream);
+        return p.tile == 256 ? launch_tiled<W8Large, OUT>(p, a, b, epi, m, n, k, stream)
+               : p.tile == 128 ? launch_tiled<W8Small, OUT>(p, a, b, epi, m, n, k, stream)
+                               : launch_tiled<W8Tiny, OUT>(p, a, b, epi, m, n, k, stream);
     case LPGEMM_KERNEL_SKINNY: {
         const int8_t *a8 = static_cast<const int8_t *>(A);
         switch (p.k_steps) {
@@ -404,7 +420,7 @@ lpgemm_status lpgemm_plan(lpgemm_variant variant, const void *A, const void *B, 
 
 lpgemm_status lpgemm_set_kernel_override(lpgemm_kernel kernel)
 {
-    if (kernel < LPGEMM_KERNEL_AUTO || kernel > LPGEMM_KERNEL_TILED_256) return LPGEMM_ERR_INVALID_ARG;
+    if (kernel < LPGEMM_KERNEL_AUTO || kernel > LPGEMM_KERNEL_TILED_64) return LPGEMM_ERR_INVALID_ARG;
     g_override.store(kernel, std::memory_order_relaxed);
     return LPGEMM_OK;
 }

@@ -86,7 +86,8 @@ def test_general_kernel(torch, variant, M, N, K):
     assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
 
 
-@pytest.mark.parametrize("tile", [L.KERNEL_TILED_128, L.KERNEL_TILED_256], ids=["t128", "t256"])
+@pytest.mark.parametrize("tile", [L.KERNEL_TILED_64, L.KERNEL_TILED_128, L.KERNEL_TILED_256],
+                         ids=["t64", "t128", "t256"])
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
 @pytest.mark.parametrize("M,N,K", ALIGNED)
 def test_tiled_kernel(torch, variant, M, N, K, tile):
@@ -124,6 +125,42 @@ def test_closed_form_extremes(torch, variant):
     else:
         A, want = np.full((M, K), -128, dtype=np.int8), 1024 * K
     assert (run_gpu(torch, variant, A, B, M, N, K) == want).all()
+
+
+# The largest K the library accepts: the x16 pre-scale keeps every partial sum
+# within int32 (16384 * K < 2^31).  All-extreme operands reach the bound: the
+# tiled path at the largest multiple of 32, the general path at K = MAX_K.
+@pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
+@pytest.mark.parametrize("K", [L.MAX_K - L.MAX_K % 32, L.MAX_K], ids=["tiled", "general"])
+def test_largest_k_closed_forms(torch, variant, K):
+    M, N = 64, 48
+    say(f"largest K {variant} K={K}")
+    B = np.full((N, K // 2), 0x88, dtype=np.uint8)                        # all -8
+    if variant == "i4i4":
+        A, want = np.full((M, K // 2), 0x88, dtype=np.uint8), 64 * K        # (-8)(-8)
+    else:
+        A, want = np.full((M, K), -128, dtype=np.int8), 1024 * K            # (-128)(-8)
+    got = run_gpu(torch, variant, A, B, M, N, K)
+    assert (got == want).all()
+    # mixed signs: b = +7 in odd k, -8 in even k; a = -8 (i4i4) or 127 (w4a8)
+    B2 = np.full((N, K // 2), 0x78, dtype=np.uint8)
+    if variant == "i4i4":
+        want2 = (K // 2) * (64 - 56)
+    else:
+        A = np.full((M, K), 127, dtype=np.int8)
+        want2 = (K // 2) * (127 * -8 + 127 * 7)
+    got2 = run_gpu(torch, variant, A, B2, M, N, K)
+    assert (got2 == want2).all()
+
+
+@pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
+def test_k_above_the_limit_is_rejected(torch, variant):
+    dev = torch.device("cuda:0")
+    buf = torch.zeros(64, dtype=torch.int32, device=dev)
+    fn = L.lib().lpgemm_int4_int4 if variant == "i4i4" else L.lib().lpgemm_w4a8
+    st = fn(buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), 1, 1, L.MAX_K + 2,
+            torch.cuda.current_stream().cuda_stream)
+    assert st == L.ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])

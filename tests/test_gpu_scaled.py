@@ -100,7 +100,8 @@ def test_general_kernel(torch, variant, fmt, M, N, K):
     check(got, oracle.gemm_scaled(variant, A, B, sa, sb, M, N, K, FORMATS[fmt][1]))
 
 
-@pytest.mark.parametrize("tile", [L.KERNEL_TILED_128, L.KERNEL_TILED_256], ids=["t128", "t256"])
+@pytest.mark.parametrize("tile", [L.KERNEL_TILED_64, L.KERNEL_TILED_128, L.KERNEL_TILED_256],
+                         ids=["t64", "t128", "t256"])
 @pytest.mark.parametrize("fmt", list(FORMATS))
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
 @pytest.mark.parametrize("M,N,K", TILED)

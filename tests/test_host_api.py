@@ -117,7 +117,9 @@ def test_tile_size_follows_the_number_of_tiles():
     assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192)["tile_m"] == 256
     assert L.lpgemm_plan(L.VARIANT_W4A8, 4096, 4096, 4096)["tile_m"] == 256
     assert L.lpgemm_plan(L.VARIANT_I4I4, 3000, 5120, 6144)["tile_m"] == 256  # 240 tiles
-    assert L.lpgemm_plan(L.VARIANT_I4I4, 1024, 1024, 1024)["tile_m"] == 128
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 2048, 2048, 2048)["tile_m"] == 128  # 256 tiles of 128
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 1024, 1024, 1024)["tile_m"] == 64   # 64 tiles of 128: too few
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 300, 260, 1056)["tile_m"] == 64
     assert L.lpgemm_plan(L.VARIANT_I4I4, 3000, 5120, 6144, cu_count=512)["tile_m"] == 128
 
 
@@ -144,6 +146,9 @@ def test_forced_kernel_that_cannot_run_is_unsupported():
         L.lpgemm_set_kernel_override(L.KERNEL_TILED_128)
         p = L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192)
         assert (p["kernel"], p["tile_m"], p["workgroups"]) == ("tiled", 128, 4096)
+        L.lpgemm_set_kernel_override(L.KERNEL_TILED_64)
+        p = L.lpgemm_plan(L.VARIANT_W4A8, 4096, 4096, 4096)
+        assert (p["kernel"], p["tile_m"], p["workgroups"]) == ("tiled", 64, 4096)
     finally:
         L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
 
