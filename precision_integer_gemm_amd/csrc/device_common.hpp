@@ -277,6 +277,24 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voffset, uint32_t lds
         : "memory");
 }
 
+// dma16 with the non-temporal hint, for data that is read exactly once (the
+// narrow-M kernel's weight stream).  Measured on MI355X: right after a kernel
+// that wrote 268 MB, a 117 MB weight stream read this way ran in half the time
+// that plain loads took there; on an idle memory system both run alike.
+__device__ __forceinline__ void dma16_nt(i32x4 rsrc, uint32_t voffset, uint32_t lds_base)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voffset), "s"(rsrc), "s"(lds_base)
+        : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight
 // (the counter holds 0..63; a larger N waits for 63, which is only stricter).
 template <int N>

@@ -11,6 +11,7 @@ namespace lpgemm {
 // B reaches LDS through direct-to-LDS buffer loads in which every instruction
 // reads 1 KB of one row, so HBM sees long row-linear bursts (a lane-per-row
 // register load, 16 rows x 64 bytes per instruction, streams markedly slower).
+// The loads carry the non-temporal hint: each byte of B is read once.
 //
 //   * workgroup = KW waves, one per compute unit, walking strips of 16 rows
 //     of B (grid-stride); two LDS strip buffers, the next strip's loads in
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
         const uint32_t base = (uint32_t)s * 16u * ldb;
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t)
-            dma16(rsrc_b, dma_live[t] ? base + dma_row_off[t] : kOutOfRange,
+            dma16_nt(rsrc_b, dma_live[t] ? base + dma_row_off[t] : kOutOfRange,
                   lds0 + (uint32_t)b * Cfg::kBufBytes + (uint32_t)(wave * KSTEPS + t) * 1024u);
     };
 
@@ -112,6 +113,26 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
     // early (the reducing wave of strip s is the wave that reads its scales
     // while strip s is contracted), so the reduction never waits on them.
     float pend_sa = 0.f, pend_sb[4] = {0.f, 0.f, 0.f, 0.f};
+    // Integer results are held back: a wave keeps the last sum it reduced and
+    // stores it when it reduces the next one, or at the end.  C's small row
+    // pieces then reach memory in a burst after the weight stream instead of
+    // interleaved with it (interleaved, they slowed the stream measurably).
+    // Scaled results are stored at once: their scales are read per strip.
+    constexpr bool kHold = OUT == OUT_I32;
+    bool held = false;
+    int held_n = 0;
+    i32x4 held_sum = {0, 0, 0, 0};
+    auto emit = [&](int n, const i32x4 &sum) {
+        if (r16 >= M) return;
+        if (!kHold) {
+            store_row4<OUT>(epi, r16, N, n, sum, pend_sa, pend_sb);
+            return;
+        }
+        if (held) store_row4<OUT>(epi, r16, N, held_n, held_sum, pend_sa, pend_sb);
+        held = true;
+        held_n = n;
+        held_sum = sum;
+    };
     for (;;) {
         const int b = it & 1;
         wait_vmcnt<0>();
@@ -124,9 +145,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
 #pragma unroll
             for (int w = 1; w < KW; ++w) sum += rp[w * 64 + lane];
             sum >>= 4;  // B carried a factor 16
-            const int m = r16;
-            const int n = prev * 16 + 4 * g;
-            if (m < M) store_row4<OUT>(epi, m, N, n, sum, pend_sa, pend_sb);
+            emit(prev * 16 + 4 * g, sum);
         }
         // Next strip's loads into the other buffer (its last readers passed
         // the barrier above).
@@ -160,10 +179,9 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
 #pragma unroll
         for (int w = 1; w < KW; ++w) sum += rp[w * 64 + lane];
         sum >>= 4;
-        const int m = r16;
-        const int n = prev * 16 + 4 * g;
-        if (m < M) store_row4<OUT>(epi, m, N, n, sum, pend_sa, pend_sb);
+        emit(prev * 16 + 4 * g, sum);
     }
+    if (kHold && held && r16 < M) store_row4<OUT>(epi, r16, N, held_n, held_sum, pend_sa, pend_sb);
 }
 
 }  // namespace lpgemm

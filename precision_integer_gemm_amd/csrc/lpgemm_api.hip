@@ -61,11 +61,12 @@ using I4Tiny = TiledKernel<I4I4, 1, 1, 2, 2, 256, 2>;
 using W8Tiny = TiledKernel<W4A8, 1, 1, 2, 2, 256, 2>;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
-// Skinny: 8 waves split K (up to 8 steps of 128 k each, A held in registers);
+// Skinny: 16 waves split K (up to 4 steps of 128 k each, A held in registers);
 // one workgroup per compute unit walks strips of 16 rows of B, staged in LDS.
-constexpr int kSkinnyKW = 8;
+// (16 waves contract a strip faster than 8 with twice the steps each.)
+constexpr int kSkinnyKW = 16;
 constexpr int kSkinnyMaxM = 16;
-constexpr int kSkinnyMaxK = kSkinnyKW * 8 * 128;
+constexpr int kSkinnyMaxK = kSkinnyKW * 4 * 128;
 
 struct Plan {
     lpgemm_kernel kernel = LPGEMM_KERNEL_AUTO;
@@ -156,8 +157,8 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         p.tile_n = 16;
         p.k_split = kSkinnyKW;
         p.threads = 64 * kSkinnyKW;
-        p.k_steps = (int)ceil_div(ceil_div(K, kSkinnyKW), 128);  // 1..8
-        while (p.k_steps & (p.k_steps - 1)) ++p.k_steps;          // 1, 2, 4 or 8
+        p.k_steps = (int)ceil_div(ceil_div(K, kSkinnyKW), 128);  // 1..4
+        while (p.k_steps & (p.k_steps - 1)) ++p.k_steps;          // 1, 2 or 4
         p.workgroups = std::min<int64_t>(ceil_div(N, 16), std::min(cu_count, 256));
         break;
     }
@@ -249,8 +250,7 @@ lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, 
         switch (p.k_steps) {
         case 1: return launch_skinny<1, OUT>(p, a8, b, epi, m, n, k, stream);
         case 2: return launch_skinny<2, OUT>(p, a8, b, epi, m, n, k, stream);
-        case 4: return launch_skinny<4, OUT>(p, a8, b, epi, m, n, k, stream);
-        default: return launch_skinny<8, OUT>(p, a8, b, epi, m, n, k, stream);
+        default: return launch_skinny<4, OUT>(p, a8, b, epi, m, n, k, stream);
         }
     }
     default:

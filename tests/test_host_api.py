@@ -164,7 +164,7 @@ def test_plan_grid_covers_the_output():
     assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=304)["workgroups"] == 304
     # the narrow-M kernel: one workgroup per compute unit walks the 16-row strips
     p = L.lpgemm_plan(L.VARIANT_W4A8, 16, 28672, 8192)
-    assert (p["workgroups"], p["tile_n"], p["k_split"]) == (256, 16, 8)
+    assert (p["workgroups"], p["tile_n"], p["k_split"]) == (256, 16, 16)
     assert L.lpgemm_plan(L.VARIANT_W4A8, 1, 1000, 96)["workgroups"] == 63
     # capped at 256 workgroups (prefetch offsets past the end stay within 32 bits)
     assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 28672, 8192, cu_count=304)["workgroups"] == 256
