@@ -42,7 +42,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Tiled kernels (gemm_pipelined.hpp), chosen by measurement on MI355X:
 //   large: 256 x 256 tiles, 8 waves (2 x 4), each wave 128 (m) x 64 (n);
 //          int4 x int4 stages 256 logical k per LDS slot (2 slots, 128 KB),
-//          W4A8 128 k per slot (3 slots, 144 KB).
+//          W4A8 128 k per slot (2 slots, 96 KB: a third slot measured
+//          1-4% slower).
 //   tiny:  64 x 64 tiles, 4 waves, when even 128 x 128 tiles would leave
 //          more than half of the compute units idle (1024^3: 64 -> 256 tiles).
 //   small: 128 x 128 tiles, 4 waves, for shapes with too few large tiles to
@@ -54,7 +55,7 @@ struct TiledKernel {
     static void *fn() { return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, BK, ST, OUT>); }
 };
 using I4Large = TiledKernel<I4I4, 4, 2, 2, 4, 256, 2>;
-using W8Large = TiledKernel<W4A8, 4, 2, 2, 4, 128, 3>;
+using W8Large = TiledKernel<W4A8, 4, 2, 2, 4, 128, 2>;
 using I4Small = TiledKernel<I4I4, 2, 2, 2, 2, 128, 3>;
 using W8Small = TiledKernel<W4A8, 2, 2, 2, 2, 128, 3>;
 using I4Tiny = TiledKernel<I4I4, 1, 1, 2, 2, 256, 2>;
