@@ -40,8 +40,12 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# MI355X published peaks (dense): int8 MFMA 5.0 POP/s, HBM3E 8 TB/s.
+# MI355X published peaks (dense): int8 MFMA 5.0 POP/s, FP6 MFMA 10.1 PFLOP/s,
+# HBM3E 8 TB/s.  A workload is priced at the peak of the matrix-core format its
+# kernel computes in: int4 x int4 calls that run on the FP6 path at the FP6
+# peak, everything else at the int8 peak.
 PEAK_INT8_TOPS = 5000.0
+PEAK_FP6_TOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
 
 # Step order: each W4A8 skinny call reads a B that no call has touched for
@@ -50,10 +54,17 @@ STEP_ORDER = ["w4a8_skinny_m16", "i4i4_8192", "w4a8_skinny_m1", "w4a8_4096", "i4
               "i4i4_256", "i4i4_1024"]
 
 KERNEL_SYMBOL = {"tiled": "gemm_pipelined_kernel", "skinny": "gemm_w4a8_skinny_kernel",
-                 "general": "gemm_general_kernel"}
+                 "general": "gemm_general_kernel",
+                 "fp6": "fp6_convert_kernel (A, B) + gemm_fp6_kernel"}
 
-# HBM traffic of the dominant kernel, from two rocprofv3 --pmc runs (FETCH_SIZE,
-# then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+
+def mfma_peak(kernel: str) -> float:
+    return PEAK_FP6_TOPS if kernel == "fp6" else PEAK_INT8_TOPS
+
+
+# HBM traffic of the dominant call, from two rocprofv3 --pmc runs (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch, summed over the call's dispatches: the two
+# FP6 re-encodings and the GEMM), each scaled by what the same counter
 # reads for a plain 256 MiB device copy (bench.py --copy-calibration 256):
 # FETCH_SIZE reads 131072 KiB for 256 MiB read (x2.0), WRITE_SIZE 262144 KiB
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
@@ -63,6 +74,7 @@ TRAFFIC = {
                   "write_scale": 1.0, "sources_sha256": "8696956ce455598f6c594f63c41a76ddd2cc29f3eede0b5f42f64ca683173a98"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
+                   "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",
                    "precision_integer_gemm_amd/csrc/device_common.hpp",
                    "precision_integer_gemm_amd/csrc/lpgemm_api.hip"]
 
@@ -124,8 +136,8 @@ def trace_summary(path: str) -> int:
     return 0
 
 
-def roofline_time_s(case) -> tuple[float, str]:
-    t_mfma = case.ops / (PEAK_INT8_TOPS * 1e12)
+def roofline_time_s(case, kernel: str = "tiled") -> tuple[float, str]:
+    t_mfma = case.ops / (mfma_peak(kernel) * 1e12)
     t_hbm = case.alg_bytes / (PEAK_HBM_GBS * 1e9)
     return (t_mfma, "mfma") if t_mfma >= t_hbm else (t_hbm, "hbm")
 
@@ -212,13 +224,16 @@ def main() -> int:
         us = np.array([events[s][i][0].elapsed_time(events[s][i][1]) * 1e3
                        for s in range(args.steps)])
         avg = float(us.mean())
-        t_roof, bound = roofline_time_s(c)
+        t_roof, bound = roofline_time_s(c, w["plan"]["kernel"])
         rec = {"kernel": w["plan"]["kernel"], "avg_us": round(avg, 3),
                "median_us": round(float(np.median(us)), 3), "min_us": round(float(us.min()), 3),
                "p90_us": round(float(np.percentile(us, 90)), 3),
                "tops": round(c.ops / (avg * 1e-6) / 1e12, 2),
                "gbs": round(c.alg_bytes / (avg * 1e-6) / 1e9, 1),
                "bound": bound, "roofline_frac": round(t_roof / (avg * 1e-6), 4)}
+        if bound == "mfma":
+            rec["mfma_peak_tops"] = mfma_peak(w["plan"]["kernel"])
+            rec["int8_peak_frac"] = round(c.ops / (avg * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4)
         per_config[c.name] = rec
         total = avg * args.steps
         if dominant is None or total > dominant[0]:
@@ -246,12 +261,31 @@ def main() -> int:
             torch.cuda.synchronize()
             us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
             med = float(np.median(us))
-            t_roof, bound = roofline_time_s(c)
+            t_roof, bound = roofline_time_s(c, w["plan"]["kernel"])
             isolated[c.name] = {"median_us": round(med, 3), "min_us": round(float(us.min()), 3),
                                 "p90_us": round(float(np.percentile(us, 90)), 3),
                                 "tops": round(c.ops / (med * 1e-6) / 1e12, 2),
                                 "gbs": round(c.alg_bytes / (med * 1e-6) / 1e9, 1),
                                 "bound": bound, "roofline_frac": round(t_roof / (med * 1e-6), 4)}
+            if w["plan"]["kernel"] == "fp6":
+                # the same workload forced onto the int8 256-tile kernel, for comparison
+                L.lpgemm_set_kernel_override(L.KERNEL_TILED_256)
+                try:
+                    evs8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                            for _ in range(args.isolated_reps)]
+                    call(w)
+                    for e0, e1 in evs8:
+                        e0.record(stream)
+                        call(w)
+                        e1.record(stream)
+                    torch.cuda.synchronize()
+                finally:
+                    L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
+                us8 = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs8])
+                med8 = float(np.median(us8))
+                isolated[c.name]["int8_path"] = {
+                    "median_us": round(med8, 3), "tops": round(c.ops / (med8 * 1e-6) / 1e12, 2),
+                    "int8_peak_frac": round(c.ops / (med8 * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4)}
             del copies
 
     # The scaled product (per-row / per-column scales, bf16 output) of every
@@ -282,7 +316,7 @@ def main() -> int:
             us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
             med = float(np.median(us))
             d_bytes = c.a_bytes + c.b_bytes + 2 * c.M * c.N + 4 * (c.M + c.N)
-            t_mfma = c.ops / (PEAK_INT8_TOPS * 1e12)
+            t_mfma = c.ops / (mfma_peak(w["plan"]["kernel"]) * 1e12)
             t_hbm = d_bytes / (PEAK_HBM_GBS * 1e9)
             scaled[c.name] = {"out": "bf16", "median_us": round(med, 3),
                               "tops": round(c.ops / (med * 1e-6) / 1e12, 2),
@@ -311,7 +345,7 @@ def main() -> int:
             torch.cuda.synchronize()
             us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
             med = float(np.median(us))
-            t_roof, bound = roofline_time_s(c)
+            t_roof, bound = roofline_time_s(c, w["plan"]["kernel"])
             cold[c.name] = {"median_us": round(med, 3), "min_us": round(float(us.min()), 3),
                             "p90_us": round(float(np.percentile(us, 90)), 3),
                             "tops": round(c.ops / (med * 1e-6) / 1e12, 2),
@@ -322,8 +356,10 @@ def main() -> int:
     _, dc, drec, davg = dominant
     if drec["bound"] == "mfma":
         achieved = dc.ops / (davg * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
-                "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
+        peak = mfma_peak(drec["kernel"])
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TOP/s", "frac": round(achieved / peak, 4),
+                "int8_peak_frac": round(achieved / PEAK_INT8_TOPS, 4)}
     else:
         achieved = dc.alg_bytes / (davg * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -343,7 +379,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8-mfma/int32 (int4 and int8 operands)",
+        "dtype": "int8-mfma/int32 and fp6-e3m2-mfma/fp32 (exact; int4 and int8 operands)",
         "data": "synthetic (seeded SplitMix64 bytes: uniform int8, uniform int4 nibbles)",
         "config": {"workload": "lpgemm suite: " + ", ".join(w["case"].name for w in work),
                    "cases": {w["case"].name: [w["case"].variant, w["case"].M, w["case"].N,

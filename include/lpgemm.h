@@ -25,7 +25,14 @@
  *
  * Conventions shared by every entry point
  *   - All data pointers are DEVICE pointers owned by the caller; the library
- *     allocates no memory and keeps no pointer after the call returns.
+ *     keeps no pointer after the call returns.
+ *   - Device memory: only the int4 x int4 FP6 path allocates.  Large int4 x
+ *     int4 calls (LPGEMM_KERNEL_FP6, below) re-encode A and B into a
+ *     temporary workspace of ((M+31)/32 + (N+31)/32) * ((K+63)/64) * 1536
+ *     bytes, taken from a library-owned stream-ordered memory pool on the
+ *     call's stream and returned to it on the same stream (the pool keeps the
+ *     memory for reuse until the process ends).  If that allocation fails the
+ *     call runs the int8 tiled kernel instead, with the same result.
  *   - Matrices are dense and row-major with no padding: A row stride is K/2
  *     bytes (packed) or K bytes (int8), B row stride K/2 bytes, C row stride
  *     N int32.
@@ -38,10 +45,13 @@
  *   - Calls are thread-safe.  Any alignment is accepted; 16-byte aligned
  *     bases with K a multiple of 32 take the fast kernels, anything else a
  *     slower general kernel with the same results.
- *   - Exactness: the kernels pre-scale 4-bit values by 16 inside int32, which
- *     is exact while 16384*K < 2^31, i.e. K <= 131070.  Larger K returns
- *     LPGEMM_ERR_UNSUPPORTED.  Within that range every result fits int32
- *     (|C| <= 64*K for int4 x int4, <= 1024*K for W4A8).
+ *   - Exactness: the int8 kernels pre-scale 4-bit values by 16 inside int32,
+ *     which is exact while 16384*K < 2^31, i.e. K <= 131070.  Larger K
+ *     returns LPGEMM_ERR_UNSUPPORTED.  Within that range every result fits
+ *     int32 (|C| <= 64*K for int4 x int4, <= 1024*K for W4A8).  The FP6 path
+ *     is exact over the same range: int4 values are exact in FP6 E3M2, each
+ *     product is an integer of magnitude <= 64, and every fp32 partial sum
+ *     (<= 64*K < 2^24) is an exact integer.
  */
 #ifndef LPGEMM_H
 #define LPGEMM_H
@@ -165,8 +175,13 @@ typedef enum lpgemm_kernel {
     LPGEMM_KERNEL_SKINNY = 3,    /* W4A8 narrow-M kernel streaming B once        */
     LPGEMM_KERNEL_TILED_128 = 4, /* block-tiled, 128 x 128 output tiles          */
     LPGEMM_KERNEL_TILED_256 = 5, /* block-tiled, 256 x 256 output tiles          */
-    LPGEMM_KERNEL_TILED_64 = 6   /* block-tiled, 64 x 64 output tiles            */
+    LPGEMM_KERNEL_TILED_64 = 6,  /* block-tiled, 64 x 64 output tiles            */
+    LPGEMM_KERNEL_FP6 = 7        /* int4 x int4: A, B re-encoded as FP6 E3M2,    */
+                                 /* 256 x 256 tiles on the FP6 matrix cores       */
 } lpgemm_kernel;
+/* LPGEMM_KERNEL_AUTO picks FP6 for int4 x int4 when the fast path applies,
+ * K >= 4096 and the 256 x 256 tiles number at least twice the compute units
+ * (the re-encoding pass then costs less than the matrix cores save). */
 
 typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
 

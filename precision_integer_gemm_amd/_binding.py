@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(_PKG, "_lpgemm.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 # lpgemm_kernel
 KERNEL_AUTO, KERNEL_GENERAL, KERNEL_TILED, KERNEL_SKINNY = 0, 1, 2, 3
-KERNEL_TILED_128, KERNEL_TILED_256, KERNEL_TILED_64 = 4, 5, 6
+KERNEL_TILED_128, KERNEL_TILED_256, KERNEL_TILED_64, KERNEL_FP6 = 4, 5, 6, 7
 KERNEL_NAMES = {KERNEL_AUTO: "auto", KERNEL_GENERAL: "general", KERNEL_TILED: "tiled",
-                KERNEL_SKINNY: "skinny"}
+                KERNEL_SKINNY: "skinny", KERNEL_FP6: "fp6"}
 # lpgemm_variant
 VARIANT_I4I4, VARIANT_W4A8 = 0, 1
 # lpgemm_out_dtype

@@ -9,6 +9,7 @@
 #include "gemm_general.hpp"
 #include "gemm_skinny.hpp"
 #include "gemm_pipelined.hpp"
+#include "gemm_fp6.hpp"
 
 using namespace lpgemm;
 
@@ -62,6 +63,13 @@ using I4Tiny = TiledKernel<I4I4, 1, 1, 2, 2, 256, 2>;
 using W8Tiny = TiledKernel<W4A8, 1, 1, 2, 2, 256, 2>;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
+// FP6 path (gemm_fp6.hpp): 256 x 256 tiles, 8 waves of 128 (m) x 64 (n), two
+// LDS stages of 128 k (96 KB).  Chosen automatically for int4 x int4 when K is
+// at least kFp6MinK and the 256-tiles number at least twice the compute units.
+constexpr int kFp6FM = 4, kFp6FN = 2, kFp6WM = 2, kFp6WN = 4, kFp6KS = 2, kFp6Stages = 2;
+using Fp6Tile = Fp6Cfg<kFp6FM, kFp6FN, kFp6WM, kFp6WN, kFp6KS, kFp6Stages>;
+constexpr int64_t kFp6MinK = 4096;
+
 // Skinny: 16 waves split K (up to 4 steps of 128 k each, A held in registers);
 // one workgroup per compute unit walks strips of 16 rows of B, staged in LDS.
 // (16 waves contract a strip faster than 8 with twice the steps each.)
@@ -99,18 +107,24 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
     const bool skinny_ok = fast_ok && variant == LPGEMM_VARIANT_W4A8 && M <= kSkinnyMaxM &&
                            K <= kSkinnyMaxK && N * (K / 2) < INT32_MAX;
 
+    const bool fp6_ok = fast_ok && variant == LPGEMM_VARIANT_I4I4;
+    const int64_t large_tiles = ceil_div(M, 256) * ceil_div(N, 256);
+
     lpgemm_kernel k = forced;
     if (k == LPGEMM_KERNEL_AUTO) {
         if (!fast_ok)
             k = LPGEMM_KERNEL_GENERAL;
         else if (skinny_ok)
             k = LPGEMM_KERNEL_SKINNY;
+        else if (fp6_ok && K >= kFp6MinK && large_tiles >= 2 * (int64_t)cu_count)
+            k = LPGEMM_KERNEL_FP6;
         else
             k = LPGEMM_KERNEL_TILED;
     }
     const bool tiled = k == LPGEMM_KERNEL_TILED || k == LPGEMM_KERNEL_TILED_128 ||
                        k == LPGEMM_KERNEL_TILED_256 || k == LPGEMM_KERNEL_TILED_64;
-    if ((tiled && !fast_ok) || (k == LPGEMM_KERNEL_SKINNY && !skinny_ok))
+    if ((tiled && !fast_ok) || (k == LPGEMM_KERNEL_SKINNY && !skinny_ok) ||
+        (k == LPGEMM_KERNEL_FP6 && !fp6_ok))
         return LPGEMM_ERR_UNSUPPORTED;
 
     Plan p;
@@ -130,7 +144,6 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         // Large tiles when they give at least 3/4 of a tile per compute unit;
         // else 128-tiles when they cover at least half of the compute units;
         // else 64-tiles.
-        const int64_t large_tiles = ceil_div(M, 256) * ceil_div(N, 256);
         const int64_t small_tiles = ceil_div(M, 128) * ceil_div(N, 128);
         if (k == LPGEMM_KERNEL_TILED)
             p.tile = large_tiles * 4 >= (int64_t)cu_count * 3 ? 256
@@ -151,6 +164,17 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         // Large tiles run one persistent workgroup per compute unit (their LDS
         // ring leaves room for one), each looping over tiles.
         if (p.tile == 256) p.workgroups = std::min<int64_t>(p.workgroups, cu_count);
+        break;
+    }
+    case LPGEMM_KERNEL_FP6: {
+        p.tile = 256;
+        p.tile_m = Fp6Tile::BM;
+        p.tile_n = Fp6Tile::BN;
+        p.threads = Fp6Tile::kThreads;
+        p.tiles_m = (int)ceil_div(M, Fp6Tile::BM);
+        p.tiles_n = (int)ceil_div(N, Fp6Tile::BN);
+        if ((int64_t)p.tiles_m * p.tiles_n > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+        p.workgroups = std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, cu_count);
         break;
     }
     case LPGEMM_KERNEL_SKINNY: {
@@ -221,6 +245,78 @@ lpgemm_status launch_skinny(const Plan &p, const int8_t *a, const uint8_t *b, Ep
     return launched();
 }
 
+// The FP6 path's workspace comes from one stream-ordered memory pool per
+// device, created on first use; freed blocks stay in the pool for reuse
+// (release threshold: never), so after the first calls an allocation costs no
+// driver round trip and never synchronizes.
+hipMemPool_t fp6_pool(int dev)
+{
+    static std::once_flag once[kMaxDevices];
+    static hipMemPool_t pools[kMaxDevices];
+    std::call_once(once[dev], [dev] {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        uint64_t keep = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        (void)hipGetLastError();
+        pools[dev] = pool;
+    });
+    return pools[dev];
+}
+
+// int4 x int4 on the FP6 matrix cores: re-encode A and B into a workspace,
+// multiply, release the workspace -- all on `stream`.  Without a workspace the
+// same plan runs on the int8 256-tile kernel.
+template <int OUT>
+lpgemm_status launch_fp6(const Plan &p, const uint8_t *a, const uint8_t *b, Epilogue epi, int m,
+                         int n, int k, hipStream_t stream)
+{
+    constexpr auto kernel = &gemm_fp6_kernel<kFp6FM, kFp6FN, kFp6WM, kFp6WN, kFp6KS, kFp6Stages, OUT>;
+    static std::once_flag once[kMaxDevices];
+    static hipError_t attr_err[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERR_HIP;
+    std::call_once(once[dev], [dev] {
+        attr_err[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            Fp6Tile::LDS_BYTES);
+    });
+    if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
+
+    const int64_t bytes_a = (fp6_bytes(m, k) + 255) / 256 * 256;
+    const int64_t bytes_b = fp6_bytes(n, k);
+    hipMemPool_t pool = fp6_pool(dev);
+    void *ws = nullptr;
+    if (pool == nullptr || hipMallocFromPoolAsync(&ws, (size_t)(bytes_a + bytes_b), pool, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return launch_tiled<I4Large, OUT>(p, a, b, epi, m, n, k, stream);
+    }
+    uint8_t *a6 = static_cast<uint8_t *>(ws);
+    uint8_t *b6 = a6 + bytes_a;
+    const unsigned kgroups = (unsigned)ceil_div(ceil_div(k, 64), 32);
+    hipLaunchKernelGGL(fp6_convert_kernel, dim3((unsigned)ceil_div(m, 32), kgroups), dim3(512), 0,
+                       stream, a, a6, (int64_t)m, k);
+    hipLaunchKernelGGL(fp6_convert_kernel, dim3((unsigned)ceil_div(n, 32), kgroups), dim3(512), 0,
+                       stream, b, b6, (int64_t)n, k);
+    const uint8_t *ca6 = a6, *cb6 = b6;
+    int tiles_m = p.tiles_m, tiles_n = p.tiles_n, xcds = kXcds;
+    void *args[] = {(void *)&ca6, (void *)&cb6, (void *)&epi, (void *)&m,       (void *)&n,
+                    (void *)&k,   (void *)&tiles_m, (void *)&tiles_n, (void *)&xcds};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel),
+                                         dim3((unsigned)p.workgroups), dim3(Fp6Tile::kThreads),
+                                         args, Fp6Tile::LDS_BYTES, stream);
+    const hipError_t f = hipFreeAsync(ws, stream);
+    return (e == hipSuccess && f == hipSuccess && hipGetLastError() == hipSuccess) ? LPGEMM_OK
+                                                                                   : LPGEMM_ERR_HIP;
+}
+
 // Launch the planned kernel for output format OUT.
 template <int OUT>
 lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, const void *B,
@@ -246,6 +342,8 @@ lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, 
         return p.tile == 256 ? launch_tiled<W8Large, OUT>(p, a, b, epi, m, n, k, stream)
                : p.tile == 128 ? launch_tiled<W8Small, OUT>(p, a, b, epi, m, n, k, stream)
                                : launch_tiled<W8Tiny, OUT>(p, a, b, epi, m, n, k, stream);
+    case LPGEMM_KERNEL_FP6:
+        return launch_fp6<OUT>(p, a, b, epi, m, n, k, stream);
     case LPGEMM_KERNEL_SKINNY: {
         const int8_t *a8 = static_cast<const int8_t *>(A);
         switch (p.k_steps) {
@@ -421,7 +519,7 @@ lpgemm_status lpgemm_plan(lpgemm_variant variant, const void *A, const void *B, 
 
 lpgemm_status lpgemm_set_kernel_override(lpgemm_kernel kernel)
 {
-    if (kernel < LPGEMM_KERNEL_AUTO || kernel > LPGEMM_KERNEL_TILED_64) return LPGEMM_ERR_INVALID_ARG;
+    if (kernel < LPGEMM_KERNEL_AUTO || kernel > LPGEMM_KERNEL_FP6) return LPGEMM_ERR_INVALID_ARG;
     g_override.store(kernel, std::memory_order_relaxed);
     return LPGEMM_OK;
 }

@@ -97,6 +97,20 @@ def test_tiled_kernel(torch, variant, M, N, K, tile):
     assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
 
 
+# The FP6 path (int4 x int4 only): tails in every dimension, K from one
+# k block to several stages, shapes smaller and larger than one 256-tile.
+FP6 = ALIGNED + [(1, 300, 64), (257, 1, 96), (513, 1000, 4160), (1000, 513, 8192),
+                 (33, 2100, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", FP6)
+def test_fp6_kernel(torch, M, N, K):
+    say(f"fp6 {M}x{N}x{K}")
+    A, B = custom_operands("i4i4", M, N, K, seed=M * 7 + N * 3 + K)
+    got = run_gpu(torch, "i4i4", A, B, M, N, K, kernel=L.KERNEL_FP6)
+    assert np.array_equal(got, oracle_full("i4i4", A, B, M, N, K))
+
+
 @pytest.mark.parametrize("M,N,K", SKINNY)
 def test_skinny_kernel(torch, M, N, K):
     say(f"skinny w4a8 {M}x{N}x{K}")
@@ -142,6 +156,9 @@ def test_largest_k_closed_forms(torch, variant, K):
         A, want = np.full((M, K), -128, dtype=np.int8), 1024 * K            # (-128)(-8)
     got = run_gpu(torch, variant, A, B, M, N, K)
     assert (got == want).all()
+    if variant == "i4i4" and K % 32 == 0:
+        # the FP6 path's fp32 accumulator holds 64 K < 2^24 exactly
+        assert (run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_FP6) == want).all()
     # mixed signs: b = +7 in odd k, -8 in even k; a = -8 (i4i4) or 127 (w4a8)
     B2 = np.full((N, K // 2), 0x78, dtype=np.uint8)
     if variant == "i4i4":
@@ -151,6 +168,8 @@ def test_largest_k_closed_forms(torch, variant, K):
         want2 = (K // 2) * (127 * -8 + 127 * 7)
     got2 = run_gpu(torch, variant, A, B2, M, N, K)
     assert (got2 == want2).all()
+    if variant == "i4i4" and K % 32 == 0:
+        assert (run_gpu(torch, variant, A, B2, M, N, K, kernel=L.KERNEL_FP6) == want2).all()
 
 
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
@@ -203,6 +222,17 @@ def test_named_case_full_parity(torch, name):
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
 
 
+@pytest.mark.parametrize("name", ["i4i4_ragged", "i4i4_1024"])
+def test_named_case_full_parity_fp6(torch, name):
+    # the FP6 path on named int4 x int4 workloads the automatic choice gives to
+    # the int8 kernel (ragged edges in M; a single k group of 1024)
+    c = CASES[name]
+    say(f"case {name} forced fp6")
+    A, B = operands(c)
+    got = run_gpu(torch, c.variant, A, B, c.M, c.N, c.K, kernel=L.KERNEL_FP6)
+    assert np.array_equal(got, oracle_full(c.variant, A, B, c.M, c.N, c.K))
+
+
 def _np_unpack(packed):
     b = np.ascontiguousarray(packed).view(np.uint8)
     lo = ((b << 4).astype(np.uint8)).view(np.int8) >> 4
@@ -210,11 +240,12 @@ def _np_unpack(packed):
     return np.stack([lo, hi], axis=-1).reshape(b.shape[0], -1)
 
 
-def test_largest_case_sampled_rows_columns_and_row_sums(torch):
+@pytest.mark.parametrize("kernel", [L.KERNEL_AUTO, L.KERNEL_TILED_256], ids=["auto-fp6", "int8-256"])
+def test_largest_case_sampled_rows_columns_and_row_sums(torch, kernel):
     c = CASES["i4i4_8192"]
-    say(f"case {c.name}: sampled")
+    say(f"case {c.name}: sampled, kernel {kernel} plan={L.lpgemm_plan(L.VARIANT_I4I4, c.M, c.N, c.K)}")
     A, B = operands(c)
-    got = run_gpu(torch, c.variant, A, B, c.M, c.N, c.K)
+    got = run_gpu(torch, c.variant, A, B, c.M, c.N, c.K, kernel=kernel)
     rng = np.random.default_rng(2024)
     # 8192 random elements, plus 8 whole rows and 8 whole columns (edges included)
     ms = rng.integers(0, c.M, 8192)

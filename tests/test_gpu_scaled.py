@@ -114,6 +114,16 @@ def test_tiled_kernel(torch, variant, fmt, M, N, K, tile):
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("M,N,K", TILED)
+def test_fp6_kernel(torch, fmt, M, N, K):
+    say(f"scaled fp6 {fmt} {M}x{N}x{K}")
+    A, B = custom_operands("i4i4", M, N, K, seed=3 * M + K)
+    sa, sb = scale_vector(M + 2 * K, 0, M), scale_vector(M + 2 * K, 1, N)
+    got = run_scaled(torch, "i4i4", A, B, sa, sb, M, N, K, fmt, kernel=L.KERNEL_FP6)
+    check(got, oracle.gemm_scaled("i4i4", A, B, sa, sb, M, N, K, FORMATS[fmt][1]))
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
 @pytest.mark.parametrize("M,N,K", SKINNY)
 def test_skinny_kernel(torch, fmt, M, N, K):
     say(f"scaled skinny {fmt} {M}x{N}x{K}")
@@ -143,6 +153,26 @@ def test_named_case_bf16(torch, name):
     sa, sb = scale_vector(c.seed, 0, c.M), scale_vector(c.seed, 1, c.N)
     got = run_scaled(torch, c.variant, A, B, sa, sb, c.M, c.N, c.K, "bf16")
     check(got, oracle.gemm_scaled(c.variant, A, B, sa, sb, c.M, c.N, c.K, oracle.FMT_BF16))
+
+
+def test_largest_case_bf16_rows_and_columns(torch):
+    # 8192^3 int4 x int4 in its benchmarked launch (the FP6 path), bf16 output:
+    # whole rows and columns against the oracle's integer results and epilogue
+    c = CASES["i4i4_8192"]
+    say(f"scaled case {c.name} bf16, plan={L.lpgemm_plan(L.VARIANT_I4I4, c.M, c.N, c.K)}")
+    A, B = operands(c)
+    sa, sb = scale_vector(c.seed, 0, c.M), scale_vector(c.seed, 1, c.N)
+    got = run_scaled(torch, c.variant, A, B, sa, sb, c.M, c.N, c.K, "bf16")
+    for m in (0, 255, 256, 4097, c.M - 1):
+        cm = oracle.gemm_i4i4_at(A, B, c.M, c.N, c.K, np.full(c.N, m), np.arange(c.N))
+        want = oracle.scaled_epilogue(cm.reshape(1, c.N).astype(np.int32), sa[m:m + 1], sb,
+                                      oracle.FMT_BF16)
+        check(got[m:m + 1], want)
+    for n in (0, 3, 255, 6001, c.N - 1):
+        cn = oracle.gemm_i4i4_at(A, B, c.M, c.N, c.K, np.arange(c.M), np.full(c.M, n))
+        want = oracle.scaled_epilogue(cn.reshape(c.M, 1).astype(np.int32), sa, sb[n:n + 1],
+                                      oracle.FMT_BF16)
+        check(got[:, n:n + 1], want)
 
 
 def test_tensor_wrappers(torch):

@@ -94,7 +94,10 @@ def test_pack_unpack_argument_errors():
 
 def test_kernel_override_rejects_unknown_values():
     with pytest.raises(L.LpgemmError):
-        L.lpgemm_set_kernel_override(7)
+        L.lpgemm_set_kernel_override(8)
+    with pytest.raises(L.LpgemmError):
+        L.lpgemm_set_kernel_override(-1)
+    L.lpgemm_set_kernel_override(L.KERNEL_FP6)
     L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
 
 
@@ -103,8 +106,11 @@ def test_kernel_override_rejects_unknown_values():
     (L.VARIANT_W4A8, 16, 28672, 8192, "skinny"),
     (L.VARIANT_W4A8, 1, 28672, 8192, "skinny"),
     (L.VARIANT_W4A8, 4096, 4096, 4096, "tiled"),
-    (L.VARIANT_I4I4, 8192, 8192, 8192, "tiled"),
-    (L.VARIANT_I4I4, 3000, 5120, 6144, "tiled"),
+    (L.VARIANT_I4I4, 8192, 8192, 8192, "fp6"),     # 1024 tiles >= 2 x 256 CUs, K >= 4096
+    (L.VARIANT_I4I4, 3000, 5120, 6144, "tiled"),   # 240 tiles: too few for the FP6 pass
+    (L.VARIANT_I4I4, 8192, 8192, 2048, "tiled"),   # K below 4096
+    (L.VARIANT_I4I4, 8192, 4096, 4096, "fp6"),     # 512 tiles
+    (L.VARIANT_W4A8, 8192, 8192, 8192, "tiled"),   # FP6 is int4 x int4 only
     (L.VARIANT_I4I4, 256, 256, 256, "tiled"),
     (L.VARIANT_I4I4, 17, 33, 34, "general"),     # K % 32 != 0
     (L.VARIANT_W4A8, 16, 100, 34, "general"),
@@ -113,8 +119,33 @@ def test_auto_plan(variant, M, N, K, kernel):
     assert L.lpgemm_plan(variant, M, N, K)["kernel"] == kernel
 
 
+def test_fp6_plan():
+    p = L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192)
+    assert (p["kernel"], p["tile_m"], p["tile_n"], p["workgroups"], p["threads"]) == ("fp6", 256, 256, 256, 512)
+    # fewer CUs: the same shape has enough tiles; more CUs: not enough
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=304)["kernel"] == "fp6"
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=1024)["kernel"] == "tiled"
+    # the FP6 path needs the fast-path conditions (K % 32, 16-byte alignment)
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8194)["kernel"] == "general"
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, B=P + 8)["kernel"] == "general"
+    try:
+        L.lpgemm_set_kernel_override(L.KERNEL_FP6)
+        assert L.lpgemm_plan(L.VARIANT_I4I4, 1, 1, 32)["kernel"] == "fp6"
+        assert L.lpgemm_plan(L.VARIANT_I4I4, 300, 5000, 64)["workgroups"] == 40
+        for args in [(L.VARIANT_W4A8, 64, 64, 64), (L.VARIANT_I4I4, 64, 64, 66)]:
+            with pytest.raises(L.LpgemmError) as e:
+                L.lpgemm_plan(*args)
+            assert e.value.status == L.ERR_UNSUPPORTED
+    finally:
+        L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
+
+
 def test_tile_size_follows_the_number_of_tiles():
-    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192)["tile_m"] == 256
+    L.lpgemm_set_kernel_override(L.KERNEL_TILED)
+    try:
+        assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192)["tile_m"] == 256
+    finally:
+        L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
     assert L.lpgemm_plan(L.VARIANT_W4A8, 4096, 4096, 4096)["tile_m"] == 256
     assert L.lpgemm_plan(L.VARIANT_I4I4, 3000, 5120, 6144)["tile_m"] == 256  # 240 tiles
     assert L.lpgemm_plan(L.VARIANT_I4I4, 2048, 2048, 2048)["tile_m"] == 128  # 256 tiles of 128
