@@ -278,3 +278,29 @@ def test_device_pack_unpack_match_oracle(torch):
     allb = np.arange(256, dtype=np.uint8).reshape(1, 256)
     out = L.lpgemm_unpack_int4(torch.from_numpy(allb).to(dev)).cpu().numpy()
     assert np.array_equal(out, oracle.unpack_int4(allb, 512))
+
+
+def test_fp6_workspace_on_two_streams(torch):
+    # Two FP6-path calls in flight on different streams at once: each call takes
+    # its own workspace from the stream-ordered pool, so neither sees the other's
+    # re-encoded operands.
+    say("fp6 two streams")
+    dev = torch.device("cuda:0")
+    shapes = [(640, 768, 4160), (512, 1024, 4096)]
+    cases = []
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = custom_operands("i4i4", M, N, K, seed=900 + i)
+        cases.append((M, N, K, A, B, torch.from_numpy(np.ascontiguousarray(A).view(np.uint8)).to(dev),
+                      torch.from_numpy(B).to(dev)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full((M, N), SENTINEL, dtype=torch.int32, device=dev) for M, N, *_ in cases]
+    torch.cuda.synchronize()
+    L.lpgemm_set_kernel_override(L.KERNEL_FP6)
+    for rep in range(3):
+        for (M, N, K, A, B, a_t, b_t), s, c_t in zip(cases, streams, outs):
+            st = L.lib().lpgemm_int4_int4(a_t.data_ptr(), b_t.data_ptr(), c_t.data_ptr(), M, N, K,
+                                          s.cuda_stream)
+            assert st == L.OK, L.lpgemm_status_string(st)
+    torch.cuda.synchronize()
+    for (M, N, K, A, B, *_), c_t in zip(cases, outs):
+        assert np.array_equal(c_t.cpu().numpy(), oracle_full("i4i4", A, B, M, N, K))
