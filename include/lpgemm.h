@@ -180,8 +180,9 @@ typedef enum lpgemm_kernel {
                                  /* 256 x 256 tiles on the FP6 matrix cores       */
 } lpgemm_kernel;
 /* LPGEMM_KERNEL_AUTO picks FP6 for int4 x int4 when the fast path applies,
- * K >= 4096 and the 256 x 256 tiles number at least twice the compute units
- * (the re-encoding pass then costs less than the matrix cores save). */
+ * K >= 2048, the 256 x 256 output tiles number at least the compute units, and
+ * either twice the compute units or K >= 8192 (there the re-encoding pass
+ * costs less than the matrix cores save). */
 
 typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
 

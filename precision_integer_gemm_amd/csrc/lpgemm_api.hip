@@ -64,11 +64,20 @@ using W8Tiny = TiledKernel<W4A8, 1, 1, 2, 2, 256, 2>;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 // FP6 path (gemm_fp6.hpp): 256 x 256 tiles, 8 waves of 128 (m) x 64 (n), two
-// LDS stages of 128 k (96 KB).  Chosen automatically for int4 x int4 when K is
-// at least kFp6MinK and the 256-tiles number at least twice the compute units.
+// LDS stages of 128 k (96 KB).  Chosen automatically for int4 x int4 when the
+// re-encoding pass pays for itself (measured against the int8 256-tile kernel,
+// interleaved): at least one 256-tile per compute unit and K >= 2048, with
+// either two tiles per compute unit or K >= 8192 (8192^2 x 2048: 6% faster,
+// 4096^2 x 16384: 8% faster; 4096^3 and 3000 x 5120 x 6144: 5-8% slower).
 constexpr int kFp6FM = 4, kFp6FN = 2, kFp6WM = 2, kFp6WN = 4, kFp6KS = 2, kFp6Stages = 2;
 using Fp6Tile = Fp6Cfg<kFp6FM, kFp6FN, kFp6WM, kFp6WN, kFp6KS, kFp6Stages>;
-constexpr int64_t kFp6MinK = 4096;
+constexpr int64_t kFp6MinK = 2048, kFp6LongK = 8192;
+
+bool fp6_pays(int64_t K, int64_t tiles256, int cu_count)
+{
+    return K >= kFp6MinK && tiles256 >= cu_count &&
+           (tiles256 >= 2 * (int64_t)cu_count || K >= kFp6LongK);
+}
 
 // Skinny: 16 waves split K (up to 4 steps of 128 k each, A held in registers);
 // one workgroup per compute unit walks strips of 16 rows of B, staged in LDS.
@@ -116,7 +125,7 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
             k = LPGEMM_KERNEL_GENERAL;
         else if (skinny_ok)
             k = LPGEMM_KERNEL_SKINNY;
-        else if (fp6_ok && K >= kFp6MinK && large_tiles >= 2 * (int64_t)cu_count)
+        else if (fp6_ok && fp6_pays(K, large_tiles, cu_count))
             k = LPGEMM_KERNEL_FP6;
         else
             k = LPGEMM_KERNEL_TILED;

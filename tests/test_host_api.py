@@ -108,8 +108,12 @@ def test_kernel_override_rejects_unknown_values():
     (L.VARIANT_W4A8, 4096, 4096, 4096, "tiled"),
     (L.VARIANT_I4I4, 8192, 8192, 8192, "fp6"),     # 1024 tiles >= 2 x 256 CUs, K >= 4096
     (L.VARIANT_I4I4, 3000, 5120, 6144, "tiled"),   # 240 tiles: too few for the FP6 pass
-    (L.VARIANT_I4I4, 8192, 8192, 2048, "tiled"),   # K below 4096
+    (L.VARIANT_I4I4, 8192, 8192, 2048, "fp6"),     # 1024 tiles, K = 2048
+    (L.VARIANT_I4I4, 8192, 8192, 1024, "tiled"),   # K below 2048
     (L.VARIANT_I4I4, 8192, 4096, 4096, "fp6"),     # 512 tiles
+    (L.VARIANT_I4I4, 4096, 4096, 4096, "tiled"),   # 256 tiles, K below 8192
+    (L.VARIANT_I4I4, 4096, 4096, 16384, "fp6"),    # 256 tiles, K >= 8192
+    (L.VARIANT_I4I4, 3840, 4096, 16384, "tiled"),  # 240 tiles: fewer than the CUs
     (L.VARIANT_W4A8, 8192, 8192, 8192, "tiled"),   # FP6 is int4 x int4 only
     (L.VARIANT_I4I4, 256, 256, 256, "tiled"),
     (L.VARIANT_I4I4, 17, 33, 34, "general"),     # K % 32 != 0
@@ -124,7 +128,9 @@ def test_fp6_plan():
     assert (p["kernel"], p["tile_m"], p["tile_n"], p["workgroups"], p["threads"]) == ("fp6", 256, 256, 256, 512)
     # fewer CUs: the same shape has enough tiles; more CUs: not enough
     assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=304)["kernel"] == "fp6"
-    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=1024)["kernel"] == "tiled"
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=1024)["kernel"] == "fp6"   # K >= 8192
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 4096, cu_count=1024)["kernel"] == "tiled"
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=1100)["kernel"] == "tiled"
     # the FP6 path needs the fast-path conditions (K % 32, 16-byte alignment)
     assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8194)["kernel"] == "general"
     assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, B=P + 8)["kernel"] == "general"
