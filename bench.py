@@ -70,8 +70,8 @@ def mfma_peak(kernel: str) -> float:
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328969.5, "fetch_scale": 2.0, "write_kib": 366728.3,
-                  "write_scale": 1.0, "sources_sha256": "795326cab758155686d7357df0a9fc65c6f1f62c82e6a13a222323f4bb69efa3"},
+    "i4i4_8192": {"fetch_kib": 329128.4, "fetch_scale": 2.0, "write_kib": 364932.6,
+                  "write_scale": 1.0, "sources_sha256": "5356ab4332994a250a257c37269a31d0ed6dcb617ddc9fbd128f89b2a18cb9b6"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",
