@@ -15,11 +15,16 @@ Pages cited (by title):
   * tilelang PR "[Example] add w4a8 gemm kernel" (#815), reviews of
     torch_convert / ref_program.
   * TileLang tutorial ch. 14 sec. 5 "low_precision_gemm.py", pack_int4,
-    matmul_int4 and gemm_blockscaled (the scaled epilogue, one K block).
+    matmul_int4, gemm_blockscaled (the scaled epilogue, one K block) and
+    gemm_fp8 (the fp8 GEMM: e4m3 operands, fp32 accumulation, fp8 C).
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` against
-hand-worked values, closed forms, brute force and an independent numpy
-computation; no function is left unpinned.
+Every function here is pinned: the integer GEMMs and pack/unpack by
+``tests/test_oracle_pins.py`` (hand-worked values, closed forms, brute force,
+an independent numpy computation), the scaled epilogue by
+``tests/test_oracle_scaled.py``, the e4m3 decode/encode and the fp8 product by
+``tests/test_oracle_fp8.py`` (PyTorch's float8_e4m3fn, exact rationals, closed
+forms); ``tests/test_oracle_mutants.py`` checks that planted mistakes fail
+them.  No function is left unpinned.
 """
 from __future__ import annotations
 
@@ -74,6 +79,12 @@ def _load():
         f = getattr(lib, name)
         f.argtypes = [p, p, i64, i64, i64, p, p, i64, p]
         f.restype = ctypes.c_int
+    for name in ("oracle_fp8_e4m3_decode", "oracle_fp8_e4m3_encode"):
+        f = getattr(lib, name)
+        f.argtypes = [p, i64, p]
+        f.restype = ctypes.c_int
+    lib.oracle_gemm_fp8.argtypes = [p, p, i64, i64, i64, p, p]
+    lib.oracle_gemm_fp8.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -206,3 +217,31 @@ def gemm_scaled(variant: str, A, B_packed, scale_a, scale_b, M: int, N: int, K: 
     """The scaled product: the exact integer GEMM, then the scaled epilogue."""
     C = (gemm_i4i4 if variant == "i4i4" else gemm_w4a8)(A, B_packed, M, N, K)
     return scaled_epilogue(C, scale_a, scale_b, fmt)
+
+
+# ---- fp8 GEMM (the tutorial's gemm_fp8 structure, e4m3 operands) ------------------
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Value of each e4m3 byte (float64; NaN for the NaN codes)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _check(_load().oracle_fp8_e4m3_decode(_ptr(c), c.size, _ptr(out)), "fp8_e4m3_decode")
+    return out
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """Nearest e4m3 code of each value, ties to even, saturating at +-448."""
+    v = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _check(_load().oracle_fp8_e4m3_encode(_ptr(v), v.size, _ptr(out)), "fp8_e4m3_encode")
+    return out
+
+
+def gemm_fp8(A, B, M: int, N: int, K: int):
+    """(C, Cabs): the exact sums C = A . B^T of the decoded e4m3 operands and the
+    sums of the products' magnitudes, float64 [M, N] each."""
+    a = _bytes2d(A, M, K, "A")
+    b = _bytes2d(B, N, K, "B")
+    C = np.zeros((M, N), dtype=np.float64)
+    Cabs = np.zeros((M, N), dtype=np.float64)
+    _check(_load().oracle_gemm_fp8(_ptr(a), _ptr(b), M, N, K, _ptr(C), _ptr(Cabs)), "gemm_fp8")
+    return C, Cabs

@@ -263,3 +263,104 @@ int oracle_scaled_epilogue(const int32_t *C, const float *scale_a, const float *
         }
     return 0;
 }
+
+/* ---- fp8 GEMM (second workload) ---------------------------------------------
+ * [tutorial] gemm_fp8 (chapter 14, the fp8 example next to matmul_int4): the
+ * same A[M,K] . B[N,K]^T structure (T.gemm(..., transpose_B=True)) with fp8
+ * operands (determine_fp8_type: the e4m3 format), a float32 accumulator, and C
+ * stored in the fp8 dtype.  The pages leave the numerics to another chapter;
+ * the oracle gives the exact value of every sum (the kernel's fp32 result is
+ * compared within a stated bound) and the conversion to e4m3 written out.
+ *
+ * E4M3 (the OCP 8-bit format without infinities, "e4m3fn"): bit 7 sign, bits
+ * 6..3 exponent with bias 7, bits 2..0 mantissa.  Exponent 0 is subnormal
+ * (m/8 * 2^-6); S.1111.111 is NaN; every other code is (1 + m/8) * 2^(e-7), so
+ * the largest finite magnitude is 1.75 * 2^8 = 448. */
+static double e4m3_value(uint8_t c)
+{
+    const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);              /* m/8 * 2^-6 */
+    else
+        v = ldexp(8.0 + m, e - 10);            /* (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+int oracle_fp8_e4m3_decode(const uint8_t *codes, int64_t n, double *out)
+{
+    if (n < 0) return ORACLE_ERR_ARG;
+    if (n == 0) return ORACLE_OK;
+    if (!codes || !out) return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_value(codes[i]);
+    return ORACLE_OK;
+}
+
+/* Nearest e4m3 code of x, ties to the even code (the one whose mantissa is
+ * even), magnitudes beyond 448 saturating to +-448 (the finite-saturating
+ * conversion); NaN -> the NaN code with x's sign.  Written as a search over the
+ * 127 non-negative finite codes, which are ordered by value. */
+static uint8_t e4m3_encode(double x)
+{
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x)) return sign | 0x7F;
+    const double ax = fabs(x);
+    if (ax >= 448.0) return sign | 0x7E;
+    int lo = 0;                                /* largest code with value <= ax */
+    for (int c = 1; c <= 0x7E; ++c)
+        if (e4m3_value((uint8_t)c) <= ax) lo = c;
+    if (e4m3_value((uint8_t)lo) == ax) return sign | (uint8_t)lo;
+    const int hi = lo + 1;                     /* next larger value (<= 0x7E) */
+    const double dlo = ax - e4m3_value((uint8_t)lo), dhi = e4m3_value((uint8_t)hi) - ax;
+    if (dlo < dhi) return sign | (uint8_t)lo;
+    if (dhi < dlo) return sign | (uint8_t)hi;
+    return sign | (uint8_t)((lo & 1) ? hi : lo);   /* tie: even mantissa */
+}
+
+int oracle_fp8_e4m3_encode(const double *x, int64_t n, uint8_t *out)
+{
+    if (n < 0) return ORACLE_ERR_ARG;
+    if (n == 0) return ORACLE_OK;
+    if (!x || !out) return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode(x[i]);
+    return ORACLE_OK;
+}
+
+/* C[m][n] = sum_k a(m,k) * b(n,k) over the decoded e4m3 values, and
+ * Cabs[m][n] = sum_k |a(m,k) * b(n,k)|, both in double.  Every product is a
+ * multiple of 2^-18 below 2^18 in magnitude, so for K < 2^17 each running sum
+ * is a multiple of 2^-18 below 2^35 and the double sums are exact.  A NaN
+ * operand gives a NaN sum. */
+int oracle_gemm_fp8(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K,
+                    double *C, double *Cabs)
+{
+    if (M < 0 || N < 0 || K < 0 || K >= ((int64_t)1 << 17)) return ORACLE_ERR_ARG;
+    if (M == 0 || N == 0) return ORACLE_OK;
+    if (!C || !Cabs || (K > 0 && (!A || !B))) return ORACLE_ERR_ARG;
+    double *a = (double *)malloc(sizeof(double) * (size_t)(M * K + 1));
+    double *b = (double *)malloc(sizeof(double) * (size_t)(N * K + 1));
+    if (!a || !b) {
+        free(a);
+        free(b);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (int64_t i = 0; i < M * K; ++i) a[i] = e4m3_value(A[i]);
+    for (int64_t i = 0; i < N * K; ++i) b[i] = e4m3_value(B[i]);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0, sa = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = a[m * K + k] * b[n * K + k];
+                s += p;
+                sa += fabs(p);
+            }
+            C[m * N + n] = s;
+            Cabs[m * N + n] = sa;
+        }
+    free(a);
+    free(b);
+    return ORACLE_OK;
+}

@@ -50,10 +50,24 @@ SCALED_MUTANTS = [
 ]
 
 
+# Mistakes in the fp8 (e4m3) oracle, caught by test_oracle_fp8.py.
+FP8_MUTANTS = [
+    ("e4m3 bias 8", "v = ldexp(8.0 + m, e - 10);", "v = ldexp(8.0 + m, e - 11);"),
+    ("e4m3 subnormal scale", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    ("e4m3 NaN code not special", "if (e == 15 && m == 7)\n        return NAN;", "if (0)\n        return NAN;"),
+    ("e4m3 ties up", "if (dhi < dlo) return sign | (uint8_t)hi;", "if (dhi <= dlo) return sign | (uint8_t)hi;"),
+    ("e4m3 no saturation", "if (ax >= 448.0) return sign | 0x7E;", "if (ax >= 464.0) return sign | 0x7F;"),
+    ("fp8 last k dropped", "for (int64_t k = 0; k < K; ++k) {\n                const double p",
+     "for (int64_t k = 0; k + 1 < K; ++k) {\n                const double p"),
+    ("fp8 abs sum signed", "sa += fabs(p);", "sa += p;"),
+]
+
+
 @pytest.mark.parametrize("what,old,new,pins",
                          [m + ("tests/test_oracle_pins.py",) for m in MUTANTS] +
-                         [m + ("tests/test_oracle_scaled.py",) for m in SCALED_MUTANTS],
-                         ids=[m[0] for m in MUTANTS + SCALED_MUTANTS])
+                         [m + ("tests/test_oracle_scaled.py",) for m in SCALED_MUTANTS] +
+                         [m + ("tests/test_oracle_fp8.py",) for m in FP8_MUTANTS],
+                         ids=[m[0] for m in MUTANTS + SCALED_MUTANTS + FP8_MUTANTS])
 def test_pins_catch_planted_mistake(tmp_path, what, old, new, pins):
     for d in ("oracle", "tests", "precision_integer_gemm_amd"):
         shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
