@@ -105,9 +105,10 @@ lpgemm_status lpgemm_w4a8(const int8_t *A, const uint8_t *B_packed, int32_t *C,
 
 /* Element type of a scaled result. */
 typedef enum lpgemm_out_dtype {
-    LPGEMM_OUT_F32 = 0,  /* IEEE binary32                                  */
-    LPGEMM_OUT_BF16 = 1, /* bfloat16 bits (upper half of a binary32)       */
-    LPGEMM_OUT_F16 = 2   /* IEEE binary16                                  */
+    LPGEMM_OUT_F32 = 0,     /* IEEE binary32                               */
+    LPGEMM_OUT_BF16 = 1,    /* bfloat16 bits (upper half of a binary32)    */
+    LPGEMM_OUT_F16 = 2,     /* IEEE binary16                               */
+    LPGEMM_OUT_FP8_E4M3 = 3 /* e4m3 byte (lpgemm_fp8_e4m3 only)            */
 } lpgemm_out_dtype;
 
 /*
@@ -141,6 +142,34 @@ lpgemm_status lpgemm_int4_int4_scaled(const void *A_packed, const void *B_packed
 lpgemm_status lpgemm_w4a8_scaled(const int8_t *A, const uint8_t *B_packed, const float *scale_a,
                                  const float *scale_b, void *D, lpgemm_out_dtype out_dtype,
                                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * fp8 GEMM (second workload):  C[m][n] = out( sum_k a(m,k) * b(n,k) )
+ *   A          device, e4m3 bytes [M][K]
+ *   B          device, e4m3 bytes [N][K]
+ *   C          device, [M][N] binary32 (LPGEMM_OUT_F32) or e4m3 bytes
+ *              (LPGEMM_OUT_FP8_E4M3), written
+ *   M, N, K    any sizes >= 0, K <= LPGEMM_MAX_K
+ * E4M3 is the OCP 8-bit format without infinities: sign, 4 exponent bits
+ * (bias 7), 3 mantissa bits; exponent 0 is subnormal; S.1111.111 is NaN; the
+ * largest finite magnitude is 448.  Every product is exact in binary32; the
+ * sum is accumulated in binary32 in an unspecified order, so it lies within
+ * K * 2^-24 * sum_k |a(m,k) b(n,k)| of the exact sum.  An e4m3 result rounds
+ * that binary32 sum to nearest, ties to even, saturating at +-448 (NaN stays
+ * NaN).  K == 0 writes zeros.
+ * Returns LPGEMM_ERR_INVALID_ARG for negative sizes, a null pointer that would
+ * be dereferenced, or an out_dtype other than the two above;
+ * LPGEMM_ERR_UNSUPPORTED for K above LPGEMM_MAX_K; LPGEMM_ERR_HIP if a launch
+ * failed.  16-byte aligned A and B with K % 16 == 0 (and C aligned to 16 bytes
+ * for binary32, 4 for e4m3) take the tiled matrix-core kernel, anything else
+ * a slower one-thread-per-element kernel.
+ * Defined by the TileLang tutorial's gemm_fp8 (chapter 14): A[M,K] and B[N,K]
+ * in the fp8 dtype (e4m3), T.gemm(..., transpose_B=True) into a float32
+ * accumulator, C stored in the fp8 dtype.
+ */
+lpgemm_status lpgemm_fp8_e4m3(const uint8_t *A, const uint8_t *B, void *C,
+                              lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                              hipStream_t stream);
 
 /*
  * Pack logical int4 values (held one per int8) into bytes, on the device:

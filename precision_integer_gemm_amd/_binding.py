@@ -23,12 +23,12 @@ KERNEL_NAMES = {KERNEL_AUTO: "auto", KERNEL_GENERAL: "general", KERNEL_TILED: "t
 # lpgemm_variant
 VARIANT_I4I4, VARIANT_W4A8 = 0, 1
 # lpgemm_out_dtype
-OUT_F32, OUT_BF16, OUT_F16 = 0, 1, 2
+OUT_F32, OUT_BF16, OUT_F16, OUT_FP8_E4M3 = 0, 1, 2, 3
 MAX_K = 131070
 
 EXPORTS = ("lpgemm_int4_int4", "lpgemm_w4a8", "lpgemm_int4_int4_scaled", "lpgemm_w4a8_scaled",
-           "lpgemm_pack_int4", "lpgemm_unpack_int4", "lpgemm_status_string", "lpgemm_plan",
-           "lpgemm_set_kernel_override")
+           "lpgemm_fp8_e4m3", "lpgemm_pack_int4", "lpgemm_unpack_int4", "lpgemm_status_string",
+           "lpgemm_plan", "lpgemm_set_kernel_override")
 
 
 class LpgemmError(RuntimeError):
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = [p, p, p, p, p, ctypes.c_int, i64, i64, i64, p]
         f.restype = ctypes.c_int
+    L.lpgemm_fp8_e4m3.argtypes = [p, p, p, ctypes.c_int, i64, i64, i64, p]
+    L.lpgemm_fp8_e4m3.restype = ctypes.c_int
     for name in ("lpgemm_pack_int4", "lpgemm_unpack_int4"):
         f = getattr(L, name)
         f.argtypes = [p, p, i64, i64, p]
@@ -236,6 +238,38 @@ def lpgemm_w4a8_scaled(A, B_packed, scale_a, scale_b, *, dtype=None, out=None, s
                                     scale_b.data_ptr(), D.data_ptr(), _out_code(dtype), M, N, K,
                                     _stream_handle(stream)), "lpgemm_w4a8_scaled")
     return D
+
+
+def lpgemm_fp8_e4m3(A, B, *, dtype=None, out=None, stream=None):
+    """C[M,N] = A . B^T of e4m3 operands (uint8 codes or torch.float8_e4m3fn
+    tensors [M,K] and [N,K]) with fp32 accumulation; C as float32 (default) or
+    e4m3 codes (dtype=torch.uint8 or torch.float8_e4m3fn)."""
+    torch = _torch()
+    f8 = getattr(torch, "float8_e4m3fn", None)
+    ok = (torch.uint8,) + ((f8,) if f8 is not None else ())
+    _check_dev(A, "A", ok)
+    _check_dev(B, "B", ok)
+    M, K = A.shape
+    N, K_b = B.shape
+    if K != K_b:
+        raise ValueError(f"K mismatch: A has K={K}, B has {K_b}")
+    dtype = dtype or (out.dtype if out is not None else torch.float32)
+    if dtype == torch.float32:
+        code = OUT_F32
+    elif dtype in ok:
+        code = OUT_FP8_E4M3
+    else:
+        raise TypeError("dtype must be torch.float32, torch.uint8 or torch.float8_e4m3fn")
+    if out is None:
+        C = torch.empty((M, N), dtype=dtype, device=A.device)
+    else:
+        _check_dev(out, "out", (dtype,))
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must have shape ({M}, {N}), got {tuple(out.shape)}")
+        C = out
+    _raise(lib().lpgemm_fp8_e4m3(A.data_ptr(), B.data_ptr(), C.data_ptr(), code, M, N, K,
+                                 _stream_handle(stream)), "lpgemm_fp8_e4m3")
+    return C
 
 
 def lpgemm_pack_int4(logical, *, out=None, stream=None):

@@ -36,8 +36,6 @@ namespace lpgemm {
 
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x6 __attribute__((ext_vector_type(6)));
-typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x32 __attribute__((ext_vector_type(32)));
 

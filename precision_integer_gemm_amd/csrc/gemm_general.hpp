@@ -46,6 +46,29 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(const uint8_t *__rest
     }
 }
 
+// fp8 (e4m3) product, one thread per output: exact products summed in fp32 in
+// k order; fp32 or e4m3 output.  Any K and alignment.
+template <int OUT>
+__global__ __launch_bounds__(256) void gemm_fp8_general_kernel(const uint8_t *__restrict__ A,
+                                                               const uint8_t *__restrict__ B,
+                                                               Epilogue epi, int64_t M, int64_t N,
+                                                               int64_t K)
+{
+    const int64_t n = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
+    const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
+    if (m >= M || n >= N) return;
+    const uint8_t *arow = A + m * K, *brow = B + n * K;
+    float sum = 0.f;
+    for (int64_t k = 0; k < K; ++k) {
+        const float p = e4m3_to_float(arow[k]) * e4m3_to_float(brow[k]);  // exact
+        sum += p;
+    }
+    if (OUT == OUT_F32)
+        static_cast<float *>(epi.out)[m * N + n] = sum;
+    else
+        static_cast<uint8_t *>(epi.out)[m * N + n] = (uint8_t)float_to_e4m3(sum);
+}
+
 // C[0 .. count) = 0: the empty sum (K == 0).  A kernel, not a memset, so the
 // call stays capturable in a graph.
 __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t *__restrict__ C, int64_t count)

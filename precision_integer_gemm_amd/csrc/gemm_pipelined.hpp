@@ -48,7 +48,7 @@ struct PipeCfg {
     static constexpr int BM = WM * FM * 32;
     static constexpr int BN = WN * FN * 32;
     static constexpr int RA = (VAR == I4I4) ? BK / 2 : BK;  // LDS bytes per A row
-    static constexpr int RB = BK / 2;                       // LDS bytes per B row
+    static constexpr int RB = (VAR == FP8) ? BK : BK / 2;   // LDS bytes per B row
     static constexpr int CPR_A = RA / 16;
     static constexpr int CPR_B = RB / 16;
     static constexpr int A_BYTES = BM * RA;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     const int wn = wave % WN;
 
     const uint32_t lda = (VAR == I4I4) ? (uint32_t)K / 2 : (uint32_t)K;  // global row bytes
-    const uint32_t ldb = (uint32_t)K / 2;
+    const uint32_t ldb = (VAR == FP8) ? (uint32_t)K : (uint32_t)K / 2;
     const int ktiles = (K + BK - 1) / BK;
 
     // Per-lane source of each DMA instruction: tile row and 16-byte column.
@@ -171,10 +171,12 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     const int h = lane >> 5;    // which 16-k half of an MFMA operand this lane feeds
     const int r32 = lane & 31;  // operand row inside a 32-row block
 
-    // Raw (still packed / int8) fragments of one 64-k step, as read from LDS.
+    // Raw (still packed / int8 / fp8) fragments of one 64-k step, as read
+    // from LDS: 16 bytes of a 4-bit row, 32 bytes of a byte-wide row.
     constexpr int AV = (VAR == I4I4) ? 1 : 2;  // 16-byte vectors per A block row
+    constexpr int BV = (VAR == FP8) ? 2 : 1;   // 16-byte vectors per B block row
     struct Frags {
-        i32x4 b[FN];
+        i32x4 b[FN][BV];
         i32x4 a[FM][AV];
     };
     auto read_frags = [&](int slot, int step, Frags &f) {
@@ -183,7 +185,11 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int row = (wn * FN + fn) * 32 + r32;
-            f.b[fn] = *reinterpret_cast<const i32x4 *>(sb + 16 * lds_chunk<CPR_B>(row, 2 * step + h));
+#pragma unroll
+            for (int v = 0; v < BV; ++v) {
+                const int col = (VAR == FP8) ? 4 * step + 2 * h + v : 2 * step + h;
+                f.b[fn][v] = *reinterpret_cast<const i32x4 *>(sb + 16 * lds_chunk<CPR_B>(row, col));
+            }
         }
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
@@ -196,26 +202,38 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
         }
     };
 
-    i32x16 acc[FN][FM];
-    // Unpack and contract one 64-k step: per block two 32x32x32 MFMAs.
+    // Integer accumulators for the int4 / int8 formats, fp32 for fp8.
+    using Acc = typename std::conditional<VAR == FP8, f32x16, i32x16>::type;
+    Acc acc[FN][FM];
+    // Unpack and contract one 64-k step: per block two 32x32x32 int8 MFMAs,
+    // or one 32x32x64 fp8 MFMA (lane l: 32 consecutive k, 32 (l / 32) onward).
     auto compute = [&](const Frags &f) {
-        i32x4 a_lo[FM], a_hi[FM];
+        if constexpr (VAR == FP8) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            i32x4 b_lo, b_hi;
-            unpack_chunk<VAR == W4A8>(f.b[fn], b_lo, b_hi);
+            for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                if (fn == 0) {
-                    if (VAR == I4I4) {
-                        unpack_chunk<false>(f.a[fm][0], a_lo[fm], a_hi[fm]);
-                    } else {
-                        a_lo[fm] = f.a[fm][0];
-                        a_hi[fm] = f.a[fm][AV - 1];
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[fn][fm] = mfma_32x32x64_fp8(f.b[fn][0], f.b[fn][BV - 1], f.a[fm][0],
+                                                    f.a[fm][AV - 1], acc[fn][fm]);
+        } else {
+            i32x4 a_lo[FM], a_hi[FM];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                i32x4 b_lo, b_hi;
+                unpack_chunk<VAR == W4A8>(f.b[fn][0], b_lo, b_hi);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    if (fn == 0) {
+                        if (VAR == I4I4) {
+                            unpack_chunk<false>(f.a[fm][0], a_lo[fm], a_hi[fm]);
+                        } else {
+                            a_lo[fm] = f.a[fm][0];
+                            a_hi[fm] = f.a[fm][AV - 1];
+                        }
                     }
+                    acc[fn][fm] = mfma_32x32x32(b_lo, a_lo[fm], acc[fn][fm]);
+                    acc[fn][fm] = mfma_32x32x32(b_hi, a_hi[fm], acc[fn][fm]);
                 }
-                acc[fn][fm] = mfma_32x32x32(b_lo, a_lo[fm], acc[fn][fm]);
-                acc[fn][fm] = mfma_32x32x32(b_hi, a_hi[fm], acc[fn][fm]);
             }
         }
     };
@@ -254,7 +272,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int j = 0; j < FM; ++j) acc[i][j] = i32x16{};
+            for (int j = 0; j < FM; ++j) acc[i][j] = Acc{};
         Frags cur, nxt;
         read_frags(0, 0, cur);
 
@@ -316,10 +334,16 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
 #pragma unroll
                     for (int rg = 0; rg < 4; ++rg) {
                         const int n = tn0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h;
-                        const i32x4 c = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
-                                              acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
-                                        Cfg::SHIFT;
-                        store_row4<OUT>(epi, m, N, n, c, sa[fm], sb[fn][rg]);
+                        if constexpr (VAR == FP8) {
+                            const float c[4] = {acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
+                                                acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]};
+                            store_row4f<OUT>(epi, m, N, n, c);
+                        } else {
+                            const i32x4 c = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
+                                                  acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
+                                            Cfg::SHIFT;
+                            store_row4<OUT>(epi, m, N, n, c, sa[fm], sb[fn][rg]);
+                        }
                     }
                 }
         };

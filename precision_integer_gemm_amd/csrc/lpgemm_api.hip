@@ -61,6 +61,11 @@ using I4Small = TiledKernel<I4I4, 2, 2, 2, 2, 128, 3>;
 using W8Small = TiledKernel<W4A8, 2, 2, 2, 2, 128, 3>;
 using I4Tiny = TiledKernel<I4I4, 1, 1, 2, 2, 256, 2>;
 using W8Tiny = TiledKernel<W4A8, 1, 1, 2, 2, 256, 2>;
+// fp8 (e4m3): one byte per element on both operands, the W4A8 kernel's A side
+// for both; 128 k per LDS stage.
+using F8Large = TiledKernel<FP8, 4, 2, 2, 4, 128, 2>;
+using F8Small = TiledKernel<FP8, 2, 2, 2, 2, 128, 3>;
+using F8Tiny = TiledKernel<FP8, 1, 1, 2, 2, 128, 2>;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 // FP6 path (gemm_fp6.hpp): 256 x 256 tiles, 8 waves of 128 (m) x 64 (n), two
@@ -413,6 +418,62 @@ lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, voi
     }
 }
 
+// fp8 (e4m3) product: its own argument rules (no packing, any K), the tiled
+// kernel when the operands allow 16-byte staging, else the general kernel.
+template <int OUT>
+lpgemm_status launch_fp8(const uint8_t *A, const uint8_t *B, void *C, int64_t M, int64_t N,
+                         int64_t K, hipStream_t stream)
+{
+    const Epilogue epi{C, nullptr, nullptr};
+    const uintptr_t c_align = OUT == OUT_F32 ? 16u : 4u;
+    const bool fast = K > 0 && K % 16 == 0 && aligned16(A) && aligned16(B) &&
+                      (reinterpret_cast<uintptr_t>(C) & (c_align - 1)) == 0;
+    const int forced = g_override.load(std::memory_order_relaxed);
+    if (forced == LPGEMM_KERNEL_SKINNY || forced == LPGEMM_KERNEL_FP6) return LPGEMM_ERR_UNSUPPORTED;
+    const bool tiled_forced = forced == LPGEMM_KERNEL_TILED || forced == LPGEMM_KERNEL_TILED_128 ||
+                              forced == LPGEMM_KERNEL_TILED_256 || forced == LPGEMM_KERNEL_TILED_64;
+    if (tiled_forced && !fast) return LPGEMM_ERR_UNSUPPORTED;
+    if (!fast || forced == LPGEMM_KERNEL_GENERAL) {
+        if (ceil_div(M, 16) > 65535 || ceil_div(N, 16) > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+        const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16));
+        hipLaunchKernelGGL(gemm_fp8_general_kernel<OUT>, grid, dim3(256), 0, stream, A, B, epi, M, N, K);
+        return launched();
+    }
+    const int cu = device_cu_count();
+    Plan p;
+    const int64_t large_tiles = ceil_div(M, 256) * ceil_div(N, 256);
+    const int64_t small_tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    p.tile = forced == LPGEMM_KERNEL_TILED_256   ? 256
+             : forced == LPGEMM_KERNEL_TILED_128 ? 128
+             : forced == LPGEMM_KERNEL_TILED_64  ? 64
+             : large_tiles * 4 >= (int64_t)cu * 3 ? 256
+             : small_tiles * 2 >= (int64_t)cu     ? 128
+                                                  : 64;
+    p.tiles_m = (int)ceil_div(M, p.tile);
+    p.tiles_n = (int)ceil_div(N, p.tile);
+    p.workgroups = (int64_t)p.tiles_m * p.tiles_n;
+    if (p.workgroups > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+    if (p.tile == 256) p.workgroups = std::min<int64_t>(p.workgroups, cu);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    return p.tile == 256 ? launch_tiled<F8Large, OUT>(p, A, B, epi, m, n, k, stream)
+           : p.tile == 128 ? launch_tiled<F8Small, OUT>(p, A, B, epi, m, n, k, stream)
+                           : launch_tiled<F8Tiny, OUT>(p, A, B, epi, m, n, k, stream);
+}
+
+lpgemm_status run_fp8(const uint8_t *A, const uint8_t *B, void *C, lpgemm_out_dtype out_dtype,
+                      int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    if (M < 0 || N < 0 || K < 0) return LPGEMM_ERR_INVALID_ARG;
+    if (out_dtype != LPGEMM_OUT_F32 && out_dtype != LPGEMM_OUT_FP8_E4M3) return LPGEMM_ERR_INVALID_ARG;
+    if (K > LPGEMM_MAX_K) return LPGEMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return LPGEMM_OK;
+    if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return LPGEMM_ERR_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    return out_dtype == LPGEMM_OUT_F32 ? launch_fp8<OUT_F32>(A, B, C, M, N, K, stream)
+                                       : launch_fp8<OUT_E4M3>(A, B, C, M, N, K, stream);
+}
+
 // lpgemm_out_dtype -> OutFormat; -1 for an unknown value.
 int out_format_of(lpgemm_out_dtype d)
 {
@@ -420,6 +481,7 @@ int out_format_of(lpgemm_out_dtype d)
     case LPGEMM_OUT_F32: return OUT_F32;
     case LPGEMM_OUT_BF16: return OUT_BF16;
     case LPGEMM_OUT_F16: return OUT_F16;
+    case LPGEMM_OUT_FP8_E4M3: return -1;  // fp8 entry point only
     }
     return -1;
 }
@@ -478,6 +540,13 @@ lpgemm_status lpgemm_w4a8_scaled(const int8_t *A, const uint8_t *B_packed, const
     const int f = out_format_of(out_dtype);
     if (f < 0) return LPGEMM_ERR_INVALID_ARG;
     return run_gemm(LPGEMM_VARIANT_W4A8, A, B_packed, D, scale_a, scale_b, f, M, N, K, stream);
+}
+
+lpgemm_status lpgemm_fp8_e4m3(const uint8_t *A, const uint8_t *B, void *C,
+                              lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                              hipStream_t stream)
+{
+    return run_fp8(A, B, C, out_dtype, M, N, K, stream);
 }
 
 lpgemm_status lpgemm_pack_int4(const int8_t *logical, uint8_t *packed, int64_t rows, int64_t K,

@@ -1,0 +1,233 @@
+"""fp8 (e4m3) GEMM on the GPU against the oracle (needs an MI355X).
+
+Two kinds of comparison:
+  * exact: operands whose values are small integers (and sums of identical
+    terms) have exactly representable partial sums in any order and at any
+    internal precision down to 13 bits, so the GPU must return the oracle's
+    exact sum bit for bit, and its e4m3 rounding;
+  * bounded: full-range random operands.  The one-thread-per-element kernel
+    adds exact products in binary32 in k order: within K * 2^-24 * sum|a b|
+    of the exact sum (the recursive-summation bound, +1% for the second-order
+    term).  The matrix-core kernel's v_mfma_scale_f32_32x32x64_f8f6f4 does not
+    add the 64 products of one instruction in IEEE binary32: small products
+    next to a large one lose low-order bits (measured: of 63 products of 1 next
+    to one of 448 * 448, 56 arrive).  Its error bound is not published; the
+    measured worst case over random sums is 1.03e-4 * sum|a b| (K = 16), and
+    the tests allow 2^-12 * sum|a b| (2.4e-4) on top of the binary32 bound.
+An e4m3 result must be the rounding of some value in the allowed interval
+(e4m3 rounding is monotone: between the codes of the interval's ends).  C sits
+between guard bands pre-filled with a sentinel.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import precision_integer_gemm_amd as L
+from precision_integer_gemm_amd.inputs import random_bytes
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 1024
+U = 2.0 ** -24
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    L.lib()
+    return t
+
+
+@pytest.fixture(autouse=True)
+def _auto_kernel():
+    yield
+    L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
+
+
+def codes(stream, rows, K):
+    """Seeded finite e4m3 codes (the NaN codes S.1111.111 replaced)."""
+    c = random_bytes(stream, rows * K)
+    c = np.where((c & 0x7F) == 0x7F, c & 0xF8, c).astype(np.uint8)
+    return c.reshape(rows, K)
+
+
+def run_gpu(torch, A, B, M, N, K, fp8_out, kernel=L.KERNEL_AUTO, c_offset=0):
+    dev = torch.device("cuda:0")
+    a_t = torch.from_numpy(np.ascontiguousarray(A).reshape(-1)).to(dev)
+    b_t = torch.from_numpy(np.ascontiguousarray(B).reshape(-1)).to(dev)
+    if fp8_out:
+        cbuf = torch.full((M * N + 2 * GUARD + c_offset,), 0x5A, dtype=torch.uint8, device=dev)
+        c_t = cbuf[GUARD + c_offset:GUARD + c_offset + M * N]
+    else:
+        cbuf = torch.full((M * N + 2 * GUARD,), 0x7EADBEEF, dtype=torch.int32, device=dev)
+        c_t = cbuf[GUARD:GUARD + M * N]
+    L.lpgemm_set_kernel_override(kernel)
+    st = L.lib().lpgemm_fp8_e4m3(a_t.data_ptr(), b_t.data_ptr(), c_t.data_ptr(),
+                                 L.OUT_FP8_E4M3 if fp8_out else L.OUT_F32, M, N, K,
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == L.OK, L.lpgemm_status_string(st)
+    torch.cuda.synchronize()
+    host = cbuf.cpu().numpy()
+    lo, hi = GUARD + c_offset, GUARD + c_offset + M * N
+    sentinel = 0x5A if fp8_out else 0x7EADBEEF
+    assert (host[:lo] == sentinel).all(), "write before C"
+    assert (host[hi:] == sentinel).all(), "write after C"
+    out = host[lo:hi].reshape(M, N)
+    return out if fp8_out else out.view(np.float32).astype(np.float64)
+
+
+MFMA_REL = 2.0 ** -12
+
+
+def tolerance(C, Cabs, K, mfma):
+    return 1.01 * K * U * Cabs + (MFMA_REL * Cabs if mfma else 0.0)
+
+
+def check_f32(got, C, Cabs, K, mfma=True):
+    tol = tolerance(C, Cabs, K, mfma)
+    bad = np.argwhere(~(np.abs(got - C) <= tol))
+    assert bad.size == 0, f"{len(bad)} outside the bound, first {bad[:3].tolist()}: " \
+                          f"{got[tuple(bad[0])]} vs {C[tuple(bad[0])]} (tol {tol[tuple(bad[0])]})"
+
+
+def check_e4m3(got, C, Cabs, K, mfma=True):
+    tol = tolerance(C, Cabs, K, mfma)
+    lo = oracle.fp8_e4m3_decode(oracle.fp8_e4m3_encode(C - tol))
+    hi = oracle.fp8_e4m3_decode(oracle.fp8_e4m3_encode(C + tol))
+    v = oracle.fp8_e4m3_decode(got)
+    bad = np.argwhere(~((v >= lo) & (v <= hi)))
+    assert bad.size == 0, f"{len(bad)} codes outside the rounding interval, first {bad[:3].tolist()}"
+
+
+SHAPES = [(1, 1, 16), (17, 33, 48), (37, 53, 96), (129, 255, 512), (300, 260, 1056),
+          (256, 256, 256), (513, 257, 2064), (64, 700, 4096)]
+RAGGED = [(1, 1, 1), (3, 5, 7), (17, 33, 50), (40, 30, 333)]
+
+
+@pytest.mark.parametrize("fp8_out", [False, True], ids=["f32", "e4m3"])
+@pytest.mark.parametrize("tile", [L.KERNEL_TILED_64, L.KERNEL_TILED_128, L.KERNEL_TILED_256],
+                         ids=["t64", "t128", "t256"])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_tiled(torch, M, N, K, tile, fp8_out):
+    say(f"fp8 tiled {tile} {M}x{N}x{K} e4m3-out={fp8_out}")
+    A, B = codes(M * 3 + K, M, K), codes(N * 5 + K + 1, N, K)
+    C, Cabs = oracle.gemm_fp8(A, B, M, N, K)
+    got = run_gpu(torch, A, B, M, N, K, fp8_out, kernel=tile)
+    (check_e4m3 if fp8_out else check_f32)(got, C, Cabs, K)
+
+
+@pytest.mark.parametrize("fp8_out", [False, True], ids=["f32", "e4m3"])
+@pytest.mark.parametrize("M,N,K", RAGGED + SHAPES[:4])
+def test_general(torch, M, N, K, fp8_out):
+    say(f"fp8 general {M}x{N}x{K} e4m3-out={fp8_out}")
+    A, B = codes(M + 7 * K, M, K), codes(N + 11 * K, N, K)
+    C, Cabs = oracle.gemm_fp8(A, B, M, N, K)
+    got = run_gpu(torch, A, B, M, N, K, fp8_out, kernel=L.KERNEL_GENERAL)
+    (check_e4m3 if fp8_out else check_f32)(got, C, Cabs, K, mfma=False)
+
+
+def integer_codes(stream, rows, K):
+    """Seeded e4m3 codes of the integers -8 .. 8."""
+    v = (random_bytes(stream, rows * K) % 17).astype(np.float64) - 8.0
+    return oracle.fp8_e4m3_encode(v).reshape(rows, K)
+
+
+@pytest.mark.parametrize("kernel", [L.KERNEL_TILED_64, L.KERNEL_TILED_128, L.KERNEL_TILED_256,
+                                    L.KERNEL_GENERAL], ids=["t64", "t128", "t256", "general"])
+@pytest.mark.parametrize("M,N,K", [(37, 53, 96), (300, 260, 1056), (513, 257, 2064), (64, 100, 8192)])
+def test_integer_operands_are_exact(torch, M, N, K, kernel):
+    # |partial sums| <= 64 K: exact in binary32 and at any internal alignment
+    say(f"fp8 integer operands {kernel} {M}x{N}x{K}")
+    A, B = integer_codes(M + K, M, K), integer_codes(N + 3 * K, N, K)
+    C, _ = oracle.gemm_fp8(A, B, M, N, K)
+    assert np.array_equal(run_gpu(torch, A, B, M, N, K, False, kernel=kernel), C)
+    assert np.array_equal(run_gpu(torch, A, B, M, N, K, True, kernel=kernel), oracle.fp8_e4m3_encode(C))
+
+
+def test_unaligned_output_takes_the_general_kernel(torch):
+    M, N, K = 33, 40, 64
+    say("fp8 unaligned C")
+    A, B = codes(1, M, K), codes(2, N, K)
+    C, Cabs = oracle.gemm_fp8(A, B, M, N, K)
+    check_e4m3(run_gpu(torch, A, B, M, N, K, True, c_offset=1), C, Cabs, K)
+
+
+@pytest.mark.parametrize("kernel", [L.KERNEL_AUTO, L.KERNEL_GENERAL], ids=["auto", "general"])
+def test_closed_forms_are_exact(torch, kernel):
+    # identical terms: every partial sum is exact in fp32, whatever the order
+    M, N, K = 96, 80, 4096
+    say(f"fp8 closed forms kernel {kernel}")
+    ones = np.full((M, K), 0x38, np.uint8)                 # 1.0
+    got = run_gpu(torch, ones, ones[:N], M, N, K, False, kernel=kernel)
+    assert (got == K).all()
+    big, nbig = np.full((M, K), 0x7E, np.uint8), np.full((N, K), 0xFE, np.uint8)   # 448, -448
+    got = run_gpu(torch, big, nbig, M, N, K, False, kernel=kernel)
+    assert (got == -200704.0 * K).all()
+    # e4m3 output saturates: |C| far above 448
+    got8 = run_gpu(torch, big, nbig, M, N, K, True, kernel=kernel)
+    assert (got8 == 0xFE).all()
+    # small values stay exact and round-trip through e4m3: K * 2^-9 * 2^-9 = 2^-6 at K = 4096
+    tiny = np.full((M, K), 0x01, np.uint8)                 # 2^-9
+    got8 = run_gpu(torch, tiny, tiny[:N], M, N, K, True, kernel=kernel)
+    assert (got8 == 0x08).all()                            # 2^-6
+
+
+def test_k_zero_and_empty(torch):
+    say("fp8 k0")
+    A, B = np.zeros((5, 0), np.uint8), np.zeros((7, 0), np.uint8)
+    assert not run_gpu(torch, A, B, 5, 7, 0, False).any()
+    assert not run_gpu(torch, A, B, 5, 7, 0, True).any()
+    dev = torch.device("cuda:0")
+    C = torch.zeros((0, 9), dtype=torch.float32, device=dev)
+    assert L.lpgemm_fp8_e4m3(torch.zeros((0, 16), dtype=torch.uint8, device=dev),
+                             torch.zeros((9, 16), dtype=torch.uint8, device=dev), out=C).shape == (0, 9)
+
+
+def test_argument_errors(torch):
+    dev = torch.device("cuda:0")
+    buf = torch.zeros(64, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    fn = L.lib().lpgemm_fp8_e4m3
+    p = buf.data_ptr()
+    assert fn(p, p, p, L.OUT_BF16, 1, 1, 16, s) == L.ERR_INVALID_ARG
+    assert fn(p, p, p, 7, 1, 1, 16, s) == L.ERR_INVALID_ARG
+    assert fn(p, p, p, L.OUT_F32, -1, 1, 16, s) == L.ERR_INVALID_ARG
+    assert fn(p, p, None, L.OUT_F32, 1, 1, 16, s) == L.ERR_INVALID_ARG
+    assert fn(p, p, p, L.OUT_F32, 1, 1, L.MAX_K + 1, s) == L.ERR_UNSUPPORTED
+    L.lpgemm_set_kernel_override(L.KERNEL_SKINNY)
+    assert fn(p, p, p, L.OUT_F32, 1, 1, 16, s) == L.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fp8_out", [False, True], ids=["f32", "e4m3"])
+def test_full_size_parity(torch, fp8_out):
+    # 2048 x 2048 x 4096 in the automatic launch (256-tiles), every element
+    M, N, K = 2048, 2048, 4096
+    say(f"fp8 {M}x{N}x{K} plan auto, e4m3-out={fp8_out}")
+    A, B = codes(31, M, K), codes(37, N, K)
+    C, Cabs = oracle.gemm_fp8(A, B, M, N, K)
+    got = run_gpu(torch, A, B, M, N, K, fp8_out)
+    (check_e4m3 if fp8_out else check_f32)(got, C, Cabs, K)
+
+
+def test_tensor_wrapper(torch):
+    say("fp8 tensor wrapper")
+    dev = torch.device("cuda:0")
+    M, N, K = 40, 72, 256
+    A, B = codes(5, M, K), codes(6, N, K)
+    C, Cabs = oracle.gemm_fp8(A, B, M, N, K)
+    a = torch.from_numpy(A).to(dev).view(torch.float8_e4m3fn)
+    b = torch.from_numpy(B).to(dev).view(torch.float8_e4m3fn)
+    c32 = L.lpgemm_fp8_e4m3(a, b)
+    c8 = L.lpgemm_fp8_e4m3(a, b, dtype=torch.float8_e4m3fn)
+    torch.cuda.synchronize()
+    check_f32(c32.cpu().numpy().astype(np.float64), C, Cabs, K)
+    check_e4m3(c8.view(torch.uint8).cpu().numpy(), C, Cabs, K)
