@@ -19,7 +19,9 @@ decode-shape B rotated over copies larger than the MALL together), free of the
 write-back a previous workload leaves behind; `per_config_cold` times each
 workload after a 512 MiB read that evicts its operands from L2 and MALL;
 `per_config_scaled_bf16` times the scaled product (per-row and per-column
-scales, bf16 output) of each workload alone.
+scales, bf16 output) of each workload alone; `per_config_fp8` times the second
+workload, the fp8 (e4m3) GEMM with fp32 output, at 4096^3 and 8192^3 (outside
+the step and `value`).
 
 The CPU baseline times the oracle (plain C, OpenMP over rows) on the first
 rows of every workload, and those rows double as a bit-exact parity check of
@@ -40,11 +42,12 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# MI355X published peaks (dense): int8 MFMA 5.0 POP/s, FP6 MFMA 10.1 PFLOP/s,
-# HBM3E 8 TB/s.  A workload is priced at the peak of the matrix-core format its
+# MI355X published peaks (dense): int8 MFMA 5.0 POP/s, fp8 5.0 PFLOP/s, FP6
+# 10.1 PFLOP/s, HBM3E 8 TB/s.  A workload is priced at the peak of the matrix-core format its
 # kernel computes in: int4 x int4 calls that run on the FP6 path at the FP6
 # peak, everything else at the int8 peak.
 PEAK_INT8_TOPS = 5000.0
+PEAK_FP8_TOPS = 5000.0
 PEAK_FP6_TOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
 
@@ -325,6 +328,37 @@ def main() -> int:
                               "roofline_frac": round(max(t_mfma, t_hbm) / (med * 1e-6), 4)}
             del copies, D
 
+    # The second workload, the fp8 (e4m3) GEMM with fp32 accumulation and
+    # fp32 output, alone (not part of the step or of `value`): priced at the
+    # 5.0 PFLOP/s dense fp8 peak.
+    fp8 = {}
+    if args.isolated_reps > 0:
+        from precision_integer_gemm_amd.inputs import fp8_codes
+        for (fm, fn_, fk) in ((4096, 4096, 4096), (8192, 8192, 8192)):
+            a8 = torch.from_numpy(fp8_codes(fm + fk, 0, fm, fk)).to(dev)
+            b8 = torch.from_numpy(fp8_codes(fm + fk, 1, fn_, fk)).to(dev)
+            c8 = torch.empty((fm, fn_), dtype=torch.float32, device=dev)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.isolated_reps)]
+            for j in range(-1, args.isolated_reps):
+                if j >= 0:
+                    evs[j][0].record(stream)
+                st = L.lib().lpgemm_fp8_e4m3(a8.data_ptr(), b8.data_ptr(), c8.data_ptr(), L.OUT_F32,
+                                             fm, fn_, fk, handle)
+                if j >= 0:
+                    evs[j][1].record(stream)
+                if st != L.OK:
+                    raise RuntimeError(f"fp8 {fm}x{fn_}x{fk}: {L.lpgemm_status_string(st)}")
+            torch.cuda.synchronize()
+            us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+            med = float(np.median(us))
+            tops = 2.0 * fm * fn_ * fk / (med * 1e-6) / 1e12
+            fp8[f"fp8_e4m3_{fm}x{fn_}x{fk}"] = {
+                "out": "f32", "median_us": round(med, 3), "min_us": round(float(us.min()), 3),
+                "tops": round(tops, 2), "bound": "mfma", "mfma_peak_tops": PEAK_FP8_TOPS,
+                "roofline_frac": round(tops / PEAK_FP8_TOPS, 4)}
+            del a8, b8, c8
+
     # Each workload cold: before every timed launch a 512 MiB buffer is read
     # (not timed), which evicts its operands from the L2s and the 256 MB MALL
     # with clean lines (a write would leave 512 MB of write-back competing
@@ -390,6 +424,7 @@ def main() -> int:
         "per_config_isolated": isolated,
         "per_config_cold": cold,
         "per_config_scaled_bf16": scaled,
+        "per_config_fp8": fp8,
     }
 
     if not args.no_cpu:

@@ -125,3 +125,12 @@ def scale_vector(seed: int, which: int, n: int, lo_exp: int = -12, hi_exp: int =
     mant = (words & np.uint64(0x7FFFFF)).astype(np.uint32)
     bits = (sign << np.uint32(31)) | (biased << np.uint32(23)) | mant
     return bits.view(np.float32)
+
+
+def fp8_codes(seed: int, which: int, rows: int, K: int) -> np.ndarray:
+    """Uniform random e4m3 bytes [rows, K] for the fp8 workload (which = 0: A,
+    1: B), drawn from stream (seed << 8) | which; the two NaN codes
+    (S.1111.111) are replaced by the code with the same sign and exponent and
+    mantissa 0, so every operand is finite."""
+    c = random_bytes(operand_stream(seed, which), rows * K)
+    return np.where((c & 0x7F) == 0x7F, c & 0xF8, c).astype(np.uint8).reshape(rows, K)
