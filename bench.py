@@ -21,13 +21,17 @@ workload after a 512 MiB read that evicts its operands from L2 and MALL;
 `per_config_scaled_bf16` times the scaled product (per-row and per-column
 scales, bf16 output) of each workload alone; `per_config_fp8` times the second
 workload, the fp8 (e4m3) GEMM with fp32 output, at 4096^3 and 8192^3 (outside
-the step and `value`).
+the step and `value`).  `ceiling` holds what the chip sustains, measured
+live by the probe kernels of _ceiling.so (matrix cores only, per format; LDS
+reads; the FP6 GEMM's inner loop without global memory), and `roofline`
+adds the dominant call's fraction of the sustained ceiling of its format.
 
 The CPU baseline times the oracle (plain C, OpenMP over rows) on the first
 rows of every workload, and those rows double as a bit-exact parity check of
 the GPU output.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--case NAME] [--no-cpu]
+    python bench.py --ceiling      # the sustained-ceiling probes alone
 """
 from __future__ import annotations
 
@@ -63,6 +67,55 @@ KERNEL_SYMBOL = {"tiled": "gemm_pipelined_kernel", "skinny": "gemm_w4a8_skinny_k
 
 def mfma_peak(kernel: str) -> float:
     return PEAK_FP6_TOPS if kernel == "fp6" else PEAK_INT8_TOPS
+
+
+# Sustained ceilings, measured live by the probe kernels of _ceiling.so
+# (csrc/ceiling_probe.hip): one workgroup per compute unit keeps the matrix
+# cores (or the LDS) busy for a few milliseconds, long enough for the clock to
+# settle at what the chip holds under that load.  A GEMM's `sustained_frac`
+# sets its throughput against the ceiling of the matrix-core format it runs on.
+PROBES = [("fp6_mfma", 0, 24000), ("int8_mfma", 1, 24000), ("fp8_mfma", 2, 12000),
+          ("lds_read", 3, 40000), ("fp6_gemm_inner_loop", 4, 12000)]
+
+
+def sustained_ceilings(torch, dev, stream, reps: int = 3) -> dict:
+    import ctypes
+
+    path = os.path.join(ROOT, "precision_integer_gemm_amd", "_ceiling.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    lib.ceiling_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_void_p]
+    lib.ceiling_probe_run.restype = ctypes.c_int
+    lib.ceiling_probe_work.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.ceiling_probe_work.restype = ctypes.c_double
+    lib.ceiling_probe_out_floats.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.ceiling_probe_out_floats.restype = ctypes.c_int64
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    n_out = max(lib.ceiling_probe_out_floats(k, blocks) for _, k, _ in PROBES)
+    out = torch.empty(n_out, dtype=torch.float32, device=dev)
+    res = {"compute_units": blocks}
+    for name, kind, iters in PROBES:
+        ms = []
+        for r in range(reps + 1):  # the first launch is a warm-up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = lib.ceiling_probe_run(kind, blocks, iters, out.data_ptr(), n_out, stream.cuda_stream)
+            e1.record(stream)
+            if st != 0:
+                raise RuntimeError(f"ceiling probe {name}: status {st}")
+            torch.cuda.synchronize()
+            if r:
+                ms.append(e0.elapsed_time(e1))
+        t = float(np.median(ms)) * 1e-3
+        work = lib.ceiling_probe_work(kind, blocks, iters)
+        if name == "lds_read":
+            res[name] = {"tb_s": round(work / t / 1e12, 2),
+                         "gb_s_per_cu": round(work / t / 1e9 / blocks, 1), "ms": round(t * 1e3, 3)}
+        else:
+            res[name] = {"tops": round(work / t / 1e12, 1), "ms": round(t * 1e3, 3)}
+    return res
 
 
 # HBM traffic of the dominant call, from two rocprofv3 --pmc runs (FETCH_SIZE,
@@ -114,6 +167,9 @@ def parse():
                     help="launches per workload, each after a 512 MiB read that evicts L2 and MALL")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="run only the sustained-ceiling probes and print their JSON")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the sustained-ceiling probes")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="summarise a rocprofv3 kernel_trace.csv per kernel and grid (no GPU use)")
     return ap.parse_args()
@@ -175,6 +231,10 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return 0
+
+    if args.ceiling:
+        print(json.dumps({"ceiling": sustained_ceilings(torch, dev, torch.cuda.current_stream())}))
         return 0
 
     names = [n for n in STEP_ORDER if args.case is None or n in args.case]
@@ -387,6 +447,8 @@ def main() -> int:
                             "bound": bound, "roofline_frac": round(t_roof / (med * 1e-6), 4)}
         del flush
 
+    ceiling = None if args.no_ceiling else sustained_ceilings(torch, dev, stream)
+
     _, dc, drec, davg = dominant
     if drec["bound"] == "mfma":
         achieved = dc.ops / (davg * 1e-6) / 1e12
@@ -394,6 +456,10 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TOP/s", "frac": round(achieved / peak, 4),
                 "int8_peak_frac": round(achieved / PEAK_INT8_TOPS, 4)}
+        if ceiling is not None:
+            sus = ceiling["fp6_mfma" if drec["kernel"] == "fp6" else "int8_mfma"]["tops"]
+            roof["sustained_peak"] = sus
+            roof["sustained_frac"] = round(achieved / sus, 4)
     else:
         achieved = dc.alg_bytes / (davg * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -425,6 +491,7 @@ def main() -> int:
         "per_config_cold": cold,
         "per_config_scaled_bf16": scaled,
         "per_config_fp8": fp8,
+        "ceiling": ceiling,
     }
 
     if not args.no_cpu:

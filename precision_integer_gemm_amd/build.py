@@ -3,7 +3,8 @@
     python -m precision_integer_gemm_amd.build
 
 compiles csrc/lpgemm_api.hip (which includes every kernel) with hipcc into
-precision_integer_gemm_amd/_lpgemm.so, next to this file.
+precision_integer_gemm_amd/_lpgemm.so, next to this file, and the measurement
+probe csrc/ceiling_probe.hip into _ceiling.so (loaded only by bench.py).
 """
 from __future__ import annotations
 
@@ -16,6 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "lpgemm_api.hip")
 LIB = os.path.join(PKG, "_lpgemm.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "ceiling_probe.hip")
+PROBE_LIB = os.path.join(PKG, "_ceiling.so")
 ARCH = "gfx950"
 
 
@@ -26,7 +29,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library needs ROCm's hipcc")
 
 
-def command(out: str) -> list[str]:
+def command(out: str, src: str = SRC) -> list[str]:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         # packed fp32 VALU forms are kept out of the generated code
@@ -35,20 +38,25 @@ def command(out: str) -> list[str]:
         # contraction of a multiply into a fused operation
         "-ffp-contract=off",
         "-Wall", "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-        "-o", out, SRC,
+        "-o", out, src,
     ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    proc = subprocess.run(command(tmp), capture_output=True, text=True)
+def compile_one(src: str, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
+    proc = subprocess.run(command(tmp, src), capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = [l for l in (proc.stdout + proc.stderr).splitlines() if noise not in l]
     if proc.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    compile_one(SRC, LIB, verbose)
+    compile_one(PROBE_SRC, PROBE_LIB, verbose)
     return LIB
 
 

@@ -1,0 +1,199 @@
+// ceiling_probe.hip -- what the matrix cores and the LDS sustain, measured.
+//
+// Measurement support beside the GEMM library (its own shared object,
+// _ceiling.so, loaded only by bench.py): each kernel keeps one unit of a
+// compute unit busy for a fixed number of iterations, so that a caller can
+// time it and set a GEMM's throughput against what the chip sustains under
+// that load, clock reduction included, next to the published peak.
+//
+// Every kernel requests 96 KB of (unused) dynamic LDS, so a compute unit holds
+// exactly one workgroup, and the grid is one workgroup per compute unit.
+//
+//   kind 0  FP6 (E3M2) v_mfma_scale_f32_32x32x64_f8f6f4, 4 waves (one per
+//           SIMD), 8 independent accumulators each: matrix cores only.
+//   kind 1  int8 v_mfma_i32_32x32x32_i8, same structure.
+//   kind 2  fp8 (E4M3) v_mfma_scale_f32_32x32x64_f8f6f4, same structure.
+//   kind 3  LDS reads only: 8 waves, ds_read_b128 + ds_read_b64 of
+//           lane-linear 1.5 KB fragments, folded into a register.
+//   kind 4  the FP6 GEMM's inner loop without global memory: 8 waves (two
+//           per SIMD) of 4 x 2 blocks of 32 x 32, per 64 k six 1.5 KB
+//           fragments read from LDS one step ahead and eight MFMAs.
+//
+// Work per launch (ceiling_probe_work): kinds 0-2 and 4 in operations
+// (2 x MACs), kind 3 in LDS bytes read.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kLdsRequest = 96 * 1024;
+constexpr int kFrag = 1536;
+constexpr int kChains = 8;
+
+// Operand registers: arbitrary nonzero bit patterns that differ per lane
+// (finite in every format used here: E3M2 has no specials, and the E4M3 mask
+// clears the lowest exponent bit so no code is a NaN).
+__device__ inline i32x8 operand(uint32_t seed, uint32_t mask)
+{
+    i32x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (int32_t)(((seed + 0x9E3779B9u * (i + 1)) * 2654435761u) & mask);
+    return v;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void mfma_loop(float *out, int iters)
+{
+    const uint32_t seed = threadIdx.x * 977u + blockIdx.x;
+    const uint32_t mask = KIND == 2 ? 0x77777777u : 0xFFFFFFFFu;
+    const i32x8 a = operand(seed, mask), b = operand(seed ^ 0x5555u, mask);
+    float s = 0.f;
+    if constexpr (KIND == 1) {
+        const i32x4 a4 = {a[0], a[1], a[2], a[3]}, b4 = {b[0], b[1], b[2], b[3]};
+        i32x16 acc[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) acc[c] = i32x16{};
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c)
+                acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a4, b4, acc[c], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) s += (float)acc[c][threadIdx.x & 15];
+    } else {
+        constexpr int fmt = KIND == 0 ? 3 : 0;  // E3M2 or E4M3 operands
+        f32x16 acc[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c)
+                acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], fmt, fmt, 0, 127,
+                                                                          0, 127);
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) s += acc[c][threadIdx.x & 15];
+    }
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// LDS image shared by kinds 3 and 4: four buffers of six fragments (36 KB),
+// rotated per step so no read is loop-invariant.
+constexpr int kFrags = 6, kBufs = 4;
+constexpr int kImage = kBufs * kFrags * kFrag;
+
+__device__ inline void fill_image(uint8_t *lds)
+{
+    for (int i = threadIdx.x * 4; i < kImage; i += blockDim.x * 4)
+        *reinterpret_cast<uint32_t *>(lds + i) = ((uint32_t)i * 2654435761u) & 0x7DF7DF7Du;
+    __syncthreads();
+}
+
+__device__ inline i32x8 frag_at(const uint8_t *lds, int buf, int f, int lane)
+{
+    const uint8_t *p = lds + (buf * kFrags + f) * kFrag;
+    const i32x4 lo = *reinterpret_cast<const i32x4 *>(p + 16 * lane);
+    const i32x2 hi = *reinterpret_cast<const i32x2 *>(p + 1024 + 8 * lane);
+    return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, 0, 0};
+}
+
+__global__ __launch_bounds__(512) void lds_loop(float *out, int iters)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    fill_image(lds);
+    const int lane = threadIdx.x & 63;
+    i32x8 x = {};
+    for (int it = 0; it < iters; ++it) {
+        const int buf = it & (kBufs - 1);
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) x ^= frag_at(lds, buf, f, lane);
+    }
+    out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(x[0] ^ x[3] ^ x[5]);
+}
+
+__global__ __launch_bounds__(512) void lds_mfma_loop(float *out, int iters)
+{
+    constexpr int FM = 4, FN = 2;
+    static_assert(FM + FN == kFrags, "one buffer holds one step's fragments");
+    extern __shared__ __align__(16) uint8_t lds[];
+    fill_image(lds);
+    const int lane = threadIdx.x & 63;
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
+    i32x8 cur[kFrags], nxt[kFrags];
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f) cur[f] = frag_at(lds, 0, f, lane);
+    for (int it = 0; it < iters; ++it) {
+        const int buf = (it + 1) & (kBufs - 1);
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) nxt[f] = frag_at(lds, buf, f, lane);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    cur[fn], cur[FN + fm], acc[fn][fm], 3, 3, 0, 127, 0, 127);
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) cur[f] = nxt[f];
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) s += acc[i][j][lane & 15];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+int threads_of(int kind) { return kind >= 3 ? 512 : 256; }
+
+}  // namespace
+
+// Work of one launch: operations (kinds 0-2, 4) or LDS bytes read (kind 3).
+extern "C" double ceiling_probe_work(int kind, int blocks, int iters)
+{
+    const double per_block_iter =
+        kind == 0 || kind == 2 ? 4.0 * kChains * 2 * 32 * 32 * 64      // 4 waves
+        : kind == 1            ? 4.0 * kChains * 2 * 32 * 32 * 32
+        : kind == 3            ? 8.0 * kFrags * kFrag                   // 8 waves
+        : kind == 4            ? 8.0 * 8 * 2 * 32 * 32 * 64
+                               : 0.0;
+    return per_block_iter * blocks * iters;
+}
+
+// Floats of `out` one launch writes (one per thread).
+extern "C" int64_t ceiling_probe_out_floats(int kind, int blocks)
+{
+    return (int64_t)blocks * threads_of(kind);
+}
+
+// Launch probe `kind` with `blocks` workgroups of `iters` iterations on
+// `stream`; `out` is device memory of ceiling_probe_out_floats(kind, blocks)
+// floats (`out_floats` says how many the caller has).  Returns 0, -1 for
+// bad arguments, or -2 if the launch failed.
+extern "C" int ceiling_probe_run(int kind, int blocks, int iters, float *out, int64_t out_floats,
+                                hipStream_t stream)
+{
+    if (kind < 0 || kind > 4 || blocks < 1 || iters < 1 || out == nullptr ||
+        out_floats < ceiling_probe_out_floats(kind, blocks))
+        return -1;
+    const void *fn = kind == 0   ? (const void *)mfma_loop<0>
+                     : kind == 1 ? (const void *)mfma_loop<1>
+                     : kind == 2 ? (const void *)mfma_loop<2>
+                     : kind == 3 ? (const void *)lds_loop
+                                 : (const void *)lds_mfma_loop;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsRequest) != hipSuccess)
+        return -2;
+    void *args[] = {&out, &iters};
+    if (hipLaunchKernel(fn, dim3((unsigned)blocks), dim3((unsigned)threads_of(kind)), args, kLdsRequest,
+                        stream) != hipSuccess)
+        return -2;
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}

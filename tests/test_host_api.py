@@ -211,3 +211,24 @@ def test_narrow_m_limits():
     assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 4096, 8192)["kernel"] == "skinny"
     assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 4096, 8224)["kernel"] == "tiled"   # K above 8192
     assert L.lpgemm_plan(L.VARIANT_W4A8, 17, 4096, 4096)["kernel"] == "tiled"   # M above 16
+
+
+def test_ceiling_probe_library_loads_and_checks_arguments():
+    # measurement support for bench.py: its own library, outside the GEMM's C ABI
+    probe = ctypes.CDLL(os.path.join(ROOT, "precision_integer_gemm_amd", "_ceiling.so"))
+    probe.ceiling_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p]
+    probe.ceiling_probe_work.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    probe.ceiling_probe_work.restype = ctypes.c_double
+    probe.ceiling_probe_out_floats.argtypes = [ctypes.c_int, ctypes.c_int]
+    probe.ceiling_probe_out_floats.restype = ctypes.c_int64
+    # 4 waves x 8 chains x one 32x32x64 MFMA (2 * 65536 ops) per iteration and workgroup
+    assert probe.ceiling_probe_work(0, 2, 3) == 2 * 3 * 4 * 8 * 2 * 32 * 32 * 64
+    assert probe.ceiling_probe_work(3, 1, 1) == 8 * 6 * 1536
+    assert probe.ceiling_probe_out_floats(0, 10) == 2560
+    assert probe.ceiling_probe_out_floats(4, 10) == 5120
+    # rejected before any HIP call: unknown kind, empty grid, no or short output
+    assert probe.ceiling_probe_run(5, 1, 1, 16, 1 << 20, None) == -1
+    assert probe.ceiling_probe_run(0, 0, 1, 16, 1 << 20, None) == -1
+    assert probe.ceiling_probe_run(0, 1, 1, None, 1 << 20, None) == -1
+    assert probe.ceiling_probe_run(0, 4, 1, 16, 1023, None) == -1
