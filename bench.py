@@ -126,8 +126,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3) -> dict:
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 329206.3, "fetch_scale": 2.0, "write_kib": 366956.8,
-                  "write_scale": 1.0, "sources_sha256": "76478899ced7bb25766286dcb19a25c2df7fd45afc3efc1db6e343a0d094b5be"},
+    "i4i4_8192": {"fetch_kib": 328086.3, "fetch_scale": 2.0, "write_kib": 361382.6,
+                  "write_scale": 1.0, "sources_sha256": "3e3dec5fb263cdcefd6e715c4c682fec95c6408d0b09da1eac4a02d584c638bc"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",

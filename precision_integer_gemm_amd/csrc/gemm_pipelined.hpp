@@ -13,7 +13,8 @@
 // and lanes whose chunk lies past K use an out-of-range offset, so tails are
 // zero-filled without branches.  All STAGES slots of an LDS ring are kept in
 // flight; one barrier per K tile, placed before the tile's last 64-k step so
-// the next tile's first fragment reads overlap that step's MFMAs.  Raw
+// the next tile's first fragment reads overlap that step's MFMAs, and the
+// copy that refills the freed slot goes out after those MFMAs.  Raw
 // fragments are double-buffered in registers one step ahead.  The loads are
 // invisible to the compiler, so the kernel issues its own vmcnt waits.
 //
@@ -278,8 +279,8 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
 
         // Steady state: every K tile but the last.  The tile's last step waits
         // for tile kt+1, passes the barrier (every wave is done reading tile
-        // kt), refills tile kt's slot with tile kt+STAGES and reads step 0 of
-        // tile kt+1.
+        // kt), reads step 0 of tile kt+1, issues its MFMAs and then refills
+        // tile kt's slot with tile kt+STAGES.
         for (int kt = 0; kt + 1 < ktiles; ++kt) {
             const int slot = kt % STAGES;
 #pragma unroll
@@ -289,10 +290,10 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
                 } else {
                     wait_tiles_after(STAGES - 2);
                     lds_barrier();
-                    issue_stage(kt + STAGES);
                     read_frags((kt + 1) % STAGES, 0, nxt);
                 }
                 compute(cur);
+                if (st + 1 == STEPS) issue_stage(kt + STAGES);
                 cur = nxt;
             }
         }

@@ -68,13 +68,13 @@ using F8Small = TiledKernel<FP8, 2, 2, 2, 2, 128, 3>;
 using F8Tiny = TiledKernel<FP8, 1, 1, 2, 2, 128, 2>;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
-// FP6 path (gemm_fp6.hpp): 256 x 256 tiles, 8 waves of 128 (m) x 64 (n), two
-// LDS stages of 128 k (96 KB).  Chosen automatically for int4 x int4 when the
+// FP6 path (gemm_fp6.hpp): 256 x 256 tiles, 8 waves of 128 (m) x 64 (n), three
+// LDS stages of 128 k (144 KB).  Chosen automatically for int4 x int4 when the
 // re-encoding pass pays for itself (measured against the int8 256-tile kernel,
 // interleaved): at least one 256-tile per compute unit and K >= 2048, with
 // either two tiles per compute unit or K >= 8192 (8192^2 x 2048: 6% faster,
 // 4096^2 x 16384: 8% faster; 4096^3 and 3000 x 5120 x 6144: 5-8% slower).
-constexpr int kFp6FM = 4, kFp6FN = 2, kFp6WM = 2, kFp6WN = 4, kFp6KS = 2, kFp6Stages = 2;
+constexpr int kFp6FM = 4, kFp6FN = 2, kFp6WM = 2, kFp6WN = 4, kFp6KS = 2, kFp6Stages = 3;
 using Fp6Tile = Fp6Cfg<kFp6FM, kFp6FN, kFp6WM, kFp6WN, kFp6KS, kFp6Stages>;
 constexpr int64_t kFp6MinK = 2048, kFp6LongK = 8192;
 
