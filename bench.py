@@ -78,7 +78,44 @@ PROBES = [("fp6_mfma", 0, 24000), ("int8_mfma", 1, 24000), ("fp8_mfma", 2, 12000
           ("lds_read", 3, 40000), ("fp6_gemm_inner_loop", 4, 12000)]
 
 
-def sustained_ceilings(torch, dev, stream, reps: int = 3) -> dict:
+# The HBM counterpart: one plain streaming read (16-byte non-temporal loads)
+# over a buffer of the decode shapes' packed weights (N * K / 2 bytes), rotated
+# over three copies like the isolated decode timing so that every pass reads
+# HBM rather than the 256 MB MALL; 16 workgroups of 256 threads per compute unit.
+STREAM_COPIES, STREAM_WG_PER_CU, STREAM_REPS = 3, 16, 21
+
+
+def stream_read_ceiling(torch, dev, stream, lib, nbytes: int, cus: int) -> dict:
+    import ctypes
+
+    lib.ceiling_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.ceiling_probe_stream_read.restype = ctypes.c_int
+    lib.ceiling_probe_stream_out_ints.argtypes = [ctypes.c_int]
+    lib.ceiling_probe_stream_out_ints.restype = ctypes.c_int64
+    blocks = STREAM_WG_PER_CU * cus
+    n_out = lib.ceiling_probe_stream_out_ints(blocks)
+    out = torch.empty(n_out, dtype=torch.int32, device=dev)
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(STREAM_COPIES)]
+    us = []
+    for r in range(STREAM_REPS + STREAM_COPIES):  # the first pass over each copy is a warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = lib.ceiling_probe_stream_read(bufs[r % STREAM_COPIES].data_ptr(), nbytes, blocks,
+                                           out.data_ptr(), n_out, stream.cuda_stream)
+        e1.record(stream)
+        if st != 0:
+            raise RuntimeError(f"stream-read probe: status {st}")
+        torch.cuda.synchronize()
+        if r >= STREAM_COPIES:
+            us.append(e0.elapsed_time(e1) * 1e3)
+    med = float(np.median(us))
+    del bufs
+    return {"bytes": nbytes, "median_us": round(med, 3), "min_us": round(float(np.min(us)), 3),
+            "gb_s": round(nbytes / (med * 1e-6) / 1e9, 1), "workgroups": blocks}
+
+
+def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0) -> dict:
     import ctypes
 
     path = os.path.join(ROOT, "precision_integer_gemm_amd", "_ceiling.so")
@@ -115,6 +152,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3) -> dict:
                          "gb_s_per_cu": round(work / t / 1e9 / blocks, 1), "ms": round(t * 1e3, 3)}
         else:
             res[name] = {"tops": round(work / t / 1e12, 1), "ms": round(t * 1e3, 3)}
+    if stream_bytes:
+        res["hbm_stream_read"] = stream_read_ceiling(torch, dev, stream, lib, stream_bytes, blocks)
     return res
 
 
@@ -183,7 +222,7 @@ def trace_summary(path: str) -> int:
     groups = defaultdict(list)
     with open(path) as f:
         for r in csv.DictReader(f):
-            name = r["Kernel_Name"].split("(")[0]
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
             grid = int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0)
             wg = int(r.get("Workgroup_Size", r.get("Workgroup_Size_X", 0)) or 0)
             dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
@@ -233,8 +272,11 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
         return 0
 
+    decode = CASES["w4a8_skinny_m16"]
+    stream_bytes = decode.N * decode.K // 2  # the decode shapes' packed weights
     if args.ceiling:
-        print(json.dumps({"ceiling": sustained_ceilings(torch, dev, torch.cuda.current_stream())}))
+        print(json.dumps({"ceiling": sustained_ceilings(torch, dev, torch.cuda.current_stream(),
+                                                        stream_bytes=stream_bytes)}))
         return 0
 
     names = [n for n in STEP_ORDER if args.case is None or n in args.case]
@@ -447,7 +489,17 @@ def main() -> int:
                             "bound": bound, "roofline_frac": round(t_roof / (med * 1e-6), 4)}
         del flush
 
-    ceiling = None if args.no_ceiling else sustained_ceilings(torch, dev, stream)
+    ceiling = (None if args.no_ceiling
+               else sustained_ceilings(torch, dev, stream, stream_bytes=stream_bytes))
+    if ceiling is not None:
+        # The decode records against one streaming pass over their weights.
+        sus_gbs = ceiling["hbm_stream_read"]["gb_s"]
+        decode_names = [w["case"].name for w in work if w["plan"]["kernel"] == "skinny"]
+        for recs in (per_config, isolated, cold):
+            for name in decode_names:
+                if name in recs:
+                    recs[name]["stream_read_gbs"] = sus_gbs
+                    recs[name]["stream_read_frac"] = round(recs[name]["gbs"] / sus_gbs, 4)
 
     _, dc, drec, davg = dominant
     if drec["bound"] == "mfma":

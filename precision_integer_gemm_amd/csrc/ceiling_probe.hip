@@ -21,6 +21,11 @@
 //
 // Work per launch (ceiling_probe_work): kinds 0-2 and 4 in operations
 // (2 x MACs), kind 3 in LDS bytes read.
+//
+// ceiling_probe_stream_read is the HBM counterpart: one plain pass over a
+// caller's buffer with 16-byte non-temporal loads, four in flight per thread,
+// every byte read once (what a single streaming pass of that size reaches,
+// launch and ramp included, for the memory-bound GEMM shapes).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -154,6 +159,30 @@ __global__ __launch_bounds__(512) void lds_mfma_loop(float *out, int iters)
 
 int threads_of(int kind) { return kind >= 3 ? 512 : 256; }
 
+constexpr int kStreamThreads = 256;
+constexpr int kStreamInFlight = 4;
+
+// Thread t folds 16-byte elements t, t + S, t + 2S, ... (S = grid threads),
+// kStreamInFlight loads issued before any is used, and writes one int.
+__global__ __launch_bounds__(kStreamThreads) void stream_read(const i32x4 *__restrict__ p, int64_t n,
+                                                              int32_t *out)
+{
+    const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+    const int64_t t = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    int32_t fold = 0;
+    for (int64_t base = t; base < n; base += stride * kStreamInFlight) {
+        i32x4 v[kStreamInFlight];
+#pragma unroll
+        for (int u = 0; u < kStreamInFlight; ++u) {
+            const int64_t i = base + u * stride;
+            v[u] = i < n ? __builtin_nontemporal_load(p + i) : i32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kStreamInFlight; ++u) fold ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    out[t] = fold;
+}
+
 }  // namespace
 
 // Work of one launch: operations (kinds 0-2, 4) or LDS bytes read (kind 3).
@@ -195,5 +224,27 @@ extern "C" int ceiling_probe_run(int kind, int blocks, int iters, float *out, in
     if (hipLaunchKernel(fn, dim3((unsigned)blocks), dim3((unsigned)threads_of(kind)), args, kLdsRequest,
                         stream) != hipSuccess)
         return -2;
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// Ints of `out` one stream_read launch of `blocks` workgroups writes.
+extern "C" int64_t ceiling_probe_stream_out_ints(int blocks)
+{
+    return (int64_t)blocks * kStreamThreads;
+}
+
+// One streaming pass over `bytes` bytes of device memory at `buf` (16-byte
+// aligned, bytes a multiple of 16) with `blocks` workgroups on `stream`; `out`
+// holds `out_ints` >= ceiling_probe_stream_out_ints(blocks) ints.  Returns 0,
+// -1 for bad arguments, or -2 if the launch failed.
+extern "C" int ceiling_probe_stream_read(const void *buf, int64_t bytes, int blocks, int32_t *out,
+                                         int64_t out_ints, hipStream_t stream)
+{
+    if (buf == nullptr || out == nullptr || bytes <= 0 || (bytes & 15) ||
+        (reinterpret_cast<uintptr_t>(buf) & 15u) || blocks < 1 ||
+        out_ints < ceiling_probe_stream_out_ints(blocks))
+        return -1;
+    hipLaunchKernelGGL(stream_read, dim3((unsigned)blocks), dim3(kStreamThreads), 0, stream,
+                       static_cast<const i32x4 *>(buf), bytes / 16, out);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }

@@ -232,3 +232,27 @@ def test_ceiling_probe_library_loads_and_checks_arguments():
     assert probe.ceiling_probe_run(0, 0, 1, 16, 1 << 20, None) == -1
     assert probe.ceiling_probe_run(0, 1, 1, None, 1 << 20, None) == -1
     assert probe.ceiling_probe_run(0, 4, 1, 16, 1023, None) == -1
+
+
+def test_stream_read_probe_checks_arguments():
+    # the HBM streaming-read probe rejects bad arguments before any HIP call
+    probe = ctypes.CDLL(os.path.join(ROOT, "precision_integer_gemm_amd", "_ceiling.so"))
+    probe.ceiling_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    probe.ceiling_probe_stream_out_ints.argtypes = [ctypes.c_int]
+    probe.ceiling_probe_stream_out_ints.restype = ctypes.c_int64
+    assert probe.ceiling_probe_stream_out_ints(4096) == 4096 * 256
+    ok = dict(buf=256, nbytes=1 << 20, blocks=4, out=256, out_ints=1024)
+
+    def run(**kw):
+        a = {**ok, **kw}
+        return probe.ceiling_probe_stream_read(a["buf"], a["nbytes"], a["blocks"], a["out"],
+                                               a["out_ints"], None)
+
+    assert run(buf=None) == -1
+    assert run(buf=264) == -1          # not 16-byte aligned
+    assert run(nbytes=0) == -1
+    assert run(nbytes=(1 << 20) + 8) == -1  # not whole 16-byte elements
+    assert run(blocks=0) == -1
+    assert run(out=None) == -1
+    assert run(out_ints=1023) == -1    # shorter than one int per thread
