@@ -177,7 +177,8 @@ lpgemm_status lpgemm_fp8_e4m3(const uint8_t *A, const uint8_t *B, void *C,
  *            bits of each value are kept, as the tutorial's pack_int4 does)
  *   packed   device, bytes [rows][K/2], written
  * K must be even (LPGEMM_ERR_INVALID_ARG otherwise, as pack_int4 raises on an
- * odd last dimension).  The tutorial's pack_int4 defines the layout.
+ * odd last dimension); rows * K/2 beyond the int64 range returns
+ * LPGEMM_ERR_UNSUPPORTED.  The tutorial's pack_int4 defines the layout.
  */
 lpgemm_status lpgemm_pack_int4(const int8_t *logical, uint8_t *packed, int64_t rows, int64_t K,
                                hipStream_t stream);
@@ -186,8 +187,9 @@ lpgemm_status lpgemm_pack_int4(const int8_t *logical, uint8_t *packed, int64_t r
  * Unpack bytes into logical int4 values, one per int8, sign-extended:
  *   packed   device, bytes [rows][K/2]
  *   logical  device, int8 [rows][K], written
- * The dequantise-only test kernel of "[Example] add w4a8 gemm kernel"
- * (u8 -> i4 -> i8 of byte j//2, nibble j%2) defines the operation.
+ * Argument errors as for lpgemm_pack_int4.  The dequantise-only test kernel
+ * of "[Example] add w4a8 gemm kernel" (u8 -> i4 -> i8 of byte j//2, nibble
+ * j%2) defines the operation.
  */
 lpgemm_status lpgemm_unpack_int4(const uint8_t *packed, int8_t *logical, int64_t rows, int64_t K,
                                  hipStream_t stream);

@@ -490,6 +490,7 @@ lpgemm_status run_elementwise(bool pack, const void *src, void *dst, int64_t row
                               hipStream_t stream)
 {
     if (rows < 0 || K < 0 || (K & 1)) return LPGEMM_ERR_INVALID_ARG;
+    if (K > 0 && rows > INT64_MAX / (K / 2)) return LPGEMM_ERR_UNSUPPORTED;  // bytes would overflow
     const int64_t bytes = rows * (K / 2);
     if (bytes == 0) return LPGEMM_OK;
     if (src == nullptr || dst == nullptr) return LPGEMM_ERR_INVALID_ARG;

@@ -90,6 +90,9 @@ def test_pack_unpack_argument_errors():
     assert lib.lpgemm_pack_int4(P, P, -1, 4, None) == L.ERR_INVALID_ARG
     assert lib.lpgemm_unpack_int4(None, P, 2, 4, None) == L.ERR_INVALID_ARG
     assert lib.lpgemm_unpack_int4(None, None, 0, 4, None) == L.OK
+    # rows * K/2 past the int64 range is refused before any HIP call
+    assert lib.lpgemm_pack_int4(P, P, 1 << 62, 8, None) == L.ERR_UNSUPPORTED
+    assert lib.lpgemm_unpack_int4(P, P, 1 << 62, 8, None) == L.ERR_UNSUPPORTED
 
 
 def test_kernel_override_rejects_unknown_values():
