@@ -211,9 +211,11 @@ typedef enum lpgemm_kernel {
                                  /* 256 x 256 tiles on the FP6 matrix cores       */
 } lpgemm_kernel;
 /* LPGEMM_KERNEL_AUTO picks FP6 for int4 x int4 when the fast path applies,
- * K >= 2048, the 256 x 256 output tiles number at least the compute units, and
- * either twice the compute units or K >= 8192 (there the re-encoding pass
- * costs less than the matrix cores save). */
+ * M > 128, K >= 2048, the 256 x 256 output tiles number at least the compute
+ * units, and either twice the compute units or K >= 8192 (there the
+ * re-encoding pass costs less than the matrix cores save).  Up to 128 rows of
+ * A it takes the tiled kernel with 128 x 128 or 64 x 64 tiles (B is read
+ * once), or the narrow-M kernel for W4A8 with M <= 16. */
 
 typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
 

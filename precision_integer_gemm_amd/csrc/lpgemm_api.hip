@@ -78,6 +78,12 @@ constexpr int kFp6FM = 4, kFp6FN = 2, kFp6WM = 2, kFp6WN = 4, kFp6KS = 2, kFp6St
 using Fp6Tile = Fp6Cfg<kFp6FM, kFp6FN, kFp6WM, kFp6WN, kFp6KS, kFp6Stages>;
 constexpr int64_t kFp6MinK = 2048, kFp6LongK = 8192;
 
+// Up to this many rows of A the product is bound by reading B once: no
+// 256-tiles and no FP6 re-encoding (which alone moves 2.5x B's bytes).  With
+// 64 x 65536 x 8192 int4 operands the FP6 path took 263 us against 80 us on
+// 64- or 128-tiles; with W4A8 64 x 65536 x 4096, 256-tiles 58 us against 48.
+constexpr int64_t kSmallM = 128;
+
 bool fp6_pays(int64_t K, int64_t tiles256, int cu_count)
 {
     return K >= kFp6MinK && tiles256 >= cu_count &&
@@ -130,7 +136,7 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
             k = LPGEMM_KERNEL_GENERAL;
         else if (skinny_ok)
             k = LPGEMM_KERNEL_SKINNY;
-        else if (fp6_ok && fp6_pays(K, large_tiles, cu_count))
+        else if (fp6_ok && M > kSmallM && fp6_pays(K, large_tiles, cu_count))
             k = LPGEMM_KERNEL_FP6;
         else
             k = LPGEMM_KERNEL_TILED;
@@ -157,12 +163,21 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
     case LPGEMM_KERNEL_TILED_64: {
         // Large tiles when they give at least 3/4 of a tile per compute unit;
         // else 128-tiles when they cover at least half of the compute units;
-        // else 64-tiles.
+        // else 64-tiles.  Up to kSmallM rows (one row of 128-tiles, B read
+        // once) never 256-tiles, mostly empty there; up to 64 rows 128-tiles
+        // only when they fill every compute unit, else 64-tiles, which also
+        // read B once and give twice the workgroups.
         const int64_t small_tiles = ceil_div(M, 128) * ceil_div(N, 128);
-        if (k == LPGEMM_KERNEL_TILED)
-            p.tile = large_tiles * 4 >= (int64_t)cu_count * 3 ? 256
-                     : small_tiles * 2 >= (int64_t)cu_count   ? 128
-                                                              : 64;
+        if (k == LPGEMM_KERNEL_TILED) {
+            if (M <= 64)
+                p.tile = small_tiles >= (int64_t)cu_count ? 128 : 64;
+            else if (M <= kSmallM)
+                p.tile = small_tiles * 2 >= (int64_t)cu_count ? 128 : 64;
+            else
+                p.tile = large_tiles * 4 >= (int64_t)cu_count * 3 ? 256
+                         : small_tiles * 2 >= (int64_t)cu_count   ? 128
+                                                                  : 64;
+        }
         else
             p.tile = k == LPGEMM_KERNEL_TILED_256 ? 256 : k == LPGEMM_KERNEL_TILED_128 ? 128 : 64;
         p.kernel = LPGEMM_KERNEL_TILED;

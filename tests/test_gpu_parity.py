@@ -205,6 +205,23 @@ def test_deterministic_repeats(torch):
         assert np.array_equal(run_gpu(torch, "w4a8", A, B, M, N, K), first)
 
 
+# ---- small M through the automatic choice: one row of 64- or 128-tiles ----------
+SMALL_M = [("w4a8", 40, 3000, 2080, 64), ("i4i4", 17, 1000, 8192, 64),
+           ("w4a8", 24, 32868, 1024, 128), ("i4i4", 64, 65536, 8192, 128),
+           ("w4a8", 100, 28700, 2048, 128), ("w4a8", 128, 65600, 512, 128)]
+
+
+@pytest.mark.parametrize("variant,M,N,K,tile", SMALL_M)
+def test_small_m_automatic_choice(torch, variant, M, N, K, tile):
+    v = L.VARIANT_I4I4 if variant == "i4i4" else L.VARIANT_W4A8
+    plan = L.lpgemm_plan(v, M, N, K)
+    say(f"small M {variant} {M}x{N}x{K} plan={plan}")
+    assert (plan["kernel"], plan["tile_m"]) == ("tiled", tile)
+    A, B = custom_operands(variant, M, N, K, seed=700 + M)
+    got = run_gpu(torch, variant, A, B, M, N, K)
+    assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
+
+
 # ---- the named workloads at full size, in the launch configuration the ----------
 # ---- benchmark times (automatic kernel selection) -------------------------------
 FULL = ["i4i4_256", "i4i4_1024", "w4a8_4096", "w4a8_skinny_m16", "w4a8_skinny_m1",

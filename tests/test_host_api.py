@@ -163,6 +163,25 @@ def test_tile_size_follows_the_number_of_tiles():
     assert L.lpgemm_plan(L.VARIANT_I4I4, 3000, 5120, 6144, cu_count=512)["tile_m"] == 128
 
 
+def test_small_m_reads_b_once_without_large_tiles_or_fp6():
+    def tile(variant, M, N, K):
+        p = L.lpgemm_plan(variant, M, N, K)
+        return p["kernel"], p["tile_m"]
+    # up to 64 rows: 128-tiles only when they fill every compute unit
+    assert tile(L.VARIANT_W4A8, 32, 28672, 8192) == ("tiled", 64)    # 224 128-tiles
+    assert tile(L.VARIANT_I4I4, 64, 28672, 8192) == ("tiled", 64)
+    assert tile(L.VARIANT_W4A8, 64, 65536, 4096) == ("tiled", 128)   # 512 128-tiles
+    assert tile(L.VARIANT_I4I4, 64, 65536, 8192) == ("tiled", 128)   # not the FP6 path
+    # 65..128 rows: 128-tiles when they cover half of the compute units, never 256
+    assert tile(L.VARIANT_W4A8, 100, 28672, 8192) == ("tiled", 128)
+    assert tile(L.VARIANT_W4A8, 128, 65536, 4096) == ("tiled", 128)
+    assert tile(L.VARIANT_I4I4, 128, 65536, 8192) == ("tiled", 128)
+    assert tile(L.VARIANT_W4A8, 96, 4096, 4096) == ("tiled", 64)
+    # from 129 rows the earlier rules apply again
+    assert tile(L.VARIANT_I4I4, 129, 65536, 8192) == ("fp6", 256)
+    assert tile(L.VARIANT_W4A8, 256, 65536, 4096) == ("tiled", 256)
+
+
 def test_unaligned_pointers_take_the_general_kernel():
     assert L.lpgemm_plan(L.VARIANT_I4I4, 256, 256, 256, A=P + 1)["kernel"] == "general"
     assert L.lpgemm_plan(L.VARIANT_W4A8, 8, 256, 256, C=P + 4)["kernel"] == "general"
