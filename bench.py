@@ -165,8 +165,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328084.1, "fetch_scale": 2.0, "write_kib": 362800.7,
-                  "write_scale": 1.0, "sources_sha256": "e3abc1795ee298d52a7765fb9aaf36f1774e319ebec66cb19db9945a94589971"},
+    "i4i4_8192": {"fetch_kib": 328112.9, "fetch_scale": 2.0, "write_kib": 361389.5,
+                  "write_scale": 1.0, "sources_sha256": "07aa4ebe60434027ecf4a2b629937cf74311039e16f5c49c6fef311196d87cff"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",

@@ -205,17 +205,19 @@ def test_deterministic_repeats(torch):
         assert np.array_equal(run_gpu(torch, "w4a8", A, B, M, N, K), first)
 
 
-# ---- small M through the automatic choice: one row of 64- or 128-tiles ----------
-SMALL_M = [("w4a8", 40, 3000, 2080, 64), ("i4i4", 17, 1000, 8192, 64),
-           ("w4a8", 24, 32868, 1024, 128), ("i4i4", 64, 65536, 8192, 128),
-           ("w4a8", 100, 28700, 2048, 128), ("w4a8", 128, 65600, 512, 128)]
+# ---- the automatic tile choice: small M (one row of 64- or 128-tiles), and ------
+# ---- 64-tiles where 128-tiles would leave compute units idle --------------------
+AUTO_TILE = [("w4a8", 40, 3000, 2080, 64), ("i4i4", 17, 1000, 8192, 64),
+             ("w4a8", 24, 32868, 1024, 128), ("i4i4", 64, 65536, 8192, 128),
+             ("w4a8", 100, 28700, 2048, 128), ("w4a8", 128, 65600, 512, 128),
+             ("i4i4", 256, 8192, 2048, 64), ("w4a8", 520, 8200, 1024, 128)]
 
 
-@pytest.mark.parametrize("variant,M,N,K,tile", SMALL_M)
-def test_small_m_automatic_choice(torch, variant, M, N, K, tile):
+@pytest.mark.parametrize("variant,M,N,K,tile", AUTO_TILE)
+def test_automatic_tile_choice(torch, variant, M, N, K, tile):
     v = L.VARIANT_I4I4 if variant == "i4i4" else L.VARIANT_W4A8
     plan = L.lpgemm_plan(v, M, N, K)
-    say(f"small M {variant} {M}x{N}x{K} plan={plan}")
+    say(f"automatic tile {variant} {M}x{N}x{K} plan={plan}")
     assert (plan["kernel"], plan["tile_m"]) == ("tiled", tile)
     A, B = custom_operands(variant, M, N, K, seed=700 + M)
     got = run_gpu(torch, variant, A, B, M, N, K)

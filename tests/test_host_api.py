@@ -161,6 +161,10 @@ def test_tile_size_follows_the_number_of_tiles():
     assert L.lpgemm_plan(L.VARIANT_I4I4, 1024, 1024, 1024)["tile_m"] == 64   # 64 tiles of 128: too few
     assert L.lpgemm_plan(L.VARIANT_W4A8, 300, 260, 1056)["tile_m"] == 64
     assert L.lpgemm_plan(L.VARIANT_I4I4, 3000, 5120, 6144, cu_count=512)["tile_m"] == 128
+    # 128-tiles only when they fill every compute unit; else 64-tiles, two per unit
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 256, 8192, 8192)["tile_m"] == 64     # 128 tiles of 128
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 1536, 1536, 8192)["tile_m"] == 64    # 144 tiles of 128
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 512, 8192, 8192)["tile_m"] == 128    # 256 tiles of 128
 
 
 def test_small_m_reads_b_once_without_large_tiles_or_fp6():
