@@ -11,9 +11,13 @@ Two kinds of comparison:
     term).  The matrix-core kernel's v_mfma_scale_f32_32x32x64_f8f6f4 does not
     add the 64 products of one instruction in IEEE binary32: small products
     next to a large one lose low-order bits (measured: of 63 products of 1 next
-    to one of 448 * 448, 56 arrive).  Its error bound is not published; the
-    measured worst case over random sums is 1.03e-4 * sum|a b| (K = 16), and
-    the tests allow 2^-12 * sum|a b| (2.4e-4) on top of the binary32 bound.
+    to one of 448 * 448, 56 arrive).  Its error bound is not published.  The
+    loss of one instruction scales with its largest product, which sum|a b|
+    bounds; the largest loss measured is 3.3e-4 of that product (12 beside
+    36864 in a 64-k sum, seen once the 300 x 49200 x 64 case put 14.8 M sums
+    through the kernel), so the tests allow 2^-10 * sum|a b| (9.8e-4, three
+    times that) on top of the binary32 bound: an envelope from measurement,
+    not a proof.
 An e4m3 result must be the rounding of some value in the allowed interval
 (e4m3 rounding is monotone: between the codes of the interval's ends).  C sits
 between guard bands pre-filled with a sentinel.
@@ -85,7 +89,7 @@ def run_gpu(torch, A, B, M, N, K, fp8_out, kernel=L.KERNEL_AUTO, c_offset=0):
     return out if fp8_out else out.view(np.float32).astype(np.float64)
 
 
-MFMA_REL = 2.0 ** -12
+MFMA_REL = 2.0 ** -10
 
 
 def tolerance(C, Cabs, K, mfma):
@@ -133,6 +137,16 @@ def test_general(torch, M, N, K, fp8_out):
     C, Cabs = oracle.gemm_fp8(A, B, M, N, K)
     got = run_gpu(torch, A, B, M, N, K, fp8_out, kernel=L.KERNEL_GENERAL)
     (check_e4m3 if fp8_out else check_f32)(got, C, Cabs, K, mfma=False)
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 49200, 128), (300, 49200, 64)])
+def test_automatic_choice_wide_shapes(torch, M, N, K):
+    # up to 128 rows the automatic choice takes 128-tiles where the 256-tiles
+    # would be mostly empty; above, 256-tiles (N >= 49152 gives enough of them)
+    say(f"fp8 automatic {M}x{N}x{K}")
+    A, B = codes(M + 13 * K, M, K), codes(N + 17 * K, N, K)
+    C, Cabs = oracle.gemm_fp8(A, B, M, N, K)
+    check_f32(run_gpu(torch, A, B, M, N, K, False), C, Cabs, K)
 
 
 def integer_codes(stream, rows, K):
