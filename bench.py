@@ -165,8 +165,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328101.4, "fetch_scale": 2.0, "write_kib": 361348.7,
-                  "write_scale": 1.0, "sources_sha256": "9385300305649296ec2e528a7cf7fca1a033e303f5e1ae2329f4c31e6a4f302d"},
+    "i4i4_8192": {"fetch_kib": 328125.1, "fetch_scale": 2.0, "write_kib": 363465.9,
+                  "write_scale": 1.0, "sources_sha256": "ef2c0b2d747456a5765fa74fae163b9c808ff9afde6745cfe11aba46cd0461e6"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",

@@ -215,7 +215,9 @@ typedef enum lpgemm_kernel {
  * units, and either twice the compute units or K >= 8192 (there the
  * re-encoding pass costs less than the matrix cores save).  Up to 128 rows of
  * A it takes the tiled kernel with 128 x 128 or 64 x 64 tiles (B is read
- * once), or the narrow-M kernel for W4A8 with M <= 16. */
+ * once), or the narrow-M kernel for W4A8 with M <= 16 (with K > 8192 and an
+ * int32 result, K is cut into ranges whose sums are added into C, which the
+ * call zeroes first; scaled results with K > 8192 take the tiled kernel). */
 
 typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
 
@@ -227,7 +229,8 @@ typedef struct lpgemm_plan_info {
     int32_t k_split;       /* waves that split K inside one workgroup (skinny)   */
     int64_t workgroups;    /* workgroups launched                                */
     int32_t threads;       /* threads per workgroup                              */
-    int32_t reserved;
+    int32_t k_chunks;      /* K ranges contracted by separate workgroup groups   */
+                           /* and added into C (skinny with K > 8192), else 1   */
 } lpgemm_plan_info;
 
 /*

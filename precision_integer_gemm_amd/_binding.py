@@ -41,12 +41,13 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("k_split", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("threads", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("k_chunks", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {"kernel": KERNEL_NAMES.get(self.kernel, self.kernel), "tile_m": self.tile_m,
                 "tile_n": self.tile_n, "k_split": self.k_split,
-                "workgroups": self.workgroups, "threads": self.threads}
+                "workgroups": self.workgroups, "threads": self.threads,
+                "k_chunks": self.k_chunks}
 
 
 _lib = None

@@ -32,8 +32,15 @@ namespace lpgemm {
 //     one wave (rotating) after the next iteration's barrier, so one barrier
 //     per strip suffices and C stores overlap the next strip's work.
 //
+// Split K (SPLIT, int32 output only): K longer than one workgroup's waves
+// cover is cut into ranges of kc; the grid is `chunks` equal groups of
+// workgroups, group c contracting k in [c kc, (c + 1) kc) for its share of the
+// strips (its A range loaded once), and every strip's sum is added into C,
+// zeroed beforehand, with int32 atomic adds -- exact and independent of order.
+//
 // Requirements (checked on the host): M <= 16, K % 32 == 0, 16-byte aligned
-// bases, N * K / 2 < 2^31, KW * KSTEPS * 128 >= K, at most 256 workgroups.
+// bases, N * K / 2 < 2^31, KW * KSTEPS * 128 >= kc, kc % 32 == 0, at most 256
+// workgroups, a multiple of the number of K ranges.
 template <int KW, int KSTEPS>
 struct SkinnyCfg {
     static constexpr int kBufBytes = KW * KSTEPS * 1024;  // one strip (16 rows x K/2 bytes, padded)
@@ -42,10 +49,21 @@ struct SkinnyCfg {
     static_assert(kLdsBytes <= 160 * 1024, "strip buffers exceed the LDS");
 };
 
-template <int KW, int KSTEPS, int OUT>
-__global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
-    const int8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N, int K)
+// C[m][n + i] += v[i] for the columns that exist (int32 atomics, no return).
+__device__ __forceinline__ void atomic_add_row4(const Epilogue &e, int64_t m, int N, int n, i32x4 v)
 {
+    int32_t *row = static_cast<int32_t *>(e.out) + m * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (n + i < N) __hip_atomic_fetch_add(row + n + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int KW, int KSTEPS, int OUT, bool SPLIT>
+__global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
+    const int8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N, int K,
+    int kc)
+{
+    static_assert(!SPLIT || OUT == OUT_I32, "split K adds int32 partial sums");
     using Cfg = SkinnyCfg<KW, KSTEPS>;
     extern __shared__ __align__(1024) uint8_t smem[];
     i32x4 *red = reinterpret_cast<i32x4 *>(smem + 2 * Cfg::kBufBytes);  // [2][KW][64]
@@ -55,21 +73,28 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
     const int g = lane >> 4;
     const int r16 = lane & 15;
     const int strips = (N + 15) / 16;
-    const uint32_t ldb = (uint32_t)K / 2;
-    const int cpr = (int)(ldb / 16);               // 16-byte chunks per row
+    // This workgroup's K range [k0, k0 + klen) and its share of the strips.
+    const int chunks = SPLIT ? (K + kc - 1) / kc : 1;
+    const int G = (int)gridDim.x / chunks;
+    const int chunk = SPLIT ? (int)blockIdx.x / G : 0;
+    const int k0 = chunk * kc;
+    const int klen = SPLIT ? min(kc, K - k0) : K;
+    const uint32_t ldb = (uint32_t)K / 2;           // row stride of B
+    const int cpr = klen / 32;                      // 16-byte chunks per row of the range
     const int swz_mask = (cpr % 16 == 0) ? 15 : 0;  // XOR swizzle only when it stays in the row
-    const int k_begin = wave * (KSTEPS * 128);
+    const int k_begin = wave * (KSTEPS * 128);      // relative to k0
 
     const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(A, (uint32_t)M * (uint32_t)K);
     const i32x4 rsrc_b = make_rsrc(B, (uint32_t)N * ldb);
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
-    // A fragments of this wave's K slice (zeros past K and past M).
+    // A fragments of this wave's K slice (zeros past the range and past M).
     i32x4 a_lo[KSTEPS], a_hi[KSTEPS];
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
         const int kl = k_begin + 128 * j + 32 * g;
-        const uint32_t off = kl < K ? (uint32_t)r16 * (uint32_t)K + (uint32_t)kl : kOutOfRange;
+        const uint32_t off =
+            kl < klen ? (uint32_t)r16 * (uint32_t)K + (uint32_t)(k0 + kl) : kOutOfRange;
         a_lo[j] = buffer_load16(rsrc_a, off);
         a_hi[j] = buffer_load16(rsrc_a, off == kOutOfRange ? kOutOfRange : off + 16);
     }
@@ -84,7 +109,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
         const int q = (wave * KSTEPS + t) * 64 + lane;
         const int row = q / cpr, slot = q % cpr;
         dma_live[t] = row < 16;
-        dma_row_off[t] = (uint32_t)row * ldb + 16u * (uint32_t)(slot ^ (row & swz_mask));
+        dma_row_off[t] = (uint32_t)row * ldb + (uint32_t)k0 / 2 + 16u * (uint32_t)(slot ^ (row & swz_mask));
     }
     auto issue_strip = [&](int s, int b) {
         const uint32_t base = (uint32_t)s * 16u * ldb;
@@ -98,13 +123,12 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
     uint32_t frag_off[KSTEPS];
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-        int kc = (k_begin + 128 * t) / 32 + g;
-        kc = kc < cpr ? kc : cpr - 1;  // past K: A is zero there, any in-strip data will do
-        frag_off[t] = 16u * (uint32_t)(r16 * cpr + (kc ^ (r16 & swz_mask)));
+        int col = (k_begin + 128 * t) / 32 + g;
+        col = col < cpr ? col : cpr - 1;  // past the range: A is zero there, any in-strip data will do
+        frag_off[t] = 16u * (uint32_t)(r16 * cpr + (col ^ (r16 & swz_mask)));
     }
 
-    const int G = gridDim.x;
-    int s = blockIdx.x;
+    int s = (int)blockIdx.x - chunk * G;
     if (s >= strips) return;
     issue_strip(s, 0);
     int it = 0;
@@ -122,13 +146,19 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
     bool held = false;
     int held_n = 0;
     i32x4 held_sum = {0, 0, 0, 0};
+    auto put = [&](int n, const i32x4 &sum) {
+        if constexpr (SPLIT)
+            atomic_add_row4(epi, r16, N, n, sum);
+        else
+            store_row4<OUT>(epi, r16, N, n, sum, pend_sa, pend_sb);
+    };
     auto emit = [&](int n, const i32x4 &sum) {
         if (r16 >= M) return;
         if (!kHold) {
-            store_row4<OUT>(epi, r16, N, n, sum, pend_sa, pend_sb);
+            put(n, sum);
             return;
         }
-        if (held) store_row4<OUT>(epi, r16, N, held_n, held_sum, pend_sa, pend_sb);
+        if (held) put(held_n, held_sum);
         held = true;
         held_n = n;
         held_sum = sum;
@@ -181,7 +211,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
         sum >>= 4;
         emit(prev * 16 + 4 * g, sum);
     }
-    if (kHold && held && r16 < M) store_row4<OUT>(epi, r16, N, held_n, held_sum, pend_sa, pend_sb);
+    if (kHold && held && r16 < M) put(held_n, held_sum);
 }
 
 }  // namespace lpgemm

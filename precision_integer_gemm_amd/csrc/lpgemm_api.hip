@@ -92,7 +92,9 @@ bool fp6_pays(int64_t K, int64_t tiles256, int cu_count)
 
 // Skinny: 16 waves split K (up to 4 steps of 128 k each, A held in registers);
 // one workgroup per compute unit walks strips of 16 rows of B, staged in LDS.
-// (16 waves contract a strip faster than 8 with twice the steps each.)
+// (16 waves contract a strip faster than 8 with twice the steps each.)  Longer
+// K (int32 output) is cut into equal ranges of at most kSkinnyMaxK, a multiple
+// of 256, each taken by its own group of workgroups and added into C.
 constexpr int kSkinnyKW = 16;
 constexpr int kSkinnyMaxM = 16;
 constexpr int kSkinnyMaxK = kSkinnyKW * 4 * 128;
@@ -102,6 +104,7 @@ struct Plan {
     int tile_m = 0, tile_n = 0, k_split = 1, threads = 0;
     int64_t workgroups = 0;
     int k_steps = 0;
+    int k_chunks = 1, kc = 0;  // skinny: K ranges added into C, and their length
     int tiles_m = 0, tiles_n = 0;
     int tile = 0;  // tiled kernels: 256, 128 or 64 (square tiles)
 };
@@ -119,13 +122,14 @@ lpgemm_status check_args(const void *A, const void *B, const void *C, int64_t M,
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// int_out: the result is the int32 C (split K is available), not a scaled one.
 lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, const void *C,
                         int64_t M, int64_t N, int64_t K, int cu_count, lpgemm_kernel forced,
-                        Plan *plan)
+                        bool int_out, Plan *plan)
 {
     const bool fast_ok = (K % 32 == 0) && aligned16(A) && aligned16(B) && aligned16(C);
     const bool skinny_ok = fast_ok && variant == LPGEMM_VARIANT_W4A8 && M <= kSkinnyMaxM &&
-                           K <= kSkinnyMaxK && N * (K / 2) < INT32_MAX;
+                           (K <= kSkinnyMaxK || int_out) && N * (K / 2) < INT32_MAX;
 
     const bool fp6_ok = fast_ok && variant == LPGEMM_VARIANT_I4I4;
     const int64_t large_tiles = ceil_div(M, 256) * ceil_div(N, 256);
@@ -212,9 +216,16 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         p.tile_n = 16;
         p.k_split = kSkinnyKW;
         p.threads = 64 * kSkinnyKW;
-        p.k_steps = (int)ceil_div(ceil_div(K, kSkinnyKW), 128);  // 1..4
-        while (p.k_steps & (p.k_steps - 1)) ++p.k_steps;          // 1, 2 or 4
-        p.workgroups = std::min<int64_t>(ceil_div(N, 16), std::min(cu_count, 256));
+        int64_t chunks = ceil_div(K, kSkinnyMaxK);
+        const int64_t kc = chunks > 1 ? ceil_div(ceil_div(K, chunks), 256) * 256 : K;
+        chunks = ceil_div(K, kc);
+        p.k_chunks = (int)chunks;
+        p.kc = (int)kc;
+        p.k_steps = (int)ceil_div(ceil_div(kc, kSkinnyKW), 128);  // 1..4
+        while (p.k_steps & (p.k_steps - 1)) ++p.k_steps;           // 1, 2 or 4
+        const int64_t per_range = std::min<int64_t>(
+            ceil_div(N, 16), std::max<int64_t>(1, std::min(cu_count, 256) / chunks));
+        p.workgroups = chunks * per_range;
         break;
     }
     default:
@@ -253,25 +264,32 @@ lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Ep
     return e == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
 }
 
-// Launch the narrow-M kernel for K up to KSTEPS * 1024; the first launch on
-// each device raises its dynamic-LDS limit to the two strip buffers.
-template <int KSTEPS, int OUT>
+// Launch the narrow-M kernel for K ranges up to KSTEPS * 1024 (SPLIT: several
+// ranges added into C, which is zeroed first by a fill kernel); the first
+// launch on each device raises its dynamic-LDS limit to the two strip buffers.
+template <int KSTEPS, int OUT, bool SPLIT>
 lpgemm_status launch_skinny(const Plan &p, const int8_t *a, const uint8_t *b, Epilogue epi, int m,
                             int n, int k, hipStream_t stream)
 {
     using Cfg = SkinnyCfg<kSkinnyKW, KSTEPS>;
+    constexpr auto kernel = &gemm_w4a8_skinny_kernel<kSkinnyKW, KSTEPS, OUT, SPLIT>;
     static std::once_flag once[kMaxDevices];
     static hipError_t attr_err[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERR_HIP;
     std::call_once(once[dev], [dev] {
-        attr_err[dev] = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&gemm_w4a8_skinny_kernel<kSkinnyKW, KSTEPS, OUT>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
+        attr_err[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
     });
     if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
-    hipLaunchKernelGGL((gemm_w4a8_skinny_kernel<kSkinnyKW, KSTEPS, OUT>), dim3((unsigned)p.workgroups),
-                       dim3(p.threads), Cfg::kLdsBytes, stream, a, b, epi, m, n, k);
+    if (SPLIT) {
+        const int64_t count = (int64_t)m * n;
+        const int blocks = (int)std::min<int64_t>(ceil_div(count, 256), 65536);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream,
+                           static_cast<int32_t *>(epi.out), count);
+    }
+    hipLaunchKernelGGL(kernel, dim3((unsigned)p.workgroups), dim3(p.threads), Cfg::kLdsBytes, stream,
+                       a, b, epi, m, n, k, p.kc);
     return launched();
 }
 
@@ -376,10 +394,16 @@ lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, 
         return launch_fp6<OUT>(p, a, b, epi, m, n, k, stream);
     case LPGEMM_KERNEL_SKINNY: {
         const int8_t *a8 = static_cast<const int8_t *>(A);
+        if constexpr (OUT == OUT_I32) {
+            if (p.k_chunks > 1) {  // ranges are longer than 4096 k: four steps per wave
+                if (p.k_steps != 4) return LPGEMM_ERR_INVALID_ARG;
+                return launch_skinny<4, OUT, true>(p, a8, b, epi, m, n, k, stream);
+            }
+        }
         switch (p.k_steps) {
-        case 1: return launch_skinny<1, OUT>(p, a8, b, epi, m, n, k, stream);
-        case 2: return launch_skinny<2, OUT>(p, a8, b, epi, m, n, k, stream);
-        default: return launch_skinny<4, OUT>(p, a8, b, epi, m, n, k, stream);
+        case 1: return launch_skinny<1, OUT, false>(p, a8, b, epi, m, n, k, stream);
+        case 2: return launch_skinny<2, OUT, false>(p, a8, b, epi, m, n, k, stream);
+        default: return launch_skinny<4, OUT, false>(p, a8, b, epi, m, n, k, stream);
         }
     }
     default:
@@ -424,7 +448,7 @@ lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, voi
     }
     Plan p;
     st = make_plan(variant, A, B, C, M, N, K, device_cu_count(),
-                   (lpgemm_kernel)g_override.load(std::memory_order_relaxed), &p);
+                   (lpgemm_kernel)g_override.load(std::memory_order_relaxed), out_format == OUT_I32, &p);
     if (st != LPGEMM_OK) return st;
     switch (out_format) {
     case OUT_I32: return launch_gemm<OUT_I32>(p, variant, A, B, epi, M, N, K, stream);
@@ -605,7 +629,7 @@ lpgemm_status lpgemm_plan(lpgemm_variant variant, const void *A, const void *B, 
     if (M == 0 || N == 0 || K == 0) return LPGEMM_OK;  // nothing, or a zero fill
     Plan p;
     st = make_plan(variant, A, B, C, M, N, K, cu_count > 0 ? cu_count : kDefaultCUs,
-                   (lpgemm_kernel)g_override.load(std::memory_order_relaxed), &p);
+                   (lpgemm_kernel)g_override.load(std::memory_order_relaxed), true, &p);
     if (st != LPGEMM_OK) return st;
     info->kernel = p.kernel;
     info->tile_m = p.tile_m;
@@ -613,6 +637,7 @@ lpgemm_status lpgemm_plan(lpgemm_variant variant, const void *A, const void *B, 
     info->k_split = p.k_split;
     info->workgroups = p.workgroups;
     info->threads = p.threads;
+    info->k_chunks = p.k_chunks;
     return LPGEMM_OK;
 }
 

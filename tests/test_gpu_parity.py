@@ -119,6 +119,24 @@ def test_skinny_kernel(torch, M, N, K):
     assert np.array_equal(got, oracle_full("w4a8", A, B, M, N, K))
 
 
+# K above 8192 on the narrow-M kernel: equal K ranges, each summed into C by its
+# own group of workgroups (C zeroed first, int32 atomic adds)
+SKINNY_SPLIT = [(1, 257, 8224), (16, 1000, 16384), (13, 2049, 12320), (7, 100, 28672),
+                (16, 64, 131040), (16, 8192, 28672)]
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY_SPLIT)
+def test_skinny_split_k(torch, M, N, K):
+    plan = L.lpgemm_plan(L.VARIANT_W4A8, M, N, K)
+    say(f"skinny split-K w4a8 {M}x{N}x{K} plan={plan}")
+    assert plan["kernel"] == "skinny" and plan["k_chunks"] > 1
+    A, B = custom_operands("w4a8", M, N, K, seed=M * 7 + N + K)
+    got = run_gpu(torch, "w4a8", A, B, M, N, K)
+    assert np.array_equal(got, oracle_full("w4a8", A, B, M, N, K))
+    # a second call must not add onto the first (C is zeroed by the call itself)
+    assert np.array_equal(run_gpu(torch, "w4a8", A, B, M, N, K), got)
+
+
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
 def test_unaligned_operand_takes_general_path(torch, variant):
     M, N, K = 40, 72, 256

@@ -134,6 +134,18 @@ def test_skinny_kernel(torch, fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))
+def test_narrow_m_long_k_scaled(torch, fmt):
+    # K above 8192 with M <= 16: the int32 result would be split over K ranges
+    # and added into C; a scaled result cannot be, and takes the tiled kernel
+    M, N, K = 16, 300, 9216
+    say(f"scaled narrow-M long K {fmt} {M}x{N}x{K}")
+    A, B = custom_operands("w4a8", M, N, K, seed=91)
+    sa, sb = scale_vector(91, 0, M), scale_vector(91, 1, N)
+    got = run_scaled(torch, "w4a8", A, B, sa, sb, M, N, K, fmt)
+    check(got, oracle.gemm_scaled("w4a8", A, B, sa, sb, M, N, K, FORMATS[fmt][1]))
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
 def test_k_zero_gives_signed_zeros(torch, variant, fmt):
     say(f"scaled k0 {variant} {fmt}")

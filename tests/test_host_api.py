@@ -235,8 +235,24 @@ def test_plan_grid_covers_the_output():
 
 def test_narrow_m_limits():
     assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 4096, 8192)["kernel"] == "skinny"
-    assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 4096, 8224)["kernel"] == "tiled"   # K above 8192
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 4096, 8192)["k_chunks"] == 1
     assert L.lpgemm_plan(L.VARIANT_W4A8, 17, 4096, 4096)["kernel"] == "tiled"   # M above 16
+    # N * K / 2 must stay below 2^31 (32-bit buffer offsets)
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 65536, 65536)["kernel"] == "tiled"
+
+
+def test_narrow_m_split_k_plan():
+    # K above 8192: equal ranges of at most 8192 (multiples of 256), one group of
+    # workgroups per range, the compute units shared between the groups
+    def plan(M, N, K, **kw):
+        p = L.lpgemm_plan(L.VARIANT_W4A8, M, N, K, **kw)
+        return p["kernel"], p["k_chunks"], p["workgroups"]
+    assert plan(16, 4096, 8224) == ("skinny", 2, 256)       # 2 ranges x min(256 strips, 128)
+    assert plan(16, 8192, 28672) == ("skinny", 4, 256)      # 4 x 7168: 4 x 64 workgroups
+    assert plan(1, 2048, 65536) == ("skinny", 8, 256)       # 128 strips, 32 workgroups per range
+    assert plan(16, 64, 131040) == ("skinny", 16, 64)       # 4 strips per range
+    assert plan(16, 100, 16384) == ("skinny", 2, 14)        # 7 strips per range
+    assert plan(16, 8192, 28672, cu_count=304) == ("skinny", 4, 256)  # at most 256 workgroups
 
 
 def test_ceiling_probe_library_loads_and_checks_arguments():
