@@ -20,8 +20,9 @@ write-back a previous workload leaves behind; `per_config_cold` times each
 workload after a 512 MiB read that evicts its operands from L2 and MALL;
 `per_config_scaled_bf16` times the scaled product (per-row and per-column
 scales, bf16 output) of each workload alone; `per_config_fp8` times the second
-workload, the fp8 (e4m3) GEMM with fp32 output, at 4096^3 and 8192^3 (outside
-the step and `value`).  `ceiling` holds what the chip sustains, measured
+workload, the fp8 (e4m3) GEMM with fp32 output, at 4096^3 and 8192^3, and
+`per_config_long_k` W4A8 decode shapes with K = 28672 on the narrow-M kernel's
+split-K path (both outside the step and `value`).  `ceiling` holds what the chip sustains, measured
 live by the probe kernels of _ceiling.so (matrix cores only, per format; LDS
 reads; the FP6 GEMM's inner loop without global memory), and `roofline`
 adds the dominant call's fraction of the sustained ceiling of its format.
@@ -461,6 +462,42 @@ def main() -> int:
                 "roofline_frac": round(tops / PEAK_FP8_TOPS, 4)}
             del a8, b8, c8
 
+    # W4A8 decode shapes with K beyond one workgroup's 8192 (the split-K path
+    # of the narrow-M kernel: K ranges added into C), alone, weights rotated
+    # over three copies like the isolated decode calls; against HBM.
+    long_k = {}
+    if args.isolated_reps > 0:
+        from precision_integer_gemm_amd.inputs import custom_operands
+        for (lm, ln, lk) in ((16, 8192, 28672), (1, 8192, 28672)):
+            A_h, B_h = custom_operands("w4a8", lm, ln, lk, seed=lk + lm)
+            la = torch.from_numpy(np.ascontiguousarray(A_h).view(np.uint8)).to(dev)
+            lbs = [torch.from_numpy(B_h).to(dev)]
+            lbs += [lbs[0].clone() for _ in range(2)]
+            lc = torch.empty((lm, ln), dtype=torch.int32, device=dev)
+            plan = L.lpgemm_plan(L.VARIANT_W4A8, lm, ln, lk, la.data_ptr(), lbs[0].data_ptr(),
+                                 lc.data_ptr())
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.isolated_reps)]
+            for j in range(-1, args.isolated_reps):
+                if j >= 0:
+                    evs[j][0].record(stream)
+                st = L.lib().lpgemm_w4a8(la.data_ptr(), lbs[max(j, 0) % 3].data_ptr(), lc.data_ptr(),
+                                         lm, ln, lk, handle)
+                if j >= 0:
+                    evs[j][1].record(stream)
+                if st != L.OK:
+                    raise RuntimeError(f"w4a8 {lm}x{ln}x{lk}: {L.lpgemm_status_string(st)}")
+            torch.cuda.synchronize()
+            us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+            med = float(np.median(us))
+            alg = ln * lk // 2 + lm * lk + 4 * lm * ln
+            long_k[f"w4a8_{lm}x{ln}x{lk}"] = {
+                "kernel": plan["kernel"], "k_chunks": plan["k_chunks"],
+                "median_us": round(med, 3), "min_us": round(float(us.min()), 3),
+                "gbs": round(alg / (med * 1e-6) / 1e9, 1), "bound": "hbm",
+                "roofline_frac": round(alg / (PEAK_HBM_GBS * 1e9) / (med * 1e-6), 4)}
+            del la, lbs, lc
+
     # Each workload cold: before every timed launch a 512 MiB buffer is read
     # (not timed), which evicts its operands from the L2s and the 256 MB MALL
     # with clean lines (a write would leave 512 MB of write-back competing
@@ -495,7 +532,8 @@ def main() -> int:
         # The decode records against one streaming pass over their weights.
         sus_gbs = ceiling["hbm_stream_read"]["gb_s"]
         decode_names = [w["case"].name for w in work if w["plan"]["kernel"] == "skinny"]
-        for recs in (per_config, isolated, cold):
+        decode_names += list(long_k)
+        for recs in (per_config, isolated, cold, long_k):
             for name in decode_names:
                 if name in recs:
                     recs[name]["stream_read_gbs"] = sus_gbs
@@ -543,6 +581,7 @@ def main() -> int:
         "per_config_cold": cold,
         "per_config_scaled_bf16": scaled,
         "per_config_fp8": fp8,
+        "per_config_long_k": long_k,
         "ceiling": ceiling,
     }
 
