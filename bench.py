@@ -61,7 +61,7 @@ PEAK_HBM_GBS = 8000.0
 STEP_ORDER = ["w4a8_skinny_m16", "i4i4_8192", "w4a8_skinny_m1", "w4a8_4096", "i4i4_ragged",
               "i4i4_256", "i4i4_1024"]
 
-KERNEL_SYMBOL = {"tiled": "gemm_pipelined_kernel", "skinny": "gemm_w4a8_skinny_kernel",
+KERNEL_SYMBOL = {"tiled": "gemm_pipelined_kernel", "skinny": "gemm_skinny_kernel",
                  "general": "gemm_general_kernel",
                  "fp6": "fp6_convert_kernel (A, B) + gemm_fp6_kernel"}
 
@@ -166,8 +166,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328125.1, "fetch_scale": 2.0, "write_kib": 363465.9,
-                  "write_scale": 1.0, "sources_sha256": "ef2c0b2d747456a5765fa74fae163b9c808ff9afde6745cfe11aba46cd0461e6"},
+    "i4i4_8192": {"fetch_kib": 328105.1, "fetch_scale": 2.0, "write_kib": 363173.8,
+                  "write_scale": 1.0, "sources_sha256": "74fab3a7a8458c8d4a7ba97cc6ebd0a14351fb5ed975dec993ed97b7073e92f5"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",

@@ -203,7 +203,7 @@ typedef enum lpgemm_kernel {
     LPGEMM_KERNEL_AUTO = 0,      /* choose by shape and alignment (default)      */
     LPGEMM_KERNEL_GENERAL = 1,   /* any shape and alignment; slow                */
     LPGEMM_KERNEL_TILED = 2,     /* block-tiled MFMA kernel, tile size by shape   */
-    LPGEMM_KERNEL_SKINNY = 3,    /* W4A8 narrow-M kernel streaming B once        */
+    LPGEMM_KERNEL_SKINNY = 3,    /* narrow-M kernel (M <= 16) streaming B once   */
     LPGEMM_KERNEL_TILED_128 = 4, /* block-tiled, 128 x 128 output tiles          */
     LPGEMM_KERNEL_TILED_256 = 5, /* block-tiled, 256 x 256 output tiles          */
     LPGEMM_KERNEL_TILED_64 = 6,  /* block-tiled, 64 x 64 output tiles            */
@@ -215,7 +215,7 @@ typedef enum lpgemm_kernel {
  * units, and either twice the compute units or K >= 8192 (there the
  * re-encoding pass costs less than the matrix cores save).  Up to 128 rows of
  * A it takes the tiled kernel with 128 x 128 or 64 x 64 tiles (B is read
- * once), or the narrow-M kernel for W4A8 with M <= 16 (with K > 8192 and an
+ * once), or the narrow-M kernel for M <= 16, either format (with K > 8192 and an
  * int32 result, K is cut into ranges whose sums are added into C, which the
  * call zeroes first; scaled results with K > 8192 take the tiled kernel). */
 

@@ -1,7 +1,9 @@
-// gemm_skinny.hpp -- narrow-M W4A8 kernel for gfx950 (decode-like shapes).
+// gemm_skinny.hpp -- narrow-M kernel for gfx950 (decode-like shapes), for
+// W4A8 and for int4 x int4.
 //
 // For M <= 16 the product is bound by reading the packed weights B once from
-// HBM, so the kernel is built around streaming B at full bandwidth.
+// HBM, so the kernel is built around streaming B at full bandwidth.  A (int8,
+// or packed int4 unpacked x16 when it is loaded) stays in registers.
 #pragma once
 
 #include "device_common.hpp"
@@ -58,12 +60,15 @@ __device__ __forceinline__ void atomic_add_row4(const Epilogue &e, int64_t m, in
         if (n + i < N) __hip_atomic_fetch_add(row + n + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int KW, int KSTEPS, int OUT, bool SPLIT>
-__global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
-    const int8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N, int K,
+template <int VAR, int KW, int KSTEPS, int OUT, bool SPLIT>
+__global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N, int K,
     int kc)
 {
     static_assert(!SPLIT || OUT == OUT_I32, "split K adds int32 partial sums");
+    static_assert(VAR == W4A8 || VAR == I4I4, "4-bit B with an int8 or int4 A");
+    // x16 pre-scale of each 4-bit operand, removed exactly at the end
+    constexpr int kShift = VAR == I4I4 ? 8 : 4;
     using Cfg = SkinnyCfg<KW, KSTEPS>;
     extern __shared__ __align__(1024) uint8_t smem[];
     i32x4 *red = reinterpret_cast<i32x4 *>(smem + 2 * Cfg::kBufBytes);  // [2][KW][64]
@@ -84,19 +89,27 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
     const int swz_mask = (cpr % 16 == 0) ? 15 : 0;  // XOR swizzle only when it stays in the row
     const int k_begin = wave * (KSTEPS * 128);      // relative to k0
 
-    const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(A, (uint32_t)M * (uint32_t)K);
+    const uint32_t lda = VAR == I4I4 ? (uint32_t)K / 2 : (uint32_t)K;  // row stride of A in bytes
+    const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(A, (uint32_t)M * lda);
     const i32x4 rsrc_b = make_rsrc(B, (uint32_t)N * ldb);
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
-    // A fragments of this wave's K slice (zeros past the range and past M).
+    // A fragments of this wave's K slice (zeros past the range and past M):
+    // the 32 k of lane group g as two 16-k MFMA operands, in k order.
     i32x4 a_lo[KSTEPS], a_hi[KSTEPS];
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
         const int kl = k_begin + 128 * j + 32 * g;
-        const uint32_t off =
-            kl < klen ? (uint32_t)r16 * (uint32_t)K + (uint32_t)(k0 + kl) : kOutOfRange;
-        a_lo[j] = buffer_load16(rsrc_a, off);
-        a_hi[j] = buffer_load16(rsrc_a, off == kOutOfRange ? kOutOfRange : off + 16);
+        if constexpr (VAR == I4I4) {
+            const uint32_t off =
+                kl < klen ? (uint32_t)r16 * lda + (uint32_t)(k0 + kl) / 2 : kOutOfRange;
+            unpack_chunk<true>(buffer_load16(rsrc_a, off), a_lo[j], a_hi[j]);
+        } else {
+            const uint32_t off =
+                kl < klen ? (uint32_t)r16 * lda + (uint32_t)(k0 + kl) : kOutOfRange;
+            a_lo[j] = buffer_load16(rsrc_a, off);
+            a_hi[j] = buffer_load16(rsrc_a, off == kOutOfRange ? kOutOfRange : off + 16);
+        }
     }
 
     // DMA of strip s into buffer b: this wave's instructions are KSTEPS
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
             i32x4 sum = rp[lane];
 #pragma unroll
             for (int w = 1; w < KW; ++w) sum += rp[w * 64 + lane];
-            sum >>= 4;  // B carried a factor 16
+            sum >>= kShift;  // the 4-bit operands carried a factor 16 each
             emit(prev * 16 + 4 * g, sum);
         }
         // Next strip's loads into the other buffer (its last readers passed
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a8_skinny_kernel(
         i32x4 sum = rp[lane];
 #pragma unroll
         for (int w = 1; w < KW; ++w) sum += rp[w * 64 + lane];
-        sum >>= 4;
+        sum >>= kShift;
         emit(prev * 16 + 4 * g, sum);
     }
     if (kHold && held && r16 < M) put(held_n, held_sum);

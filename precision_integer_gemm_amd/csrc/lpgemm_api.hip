@@ -90,7 +90,8 @@ bool fp6_pays(int64_t K, int64_t tiles256, int cu_count)
            (tiles256 >= 2 * (int64_t)cu_count || K >= kFp6LongK);
 }
 
-// Skinny: 16 waves split K (up to 4 steps of 128 k each, A held in registers);
+// Skinny (both formats, M <= 16): 16 waves split K (up to 4 steps of 128 k
+// each, A held in registers);
 // one workgroup per compute unit walks strips of 16 rows of B, staged in LDS.
 // (16 waves contract a strip faster than 8 with twice the steps each.)  Longer
 // K (int32 output) is cut into equal ranges of at most kSkinnyMaxK, a multiple
@@ -128,8 +129,8 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
                         bool int_out, Plan *plan)
 {
     const bool fast_ok = (K % 32 == 0) && aligned16(A) && aligned16(B) && aligned16(C);
-    const bool skinny_ok = fast_ok && variant == LPGEMM_VARIANT_W4A8 && M <= kSkinnyMaxM &&
-                           (K <= kSkinnyMaxK || int_out) && N * (K / 2) < INT32_MAX;
+    const bool skinny_ok = fast_ok && M <= kSkinnyMaxM && (K <= kSkinnyMaxK || int_out) &&
+                           N * (K / 2) < INT32_MAX;
 
     const bool fp6_ok = fast_ok && variant == LPGEMM_VARIANT_I4I4;
     const int64_t large_tiles = ceil_div(M, 256) * ceil_div(N, 256);
@@ -267,12 +268,12 @@ lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Ep
 // Launch the narrow-M kernel for K ranges up to KSTEPS * 1024 (SPLIT: several
 // ranges added into C, which is zeroed first by a fill kernel); the first
 // launch on each device raises its dynamic-LDS limit to the two strip buffers.
-template <int KSTEPS, int OUT, bool SPLIT>
-lpgemm_status launch_skinny(const Plan &p, const int8_t *a, const uint8_t *b, Epilogue epi, int m,
+template <int VAR, int KSTEPS, int OUT, bool SPLIT>
+lpgemm_status launch_skinny(const Plan &p, const uint8_t *a, const uint8_t *b, Epilogue epi, int m,
                             int n, int k, hipStream_t stream)
 {
     using Cfg = SkinnyCfg<kSkinnyKW, KSTEPS>;
-    constexpr auto kernel = &gemm_w4a8_skinny_kernel<kSkinnyKW, KSTEPS, OUT, SPLIT>;
+    constexpr auto kernel = &gemm_skinny_kernel<VAR, kSkinnyKW, KSTEPS, OUT, SPLIT>;
     static std::once_flag once[kMaxDevices];
     static hipError_t attr_err[kMaxDevices];
     int dev = 0;
@@ -291,6 +292,24 @@ lpgemm_status launch_skinny(const Plan &p, const int8_t *a, const uint8_t *b, Ep
     hipLaunchKernelGGL(kernel, dim3((unsigned)p.workgroups), dim3(p.threads), Cfg::kLdsBytes, stream,
                        a, b, epi, m, n, k, p.kc);
     return launched();
+}
+
+// The narrow-M instance for the plan's steps per wave and K ranges.
+template <int VAR, int OUT>
+lpgemm_status launch_skinny_steps(const Plan &p, const uint8_t *a, const uint8_t *b, Epilogue epi,
+                                  int m, int n, int k, hipStream_t stream)
+{
+    if constexpr (OUT == OUT_I32) {
+        if (p.k_chunks > 1) {  // ranges are longer than 4096 k: four steps per wave
+            if (p.k_steps != 4) return LPGEMM_ERR_INVALID_ARG;
+            return launch_skinny<VAR, 4, OUT, true>(p, a, b, epi, m, n, k, stream);
+        }
+    }
+    switch (p.k_steps) {
+    case 1: return launch_skinny<VAR, 1, OUT, false>(p, a, b, epi, m, n, k, stream);
+    case 2: return launch_skinny<VAR, 2, OUT, false>(p, a, b, epi, m, n, k, stream);
+    default: return launch_skinny<VAR, 4, OUT, false>(p, a, b, epi, m, n, k, stream);
+    }
 }
 
 // The FP6 path's workspace comes from one stream-ordered memory pool per
@@ -392,20 +411,10 @@ lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, 
                                : launch_tiled<W8Tiny, OUT>(p, a, b, epi, m, n, k, stream);
     case LPGEMM_KERNEL_FP6:
         return launch_fp6<OUT>(p, a, b, epi, m, n, k, stream);
-    case LPGEMM_KERNEL_SKINNY: {
-        const int8_t *a8 = static_cast<const int8_t *>(A);
-        if constexpr (OUT == OUT_I32) {
-            if (p.k_chunks > 1) {  // ranges are longer than 4096 k: four steps per wave
-                if (p.k_steps != 4) return LPGEMM_ERR_INVALID_ARG;
-                return launch_skinny<4, OUT, true>(p, a8, b, epi, m, n, k, stream);
-            }
-        }
-        switch (p.k_steps) {
-        case 1: return launch_skinny<1, OUT, false>(p, a8, b, epi, m, n, k, stream);
-        case 2: return launch_skinny<2, OUT, false>(p, a8, b, epi, m, n, k, stream);
-        default: return launch_skinny<4, OUT, false>(p, a8, b, epi, m, n, k, stream);
-        }
-    }
+    case LPGEMM_KERNEL_SKINNY:
+        return variant == LPGEMM_VARIANT_I4I4
+                   ? launch_skinny_steps<I4I4, OUT>(p, a, b, epi, m, n, k, stream)
+                   : launch_skinny_steps<W4A8, OUT>(p, a, b, epi, m, n, k, stream);
     default:
         return LPGEMM_ERR_INVALID_ARG;
     }

@@ -111,12 +111,13 @@ def test_fp6_kernel(torch, M, N, K):
     assert np.array_equal(got, oracle_full("i4i4", A, B, M, N, K))
 
 
+@pytest.mark.parametrize("variant", ["w4a8", "i4i4"])
 @pytest.mark.parametrize("M,N,K", SKINNY)
-def test_skinny_kernel(torch, M, N, K):
-    say(f"skinny w4a8 {M}x{N}x{K}")
-    A, B = custom_operands("w4a8", M, N, K, seed=M * 3 + N)
-    got = run_gpu(torch, "w4a8", A, B, M, N, K, kernel=L.KERNEL_SKINNY)
-    assert np.array_equal(got, oracle_full("w4a8", A, B, M, N, K))
+def test_skinny_kernel(torch, variant, M, N, K):
+    say(f"skinny {variant} {M}x{N}x{K}")
+    A, B = custom_operands(variant, M, N, K, seed=M * 3 + N)
+    got = run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_SKINNY)
+    assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
 
 
 # K above 8192 on the narrow-M kernel: equal K ranges, each summed into C by its
@@ -125,16 +126,17 @@ SKINNY_SPLIT = [(1, 257, 8224), (16, 1000, 16384), (13, 2049, 12320), (7, 100, 2
                 (16, 64, 131040), (16, 8192, 28672)]
 
 
+@pytest.mark.parametrize("variant", ["w4a8", "i4i4"])
 @pytest.mark.parametrize("M,N,K", SKINNY_SPLIT)
-def test_skinny_split_k(torch, M, N, K):
-    plan = L.lpgemm_plan(L.VARIANT_W4A8, M, N, K)
-    say(f"skinny split-K w4a8 {M}x{N}x{K} plan={plan}")
+def test_skinny_split_k(torch, variant, M, N, K):
+    plan = L.lpgemm_plan(L.VARIANT_W4A8 if variant == "w4a8" else L.VARIANT_I4I4, M, N, K)
+    say(f"skinny split-K {variant} {M}x{N}x{K} plan={plan}")
     assert plan["kernel"] == "skinny" and plan["k_chunks"] > 1
-    A, B = custom_operands("w4a8", M, N, K, seed=M * 7 + N + K)
-    got = run_gpu(torch, "w4a8", A, B, M, N, K)
-    assert np.array_equal(got, oracle_full("w4a8", A, B, M, N, K))
+    A, B = custom_operands(variant, M, N, K, seed=M * 7 + N + K)
+    got = run_gpu(torch, variant, A, B, M, N, K)
+    assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
     # a second call must not add onto the first (C is zeroed by the call itself)
-    assert np.array_equal(run_gpu(torch, "w4a8", A, B, M, N, K), got)
+    assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K), got)
 
 
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
@@ -177,6 +179,9 @@ def test_largest_k_closed_forms(torch, variant, K):
     if variant == "i4i4" and K % 32 == 0:
         # the FP6 path's fp32 accumulator holds 64 K < 2^24 exactly
         assert (run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_FP6) == want).all()
+    if K % 32 == 0:
+        # the narrow-M kernel over 16 K ranges added into C
+        assert (run_gpu(torch, variant, A[:16], B, 16, N, K, kernel=L.KERNEL_SKINNY) == want).all()
     # mixed signs: b = +7 in odd k, -8 in even k; a = -8 (i4i4) or 127 (w4a8)
     B2 = np.full((N, K // 2), 0x78, dtype=np.uint8)
     if variant == "i4i4":
@@ -188,6 +193,8 @@ def test_largest_k_closed_forms(torch, variant, K):
     assert (got2 == want2).all()
     if variant == "i4i4" and K % 32 == 0:
         assert (run_gpu(torch, variant, A, B2, M, N, K, kernel=L.KERNEL_FP6) == want2).all()
+    if K % 32 == 0:
+        assert (run_gpu(torch, variant, A[:16], B2, 16, N, K, kernel=L.KERNEL_SKINNY) == want2).all()
 
 
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])

@@ -124,13 +124,14 @@ def test_fp6_kernel(torch, fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("variant", ["w4a8", "i4i4"])
 @pytest.mark.parametrize("M,N,K", SKINNY)
-def test_skinny_kernel(torch, fmt, M, N, K):
-    say(f"scaled skinny {fmt} {M}x{N}x{K}")
-    A, B = custom_operands("w4a8", M, N, K, seed=M * 5 + N)
+def test_skinny_kernel(torch, variant, fmt, M, N, K):
+    say(f"scaled skinny {variant} {fmt} {M}x{N}x{K}")
+    A, B = custom_operands(variant, M, N, K, seed=M * 5 + N)
     sa, sb = scale_vector(N, 0, M), scale_vector(N, 1, N)
-    got = run_scaled(torch, "w4a8", A, B, sa, sb, M, N, K, fmt, kernel=L.KERNEL_SKINNY)
-    check(got, oracle.gemm_scaled("w4a8", A, B, sa, sb, M, N, K, FORMATS[fmt][1]))
+    got = run_scaled(torch, variant, A, B, sa, sb, M, N, K, fmt, kernel=L.KERNEL_SKINNY)
+    check(got, oracle.gemm_scaled(variant, A, B, sa, sb, M, N, K, FORMATS[fmt][1]))
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))

@@ -195,9 +195,10 @@ def test_forced_kernel_that_cannot_run_is_unsupported():
     try:
         L.lpgemm_set_kernel_override(L.KERNEL_SKINNY)
         with pytest.raises(L.LpgemmError) as e:
-            L.lpgemm_plan(L.VARIANT_I4I4, 8, 256, 256)
+            L.lpgemm_plan(L.VARIANT_I4I4, 17, 256, 256)   # M above 16
         assert e.value.status == L.ERR_UNSUPPORTED
         assert L.lpgemm_plan(L.VARIANT_W4A8, 8, 256, 256)["kernel"] == "skinny"
+        assert L.lpgemm_plan(L.VARIANT_I4I4, 8, 256, 256)["kernel"] == "skinny"
         L.lpgemm_set_kernel_override(L.KERNEL_TILED)
         with pytest.raises(L.LpgemmError):
             L.lpgemm_plan(L.VARIANT_W4A8, 8, 256, 34)
@@ -239,6 +240,14 @@ def test_narrow_m_limits():
     assert L.lpgemm_plan(L.VARIANT_W4A8, 17, 4096, 4096)["kernel"] == "tiled"   # M above 16
     # N * K / 2 must stay below 2^31 (32-bit buffer offsets)
     assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 65536, 65536)["kernel"] == "tiled"
+
+
+def test_narrow_m_takes_both_formats():
+    for v in (L.VARIANT_W4A8, L.VARIANT_I4I4):
+        p = L.lpgemm_plan(v, 16, 28672, 8192)
+        assert (p["kernel"], p["workgroups"], p["k_chunks"]) == ("skinny", 256, 1)
+        assert L.lpgemm_plan(v, 1, 8192, 28672)["k_chunks"] == 4
+        assert L.lpgemm_plan(v, 17, 28672, 8192)["kernel"] == "tiled"
 
 
 def test_narrow_m_split_k_plan():
