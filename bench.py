@@ -166,8 +166,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328105.1, "fetch_scale": 2.0, "write_kib": 363173.8,
-                  "write_scale": 1.0, "sources_sha256": "74fab3a7a8458c8d4a7ba97cc6ebd0a14351fb5ed975dec993ed97b7073e92f5"},
+    "i4i4_8192": {"fetch_kib": 328176.4, "fetch_scale": 2.0, "write_kib": 363653.1,
+                  "write_scale": 1.0, "sources_sha256": "8250825aba24c1b3e4496331fd4ca64cea109ee781909c4a379b3fbc1c76a23f"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",

@@ -34,15 +34,23 @@ namespace lpgemm {
 //     one wave (rotating) after the next iteration's barrier, so one barrier
 //     per strip suffices and C stores overlap the next strip's work.
 //
-// Split K (SPLIT, int32 output only): K longer than one workgroup's waves
-// cover is cut into ranges of kc; the grid is `chunks` equal groups of
-// workgroups, group c contracting k in [c kc, (c + 1) kc) for its share of the
-// strips (its A range loaded once), and every strip's sum is added into C,
-// zeroed beforehand, with int32 atomic adds -- exact and independent of order.
+// Row groups: M up to 64 is taken as ceil(M / 16) groups of 16 rows of A, each
+// by its own equal group of workgroups over all strips; workgroups b and
+// b + (a multiple of 8) run on one XCD, so the groups' reads of a strip after
+// the first are served by that XCD's L2 or the MALL.  Each group writes its
+// own rows of C.
 //
-// Requirements (checked on the host): M <= 16, K % 32 == 0, 16-byte aligned
+// Split K (SPLIT, int32 output only): K longer than one workgroup's waves
+// cover is cut into ranges of kc; every row group's workgroups are split again
+// into `chunks` equal sets, set c contracting k in [c kc, (c + 1) kc) for its
+// share of the strips (its A range loaded once), and every strip's sum is
+// added into C, zeroed beforehand, with int32 atomic adds -- exact and
+// independent of order.
+//
+// Requirements (checked on the host): M <= 64, K % 32 == 0, 16-byte aligned
 // bases, N * K / 2 < 2^31, KW * KSTEPS * 128 >= kc, kc % 32 == 0, at most 256
-// workgroups, a multiple of the number of K ranges.
+// workgroups, a multiple of (row groups x K ranges) with a multiple of 8
+// workgroups per set.
 template <int KW, int KSTEPS>
 struct SkinnyCfg {
     static constexpr int kBufBytes = KW * KSTEPS * 1024;  // one strip (16 rows x K/2 bytes, padded)
@@ -80,8 +88,12 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     const int strips = (N + 15) / 16;
     // This workgroup's K range [k0, k0 + klen) and its share of the strips.
     const int chunks = SPLIT ? (K + kc - 1) / kc : 1;
-    const int G = (int)gridDim.x / chunks;
-    const int chunk = SPLIT ? (int)blockIdx.x / G : 0;
+    const int mgroups = (M + 15) / 16;
+    const int G = (int)gridDim.x / (chunks * mgroups);  // workgroups per set
+    const int set = (int)blockIdx.x / G;
+    const int chunk = SPLIT ? set % chunks : 0;
+    const int m0 = 16 * (set / chunks);  // first row of A and C of this group
+    const int mrows = min(16, M - m0);
     const int k0 = chunk * kc;
     const int klen = SPLIT ? min(kc, K - k0) : K;
     const uint32_t ldb = (uint32_t)K / 2;           // row stride of B
@@ -101,12 +113,14 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     for (int j = 0; j < KSTEPS; ++j) {
         const int kl = k_begin + 128 * j + 32 * g;
         if constexpr (VAR == I4I4) {
-            const uint32_t off =
-                kl < klen ? (uint32_t)r16 * lda + (uint32_t)(k0 + kl) / 2 : kOutOfRange;
+            const uint32_t off = kl < klen && r16 < mrows
+                                     ? (uint32_t)(m0 + r16) * lda + (uint32_t)(k0 + kl) / 2
+                                     : kOutOfRange;
             unpack_chunk<true>(buffer_load16(rsrc_a, off), a_lo[j], a_hi[j]);
         } else {
-            const uint32_t off =
-                kl < klen ? (uint32_t)r16 * lda + (uint32_t)(k0 + kl) : kOutOfRange;
+            const uint32_t off = kl < klen && r16 < mrows
+                                     ? (uint32_t)(m0 + r16) * lda + (uint32_t)(k0 + kl)
+                                     : kOutOfRange;
             a_lo[j] = buffer_load16(rsrc_a, off);
             a_hi[j] = buffer_load16(rsrc_a, off == kOutOfRange ? kOutOfRange : off + 16);
         }
@@ -141,7 +155,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
         frag_off[t] = 16u * (uint32_t)(r16 * cpr + (col ^ (r16 & swz_mask)));
     }
 
-    int s = (int)blockIdx.x - chunk * G;
+    int s = (int)blockIdx.x - set * G;
     if (s >= strips) return;
     issue_strip(s, 0);
     int it = 0;
@@ -161,12 +175,12 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     i32x4 held_sum = {0, 0, 0, 0};
     auto put = [&](int n, const i32x4 &sum) {
         if constexpr (SPLIT)
-            atomic_add_row4(epi, r16, N, n, sum);
+            atomic_add_row4(epi, m0 + r16, N, n, sum);
         else
-            store_row4<OUT>(epi, r16, N, n, sum, pend_sa, pend_sb);
+            store_row4<OUT>(epi, m0 + r16, N, n, sum, pend_sa, pend_sb);
     };
     auto emit = [&](int n, const i32x4 &sum) {
-        if (r16 >= M) return;
+        if (r16 >= mrows) return;
         if (!kHold) {
             put(n, sum);
             return;
@@ -194,8 +208,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
         // the barrier above).
         const int sn = s + G;
         if (sn < strips) issue_strip(sn, b ^ 1);
-        if (OUT != OUT_I32 && wave == it % KW && r16 < M)
-            load_scales<OUT>(epi, r16, N, s * 16 + 4 * g, pend_sa, pend_sb);
+        if (OUT != OUT_I32 && wave == it % KW && r16 < mrows)
+            load_scales<OUT>(epi, m0 + r16, N, s * 16 + 4 * g, pend_sa, pend_sb);
 
         // Contract this wave's K slice of strip s.
         const uint8_t *buf = smem + b * Cfg::kBufBytes;
@@ -224,7 +238,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
         sum >>= kShift;
         emit(prev * 16 + 4 * g, sum);
     }
-    if (kHold && held && r16 < M) put(held_n, held_sum);
+    if (kHold && held && r16 < mrows) put(held_n, held_sum);
 }
 
 }  // namespace lpgemm

@@ -96,8 +96,15 @@ bool fp6_pays(int64_t K, int64_t tiles256, int cu_count)
 // (16 waves contract a strip faster than 8 with twice the steps each.)  Longer
 // K (int32 output) is cut into equal ranges of at most kSkinnyMaxK, a multiple
 // of 256, each taken by its own group of workgroups and added into C.
+// Up to kSkinnyMaxM rows run as row groups of 16 (each group's workgroups
+// stream every strip; the other groups' reads hit L2 / MALL).  The automatic
+// choice takes the kernel up to kSkinnyAutoM rows, and up to kSkinnyMaxM rows
+// when K needs several K ranges or 64-tiles would not fill the compute units
+// (measured: 32 x 8192 x 28672 107 -> 53 us, 32 x 4096 x 4096 20 -> 15 us; at
+// 48-64 x 28672 x 8192 the row groups lose to 64-tiles, 52-60 against 41-47 us).
 constexpr int kSkinnyKW = 16;
-constexpr int kSkinnyMaxM = 16;
+constexpr int kSkinnyMaxM = 64;
+constexpr int kSkinnyAutoM = 16;
 constexpr int kSkinnyMaxK = kSkinnyKW * 4 * 128;
 
 struct Plan {
@@ -139,7 +146,8 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
     if (k == LPGEMM_KERNEL_AUTO) {
         if (!fast_ok)
             k = LPGEMM_KERNEL_GENERAL;
-        else if (skinny_ok)
+        else if (skinny_ok && (M <= kSkinnyAutoM || K > kSkinnyMaxK ||
+                               ceil_div(M, 64) * ceil_div(N, 64) < cu_count))
             k = LPGEMM_KERNEL_SKINNY;
         else if (fp6_ok && M > kSmallM && fp6_pays(K, large_tiles, cu_count))
             k = LPGEMM_KERNEL_FP6;
@@ -213,7 +221,7 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         break;
     }
     case LPGEMM_KERNEL_SKINNY: {
-        p.tile_m = kSkinnyMaxM;
+        p.tile_m = 16;  // rows per group
         p.tile_n = 16;
         p.k_split = kSkinnyKW;
         p.threads = 64 * kSkinnyKW;
@@ -224,9 +232,15 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         p.kc = (int)kc;
         p.k_steps = (int)ceil_div(ceil_div(kc, kSkinnyKW), 128);  // 1..4
         while (p.k_steps & (p.k_steps - 1)) ++p.k_steps;           // 1, 2 or 4
-        const int64_t per_range = std::min<int64_t>(
-            ceil_div(N, 16), std::max<int64_t>(1, std::min(cu_count, 256) / chunks));
-        p.workgroups = chunks * per_range;
+        // sets of workgroups: row groups x K ranges; with several row groups a
+        // set's size is a multiple of 8 (when it has 8 or more), which keeps
+        // the sets that read one strip on one XCD
+        const int64_t mgroups = ceil_div(M, 16);
+        const int64_t sets = mgroups * chunks;
+        int64_t per_set = std::min<int64_t>(ceil_div(N, 16),
+                                            std::max<int64_t>(1, std::min(cu_count, 256) / sets));
+        if (mgroups > 1 && per_set >= 8) per_set -= per_set % 8;
+        p.workgroups = sets * per_set;
         break;
     }
     default:

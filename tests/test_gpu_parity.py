@@ -139,6 +139,31 @@ def test_skinny_split_k(torch, variant, M, N, K):
     assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K), got)
 
 
+# 17..64 rows on the narrow-M kernel (forced): row groups of 16, each over all
+# strips, and with K above 8192 also K ranges added into C
+SKINNY_ROWS = [(17, 100, 256), (32, 1000, 4096), (40, 257, 1056), (64, 2049, 8192),
+               (33, 700, 12320)]
+
+
+@pytest.mark.parametrize("variant", ["w4a8", "i4i4"])
+@pytest.mark.parametrize("M,N,K", SKINNY_ROWS)
+def test_skinny_row_groups(torch, variant, M, N, K):
+    say(f"skinny row groups {variant} {M}x{N}x{K}")
+    A, B = custom_operands(variant, M, N, K, seed=M * 11 + N + K)
+    got = run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_SKINNY)
+    assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
+
+
+@pytest.mark.parametrize("variant,M,N,K", [("w4a8", 32, 3000, 4096), ("i4i4", 64, 1000, 2048),
+                                           ("w4a8", 40, 2000, 12320)])
+def test_row_groups_automatic_choice(torch, variant, M, N, K):
+    plan = L.lpgemm_plan(L.VARIANT_W4A8 if variant == "w4a8" else L.VARIANT_I4I4, M, N, K)
+    say(f"automatic row groups {variant} {M}x{N}x{K} plan={plan}")
+    assert plan["kernel"] == "skinny"
+    A, B = custom_operands(variant, M, N, K, seed=M * 13 + N + K)
+    assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K), oracle_full(variant, A, B, M, N, K))
+
+
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
 def test_unaligned_operand_takes_general_path(torch, variant):
     M, N, K = 40, 72, 256
@@ -232,7 +257,7 @@ def test_deterministic_repeats(torch):
 
 # ---- the automatic tile choice: small M (one row of 64- or 128-tiles), and ------
 # ---- 64-tiles where 128-tiles would leave compute units idle --------------------
-AUTO_TILE = [("w4a8", 40, 3000, 2080, 64), ("i4i4", 17, 1000, 8192, 64),
+AUTO_TILE = [("w4a8", 40, 16400, 2080, 64), ("i4i4", 17, 16448, 1024, 64),
              ("w4a8", 24, 32868, 1024, 128), ("i4i4", 64, 65536, 8192, 128),
              ("w4a8", 100, 28700, 2048, 128), ("w4a8", 128, 65600, 512, 128),
              ("i4i4", 256, 8192, 2048, 64), ("w4a8", 520, 8200, 1024, 128)]

@@ -86,7 +86,7 @@ def check(got, want):
 SHAPES = [(1, 1, 2), (17, 33, 34), (37, 53, 96), (129, 255, 512), (300, 260, 1056),
           (513, 257, 288)]
 TILED = [(16, 64, 128), (129, 255, 512), (300, 260, 1056), (600, 700, 2080), (255, 129, 4096)]
-SKINNY = [(1, 31, 96), (7, 100, 1056), (16, 1000, 4096), (13, 257, 8192)]
+SKINNY = [(1, 31, 96), (7, 100, 1056), (16, 1000, 4096), (13, 257, 8192), (40, 300, 1024)]
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))

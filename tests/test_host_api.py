@@ -195,7 +195,7 @@ def test_forced_kernel_that_cannot_run_is_unsupported():
     try:
         L.lpgemm_set_kernel_override(L.KERNEL_SKINNY)
         with pytest.raises(L.LpgemmError) as e:
-            L.lpgemm_plan(L.VARIANT_I4I4, 17, 256, 256)   # M above 16
+            L.lpgemm_plan(L.VARIANT_I4I4, 65, 256, 256)   # M above 64
         assert e.value.status == L.ERR_UNSUPPORTED
         assert L.lpgemm_plan(L.VARIANT_W4A8, 8, 256, 256)["kernel"] == "skinny"
         assert L.lpgemm_plan(L.VARIANT_I4I4, 8, 256, 256)["kernel"] == "skinny"
@@ -237,9 +237,36 @@ def test_plan_grid_covers_the_output():
 def test_narrow_m_limits():
     assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 4096, 8192)["kernel"] == "skinny"
     assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 4096, 8192)["k_chunks"] == 1
-    assert L.lpgemm_plan(L.VARIANT_W4A8, 17, 4096, 4096)["kernel"] == "tiled"   # M above 16
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 17, 28672, 4096)["kernel"] == "tiled"  # M above 16, wide N
     # N * K / 2 must stay below 2^31 (32-bit buffer offsets)
     assert L.lpgemm_plan(L.VARIANT_W4A8, 16, 65536, 65536)["kernel"] == "tiled"
+
+
+def test_narrow_m_row_groups_when_forced():
+    # 17..64 rows: ceil(M / 16) groups of workgroups, each set a multiple of 8
+    L.lpgemm_set_kernel_override(L.KERNEL_SKINNY)
+    try:
+        def plan(M, N, K):
+            p = L.lpgemm_plan(L.VARIANT_W4A8, M, N, K)
+            return p["kernel"], p["k_chunks"], p["workgroups"]
+        assert plan(32, 28672, 8192) == ("skinny", 1, 256)      # 2 groups x 128
+        assert plan(48, 28672, 8192) == ("skinny", 1, 240)      # 3 groups x 80
+        assert plan(64, 28672, 8192) == ("skinny", 1, 256)      # 4 groups x 64
+        assert plan(64, 8192, 28672) == ("skinny", 4, 256)      # 4 groups x 4 ranges x 16
+        assert plan(20, 100, 512) == ("skinny", 1, 14)          # 2 groups x 7 strips
+    finally:
+        L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
+
+
+def test_narrow_m_row_groups_automatic_choice():
+    def kern(M, N, K, v=L.VARIANT_W4A8):
+        return L.lpgemm_plan(v, M, N, K)["kernel"]
+    assert kern(32, 4096, 4096) == "skinny"                       # 64 64-tiles < 256 CUs
+    assert kern(64, 14336, 4096, L.VARIANT_I4I4) == "skinny"      # 224 64-tiles
+    assert kern(32, 8192, 28672) == "skinny"                      # K in 4 ranges
+    assert kern(32, 28672, 8192) == "tiled"                       # 448 64-tiles, one range
+    assert kern(48, 16384, 8192, L.VARIANT_I4I4) == "tiled"       # 256 64-tiles
+    assert kern(65, 4096, 4096) == "tiled"                        # above 64 rows
 
 
 def test_narrow_m_takes_both_formats():
@@ -247,7 +274,7 @@ def test_narrow_m_takes_both_formats():
         p = L.lpgemm_plan(v, 16, 28672, 8192)
         assert (p["kernel"], p["workgroups"], p["k_chunks"]) == ("skinny", 256, 1)
         assert L.lpgemm_plan(v, 1, 8192, 28672)["k_chunks"] == 4
-        assert L.lpgemm_plan(v, 17, 28672, 8192)["kernel"] == "tiled"
+        assert L.lpgemm_plan(v, 17, 28672, 8192)["kernel"] == "tiled"   # 448 64-tiles
 
 
 def test_narrow_m_split_k_plan():
