@@ -227,6 +227,16 @@ __device__ __forceinline__ void store_row4(const Epilogue &e, int64_t m, int N, 
     }
 }
 
+// C[m][n + i] += v[i] for the columns that exist (int32 atomics, no return):
+// partial sums of K ranges, added into a C zeroed beforehand.
+__device__ __forceinline__ void atomic_add_row4(const Epilogue &e, int64_t m, int N, int n, i32x4 v)
+{
+    int32_t *row = static_cast<int32_t *>(e.out) + m * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (n + i < N) __hip_atomic_fetch_add(row + n + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // scale_a[m] (scaled formats; 0 otherwise).
 template <int OUT>
 __device__ __forceinline__ float load_scale_a(const Epilogue &e, int64_t m)

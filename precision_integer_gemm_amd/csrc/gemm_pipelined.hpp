@@ -34,8 +34,13 @@
 // renumbered so each XCD walks a compact band of C (shared A rows and B
 // columns in its L2).
 //
+// Split K (SPLIT, int32 output, one tile per workgroup): the grid is the tiles
+// times `chunks` K ranges of kc; workgroup b contracts range b / tiles of tile
+// b % tiles and adds its sums into C, zeroed beforehand, with int32 atomics.
+//
 // Requirements (checked on the host): K % 32 == 0, 16-byte aligned bases,
-// M, N < 2^31, K <= 131070.
+// M, N < 2^31, K <= 131070; with SPLIT kc % 256 == 0 and a grid of exactly
+// tiles x ranges.
 #pragma once
 
 #include "device_common.hpp"
@@ -76,11 +81,12 @@ __device__ __forceinline__ int lds_chunk(int row, int col)
     return row * CPR + (col ^ ((row / rows_per_256) % CPR));
 }
 
-template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, int OUT>
+template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, int OUT, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pipelined_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N,
-    int K, int tiles_m, int tiles_n, int xcds)
+    int K, int tiles_m, int tiles_n, int xcds, int kc)
 {
+    static_assert(!SPLIT || OUT == OUT_I32, "split K adds int32 partial sums");
     using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, STAGES>;
     static_assert(Cfg::kFits, "LDS ring does not fit in 160 KB");
     constexpr int RA = Cfg::RA, RB = Cfg::RB, CPR_A = Cfg::CPR_A, CPR_B = Cfg::CPR_B;
@@ -101,7 +107,17 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
 
     const uint32_t lda = (VAR == I4I4) ? (uint32_t)K / 2 : (uint32_t)K;  // global row bytes
     const uint32_t ldb = (VAR == FP8) ? (uint32_t)K : (uint32_t)K / 2;
-    const int ktiles = (K + BK - 1) / BK;
+    // This workgroup's K range [k0, k0 + klen) (all of K unless SPLIT), and its
+    // offset and length in bytes of an A row and a B row.
+    const int nblocks = tiles_m * tiles_n;
+    const int chunk = SPLIT ? (int)blockIdx.x / nblocks : 0;
+    const int k0 = chunk * kc;
+    const int klen = SPLIT ? min(kc, K - k0) : K;
+    const uint32_t a_k0 = (VAR == I4I4) ? (uint32_t)k0 / 2 : (uint32_t)k0;
+    const uint32_t b_k0 = (VAR == FP8) ? (uint32_t)k0 : (uint32_t)k0 / 2;
+    const uint32_t a_len = (VAR == I4I4) ? (uint32_t)klen / 2 : (uint32_t)klen;
+    const uint32_t b_len = (VAR == FP8) ? (uint32_t)klen : (uint32_t)klen / 2;
+    const int ktiles = (klen + BK - 1) / BK;
 
     // Per-lane source of each DMA instruction: tile row and 16-byte column.
     uint32_t a_off[NA], a_col[NA], b_off[NB], b_col[NB];
@@ -128,7 +144,6 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     // (workgroup b runs on XCD b % xcds) walks a contiguous range of tile
     // ids, taken in bands of 4 tile rows, which keeps the A rows and B columns
     // its workgroups share in that XCD's L2.
-    const int nblocks = tiles_m * tiles_n;
     const int whole = nblocks - nblocks % xcds;
     auto tile_origin = [&](int v, int &m0, int &n0) {
         int id = v;
@@ -142,7 +157,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
         n0 = (in_band / band_rows) * Cfg::BN;
     };
 
-    int v = blockIdx.x;
+    int v = (int)blockIdx.x - chunk * nblocks;
     int m0, n0;
     tile_origin(v, m0, n0);
     i32x4 rsrc_a, rsrc_b;
@@ -159,12 +174,12 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
         const uint32_t ka = (uint32_t)kt * RA, kb = (uint32_t)kt * RB;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            const uint32_t off = (ka + a_col[i] < lda) ? a_off[i] + ka : kOutOfRange;
+            const uint32_t off = (ka + a_col[i] < a_len) ? a_off[i] + a_k0 + ka : kOutOfRange;
             dma16(rsrc_a, off, base + (uint32_t)(wave * NA + i) * 1024u);
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const uint32_t off = (kb + b_col[i] < ldb) ? b_off[i] + kb : kOutOfRange;
+            const uint32_t off = (kb + b_col[i] < b_len) ? b_off[i] + b_k0 + kb : kOutOfRange;
             dma16(rsrc_b, off, base + Cfg::A_BYTES + (uint32_t)(wave * NB + i) * 1024u);
         }
     };
@@ -343,7 +358,10 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
                             const i32x4 c = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
                                                   acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
                                             Cfg::SHIFT;
-                            store_row4<OUT>(epi, m, N, n, c, sa[fm], sb[fn][rg]);
+                            if constexpr (SPLIT)
+                                atomic_add_row4(epi, m, N, n, c);
+                            else
+                                store_row4<OUT>(epi, m, N, n, c, sa[fm], sb[fn][rg]);
                         }
                     }
                 }

@@ -59,15 +59,6 @@ struct SkinnyCfg {
     static_assert(kLdsBytes <= 160 * 1024, "strip buffers exceed the LDS");
 };
 
-// C[m][n + i] += v[i] for the columns that exist (int32 atomics, no return).
-__device__ __forceinline__ void atomic_add_row4(const Epilogue &e, int64_t m, int N, int n, i32x4 v)
-{
-    int32_t *row = static_cast<int32_t *>(e.out) + m * N;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (n + i < N) __hip_atomic_fetch_add(row + n + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <int VAR, int KW, int KSTEPS, int OUT, bool SPLIT>
 __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N, int K,

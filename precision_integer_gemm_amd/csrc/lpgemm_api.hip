@@ -4,6 +4,7 @@
 #include "lpgemm.h"
 
 #include <atomic>
+#include <cmath>
 #include <mutex>
 
 #include "gemm_general.hpp"
@@ -52,8 +53,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 template <int VAR, int FM, int FN, int WM, int WN, int BK, int ST>
 struct TiledKernel {
     using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, ST>;
-    template <int OUT>
-    static void *fn() { return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, BK, ST, OUT>); }
+    template <int OUT, bool SPLIT = false>
+    static void *fn() { return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, BK, ST, OUT, SPLIT>); }
 };
 using I4Large = TiledKernel<I4I4, 4, 2, 2, 4, 256, 2>;
 using W8Large = TiledKernel<W4A8, 4, 2, 2, 4, 128, 2>;
@@ -83,6 +84,8 @@ constexpr int64_t kFp6MinK = 2048, kFp6LongK = 8192;
 // 64 x 65536 x 8192 int4 operands the FP6 path took 263 us against 80 us on
 // 64- or 128-tiles; with W4A8 64 x 65536 x 4096, 256-tiles 58 us against 48.
 constexpr int64_t kSmallM = 128;
+// Shortest K range of a split 64-tile call.
+constexpr int64_t kTiledMinRange = 1024;
 
 bool fp6_pays(int64_t K, int64_t tiles256, int cu_count)
 {
@@ -204,6 +207,35 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         p.tiles_n = (int)ceil_div(N, p.tile_n);
         p.workgroups = (int64_t)p.tiles_m * p.tiles_n;
         if (p.workgroups > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+        // Automatic 64-tiles too few for two per compute unit, with long K
+        // (int32 result): K ranges of at least kTiledMinRange, each added into
+        // C with int32 atomics, at most two workgroups per compute unit.  The
+        // atomics are costly (device-scope adds are not served by one XCD's
+        // L2: about 17 us per million, measured), so the number of ranges S
+        // follows a cost model fitted on MI355X: one range takes about
+        // 6 + 0.0024 K us, S ranges 10 + 0.0024 K / S + 1.67e-5 M N S us
+        // (zero fill, the longest range, the adds); S = 12 sqrt(K / (M N)),
+        // taken only when it predicts 20% less time.  Measured with S ranges
+        // against one: 128 x 2048 x 65536 (S = 8) 161.6 -> 76.5 us, 300 x 300 x
+        // 32768 (S = 19) 86.8 -> 68.7 us; without the model 64 x 28672 x 8192
+        // went 47 -> 117 us and 1024 x 1024 x 4096 23.5 -> 59.6 us.
+        if (k == LPGEMM_KERNEL_TILED && int_out && p.tile == 64 &&
+            p.workgroups < 2 * (int64_t)cu_count && K >= 2 * kTiledMinRange) {
+            const double mn = (double)M * (double)N;
+            int64_t chunks = std::llround(12.0 * std::sqrt((double)K / mn));
+            chunks = std::max<int64_t>(1, std::min<int64_t>(
+                chunks, std::min<int64_t>(ceil_div(2 * (int64_t)cu_count, p.workgroups),
+                                          K / kTiledMinRange)));
+            const double one = 6.0 + 2.4e-3 * (double)K;
+            const double split = 10.0 + 2.4e-3 * (double)K / (double)chunks + 1.67e-5 * mn * (double)chunks;
+            if (chunks > 1 && split < 0.8 * one) {
+                const int64_t kc = ceil_div(ceil_div(K, chunks), 256) * 256;
+                chunks = ceil_div(K, kc);
+                p.k_chunks = (int)chunks;
+                p.kc = (int)kc;
+                p.workgroups *= chunks;
+            }
+        }
         // Large tiles run one persistent workgroup per compute unit (their LDS
         // ring leaves room for one), each looping over tiles.
         if (p.tile == 256) p.workgroups = std::min<int64_t>(p.workgroups, cu_count);
@@ -257,7 +289,9 @@ lpgemm_status launched()
 
 // Launch a tiled configuration; the first launch on each device raises the
 // kernel's dynamic-LDS limit to the ring size (above the 64 KB default).
-template <class TK, int OUT>
+// SPLIT: the plan's K ranges, each added into C, which a fill kernel zeroes
+// first on the same stream.
+template <class TK, int OUT, bool SPLIT = false>
 lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Epilogue epi, int m,
                            int n, int k, hipStream_t stream)
 {
@@ -266,15 +300,23 @@ lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Ep
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERR_HIP;
     std::call_once(once[dev], [dev] {
-        attr_err[dev] = hipFuncSetAttribute(TK::template fn<OUT>(),
+        attr_err[dev] = hipFuncSetAttribute(TK::template fn<OUT, SPLIT>(),
                                             hipFuncAttributeMaxDynamicSharedMemorySize,
                                             TK::Cfg::LDS_BYTES);
     });
     if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
+    if (SPLIT) {
+        const int64_t count = (int64_t)m * n;
+        const int blocks = (int)std::min<int64_t>(ceil_div(count, 256), 65536);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream,
+                           static_cast<int32_t *>(epi.out), count);
+    }
     int tiles_m = p.tiles_m, tiles_n = p.tiles_n, xcds = kXcds;
-    void *args[] = {(void *)&a, (void *)&b, (void *)&epi, (void *)&m,       (void *)&n,
-                    (void *)&k, (void *)&tiles_m,        (void *)&tiles_n, (void *)&xcds};
-    const hipError_t e = hipLaunchKernel(TK::template fn<OUT>(), dim3((unsigned)p.workgroups),
+    int kc = SPLIT ? p.kc : k;
+    void *args[] = {(void *)&a,       (void *)&b,       (void *)&epi,  (void *)&m,
+                    (void *)&n,       (void *)&k,       (void *)&tiles_m, (void *)&tiles_n,
+                    (void *)&xcds,    (void *)&kc};
+    const hipError_t e = hipLaunchKernel(TK::template fn<OUT, SPLIT>(), dim3((unsigned)p.workgroups),
                                          dim3(TK::Cfg::kThreads), args, TK::Cfg::LDS_BYTES, stream);
     return e == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
 }
@@ -416,6 +458,14 @@ lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, 
         return launched();
     }
     case LPGEMM_KERNEL_TILED:
+        if constexpr (OUT == OUT_I32) {
+            if (p.k_chunks > 1) {  // K ranges on 64-tiles
+                if (p.tile != 64) return LPGEMM_ERR_INVALID_ARG;
+                return variant == LPGEMM_VARIANT_I4I4
+                           ? launch_tiled<I4Tiny, OUT, true>(p, a, b, epi, m, n, k, stream)
+                           : launch_tiled<W8Tiny, OUT, true>(p, a, b, epi, m, n, k, stream);
+            }
+        }
         if (variant == LPGEMM_VARIANT_I4I4)
             return p.tile == 256 ? launch_tiled<I4Large, OUT>(p, a, b, epi, m, n, k, stream)
                    : p.tile == 128 ? launch_tiled<I4Small, OUT>(p, a, b, epi, m, n, k, stream)

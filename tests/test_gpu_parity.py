@@ -164,6 +164,22 @@ def test_row_groups_automatic_choice(torch, variant, M, N, K):
     assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K), oracle_full(variant, A, B, M, N, K))
 
 
+# 64-tiles too few for two per compute unit with long K: K ranges added into C
+TILED_SPLIT = [("i4i4", 80, 512, 32768), ("w4a8", 300, 300, 32768), ("w4a8", 100, 700, 65536),
+               ("i4i4", 200, 100, 131040)]
+
+
+@pytest.mark.parametrize("variant,M,N,K", TILED_SPLIT)
+def test_tiled_split_k(torch, variant, M, N, K):
+    plan = L.lpgemm_plan(L.VARIANT_W4A8 if variant == "w4a8" else L.VARIANT_I4I4, M, N, K)
+    say(f"tiled split-K {variant} {M}x{N}x{K} plan={plan}")
+    assert (plan["kernel"], plan["tile_m"]) == ("tiled", 64) and plan["k_chunks"] > 1
+    A, B = custom_operands(variant, M, N, K, seed=M * 17 + N + K)
+    got = run_gpu(torch, variant, A, B, M, N, K)
+    assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
+    assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K), got)  # C zeroed per call
+
+
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
 def test_unaligned_operand_takes_general_path(torch, variant):
     M, N, K = 40, 72, 256
