@@ -232,4 +232,151 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     if (kHold && held && r16 < mrows) put(held_n, held_sum);
 }
 
+// Several K ranges without atomics (the scaled formats, whose rounded results
+// cannot be added): each workgroup contracts every range of its own strips in
+// turn (range by range), so no two workgroups share a strip and C needs
+// neither a zero fill nor atomic adds.  A of the next range is
+// loaded into a second register set while the last strip of the current range
+// is contracted; the sums of local strip j (at most KW per workgroup) are
+// accumulated across ranges by wave j and stored once, after the last range
+// (scaled formats too).  Grid: row groups x workgroups, as for one range.
+//
+// Requirements (checked on the host): as for gemm_skinny_kernel with SPLIT,
+// and at most KW strips per workgroup.
+template <int VAR, int KW, int OUT>
+__global__ __launch_bounds__(64 * KW) void gemm_skinny_seq_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N, int K,
+    int kc)
+{
+    static_assert(VAR == W4A8 || VAR == I4I4, "4-bit B with an int8 or int4 A");
+    constexpr int KSTEPS = 4;  // ranges are longer than 4096 k
+    constexpr int kShift = VAR == I4I4 ? 8 : 4;
+    using Cfg = SkinnyCfg<KW, KSTEPS>;
+    extern __shared__ __align__(1024) uint8_t smem[];
+    i32x4 *red = reinterpret_cast<i32x4 *>(smem + 2 * Cfg::kBufBytes);  // [2][KW][64]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+    const int strips = (N + 15) / 16;
+    const int chunks = (K + kc - 1) / kc;
+    const int mgroups = (M + 15) / 16;
+    const int G = (int)gridDim.x / mgroups;  // workgroups per row group
+    const int grp = (int)blockIdx.x / G;
+    const int m0 = 16 * grp;
+    const int mrows = min(16, M - m0);
+    const int s0 = (int)blockIdx.x - grp * G;
+    if (s0 >= strips) return;
+    const int nloc = (strips - s0 + G - 1) / G;  // this workgroup's strips s0, s0 + G, ...
+    const int items = chunks * nloc;             // item i: range i / nloc, local strip i % nloc
+
+    const uint32_t lda = VAR == I4I4 ? (uint32_t)K / 2 : (uint32_t)K;
+    const uint32_t ldb = (uint32_t)K / 2;
+    const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(A, (uint32_t)M * lda);
+    const i32x4 rsrc_b = make_rsrc(B, (uint32_t)N * ldb);
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+    const int k_begin = wave * (KSTEPS * 128);
+
+    auto range_len = [&](int c) { return min(kc, K - c * kc); };
+    // This wave's A fragments of range c (zeros past the range and past the group).
+    auto load_a = [&](int c, i32x4 (&lo)[KSTEPS], i32x4 (&hi)[KSTEPS]) {
+        const int k0 = c * kc, klen = range_len(c);
+#pragma unroll
+        for (int j = 0; j < KSTEPS; ++j) {
+            const int kl = k_begin + 128 * j + 32 * g;
+            const bool live = kl < klen && r16 < mrows;
+            if constexpr (VAR == I4I4) {
+                const uint32_t off = live ? (uint32_t)(m0 + r16) * lda + (uint32_t)(k0 + kl) / 2 : kOutOfRange;
+                unpack_chunk<true>(buffer_load16(rsrc_a, off), lo[j], hi[j]);
+            } else {
+                const uint32_t off = live ? (uint32_t)(m0 + r16) * lda + (uint32_t)(k0 + kl) : kOutOfRange;
+                lo[j] = buffer_load16(rsrc_a, off);
+                hi[j] = buffer_load16(rsrc_a, live ? off + 16 : kOutOfRange);
+            }
+        }
+    };
+    // Copy of range c of strip s into buffer b (layout as in gemm_skinny_kernel).
+    auto issue_item = [&](int c, int s, int b) {
+        const int cpr = range_len(c) / 32;
+        const int swz = (cpr % 16 == 0) ? 15 : 0;
+        const uint32_t base = (uint32_t)s * 16u * ldb + (uint32_t)(c * kc) / 2;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            const int q = (wave * KSTEPS + t) * 64 + lane;
+            const int row = q / cpr, slot = q % cpr;
+            const uint32_t off = row < 16 ? base + (uint32_t)row * ldb + 16u * (uint32_t)(slot ^ (row & swz))
+                                          : kOutOfRange;
+            dma16_nt(rsrc_b, off, lds0 + (uint32_t)b * Cfg::kBufBytes + (uint32_t)(wave * KSTEPS + t) * 1024u);
+        }
+    };
+    auto frag_offsets = [&](int c, uint32_t (&fo)[KSTEPS]) {
+        const int cpr = range_len(c) / 32;
+        const int swz = (cpr % 16 == 0) ? 15 : 0;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            int col = (k_begin + 128 * t) / 32 + g;
+            col = col < cpr ? col : cpr - 1;  // past the range: A is zero there
+            fo[t] = 16u * (uint32_t)(r16 * cpr + (col ^ (r16 & swz)));
+        }
+    };
+    i32x4 run = {0, 0, 0, 0};  // wave j: the sum so far of local strip j
+    // Wave j adds the partial tiles of item (c, j) to its sum and, after the
+    // last range, stores the strip.
+    auto reduce = [&](int item, int slot) {
+        const int c = item / nloc, j = item - c * nloc;
+        if (wave != j) return;
+        const i32x4 *rp = red + slot * KW * 64;
+#pragma unroll
+        for (int w = 0; w < KW; ++w) run += rp[w * 64 + lane];
+        if (c == chunks - 1 && r16 < mrows) {
+            const int n = (s0 + j * G) * 16 + 4 * g;
+            float sa = 0.f, sb[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (OUT != OUT_I32) load_scales<OUT>(epi, m0 + r16, N, n, sa, sb);
+            store_row4<OUT>(epi, m0 + r16, N, n, run >> kShift, sa, sb);
+        }
+    };
+
+    i32x4 a_lo[KSTEPS], a_hi[KSTEPS], n_lo[KSTEPS], n_hi[KSTEPS];
+    uint32_t fo[KSTEPS];
+    load_a(0, a_lo, a_hi);
+    frag_offsets(0, fo);
+    issue_item(0, s0, 0);
+    for (int i = 0; i < items; ++i) {
+        const int b = i & 1;
+        const int c = i / nloc;
+        wait_vmcnt<0>();
+        lds_barrier();  // item i is in buffer b; the partial tiles of item i - 1 in red[b ^ 1]
+        if (i > 0) {
+            reduce(i - 1, b ^ 1);
+            if (c != (i - 1) / nloc) {  // a new range: its A arrived with the wait above
+#pragma unroll
+                for (int t = 0; t < KSTEPS; ++t) {
+                    a_lo[t] = n_lo[t];
+                    a_hi[t] = n_hi[t];
+                }
+                frag_offsets(c, fo);
+            }
+        }
+        if (i + 1 < items) {
+            const int cn = (i + 1) / nloc;
+            issue_item(cn, s0 + ((i + 1) - cn * nloc) * G, b ^ 1);
+            if (cn != c) load_a(cn, n_lo, n_hi);
+        }
+        const uint8_t *buf = smem + b * Cfg::kBufBytes;
+        i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            const i32x4 q = *reinterpret_cast<const i32x4 *>(buf + fo[t]);
+            i32x4 b_lo, b_hi;
+            unpack_chunk<true>(q, b_lo, b_hi);
+            acc = mfma_16x16x64(b_lo, a_lo[t], acc);
+            acc = mfma_16x16x64(b_hi, a_hi[t], acc);
+        }
+        red[b * KW * 64 + wave * 64 + lane] = acc;
+    }
+    lds_barrier();  // the last item's partial tiles are written
+    reduce(items - 1, (items - 1) & 1);
+}
+
 }  // namespace lpgemm

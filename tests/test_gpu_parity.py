@@ -121,9 +121,10 @@ def test_skinny_kernel(torch, variant, M, N, K):
 
 
 # K above 8192 on the narrow-M kernel: equal K ranges, each summed into C by its
-# own group of workgroups (C zeroed first, int32 atomic adds)
+# own group of workgroups (C zeroed first, int32 atomic adds), or, when there
+# are enough strips, taken in turn by the workgroup that owns a strip
 SKINNY_SPLIT = [(1, 257, 8224), (16, 1000, 16384), (13, 2049, 12320), (7, 100, 28672),
-                (16, 64, 131040), (16, 8192, 28672)]
+                (16, 64, 131040), (16, 8192, 28672), (40, 4200, 12320), (3, 4100, 40000)]
 
 
 @pytest.mark.parametrize("variant", ["w4a8", "i4i4"])

@@ -147,6 +147,21 @@ def test_narrow_m_long_k_scaled(torch, fmt):
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("variant,M,N,K", [("w4a8", 16, 4100, 9216), ("i4i4", 5, 2050, 16448),
+                                           ("w4a8", 40, 4200, 12320)])
+def test_narrow_m_long_k_ranges_in_turn(torch, variant, fmt, M, N, K):
+    # enough strips: each workgroup takes every K range of its strips and
+    # stores the sum once, so a scaled result works too
+    v = L.VARIANT_W4A8 if variant == "w4a8" else L.VARIANT_I4I4
+    assert L.lpgemm_plan(v, M, N, K)["kernel"] == "skinny"
+    say(f"scaled narrow-M ranges in turn {variant} {fmt} {M}x{N}x{K}")
+    A, B = custom_operands(variant, M, N, K, seed=M + N + K)
+    sa, sb = scale_vector(92, 0, M), scale_vector(92, 1, N)
+    got = run_scaled(torch, variant, A, B, sa, sb, M, N, K, fmt)
+    check(got, oracle.gemm_scaled(variant, A, B, sa, sb, M, N, K, FORMATS[fmt][1]))
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
 def test_k_zero_gives_signed_zeros(torch, variant, fmt):
     say(f"scaled k0 {variant} {fmt}")

@@ -310,7 +310,7 @@ def test_narrow_m_split_k_plan():
     assert plan(16, 4096, 8224) == ("skinny", 2, 256)       # 2 ranges x min(256 strips, 128)
     assert plan(16, 8192, 28672) == ("skinny", 4, 256)      # 4 x 7168: 4 x 64 workgroups
     assert plan(1, 2048, 65536) == ("skinny", 8, 256)       # 128 strips, 32 workgroups per range
-    assert plan(16, 64, 131040) == ("skinny", 16, 64)       # 4 strips per range
+    assert plan(16, 64, 131040) == ("skinny", 16, 64)       # 4 strips: 16 ranges x 4, added into C
     assert plan(16, 100, 16384) == ("skinny", 2, 14)        # 7 strips per range
     assert plan(16, 8192, 28672, cu_count=304) == ("skinny", 4, 256)  # at most 256 workgroups
 
