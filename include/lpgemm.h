@@ -215,9 +215,12 @@ typedef enum lpgemm_kernel {
  * units, and either twice the compute units or K >= 8192 (there the
  * re-encoding pass costs less than the matrix cores save).  Up to 128 rows of
  * A it takes the tiled kernel with 128 x 128 or 64 x 64 tiles (B is read
- * once), or the narrow-M kernel for M <= 16, either format (with K > 8192 and an
- * int32 result, K is cut into ranges whose sums are added into C, which the
- * call zeroes first; scaled results with K > 8192 take the tiled kernel). */
+ * once), or the narrow-M kernel for M <= 16, either format, and up to 64 rows
+ * where the tiled kernel would have few workgroups.  With an int32 result and
+ * K > 8192 on the narrow-M kernel, or long K over few 64-tiles (chosen by a
+ * cost model), K is cut into ranges whose sums are added into C, which the call
+ * zeroes first; scaled results with K > 8192 take each range in turn inside one
+ * workgroup when there are enough strips, else the tiled kernel. */
 
 typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
 
@@ -229,14 +232,15 @@ typedef struct lpgemm_plan_info {
     int32_t k_split;       /* waves that split K inside one workgroup (skinny)   */
     int64_t workgroups;    /* workgroups launched                                */
     int32_t threads;       /* threads per workgroup                              */
-    int32_t k_chunks;      /* K ranges contracted by separate workgroup groups   */
-                           /* and added into C (skinny with K > 8192), else 1   */
+    int32_t k_chunks;      /* K ranges whose sums are added into C (narrow-M   */
+                           /* with K > 8192; 64-tiles with long K over few     */
+                           /* tiles), else 1                                   */
 } lpgemm_plan_info;
 
 /*
  * Fill *info with the kernel and launch shape a call with these arguments
- * would use, without touching the device (pointers are only inspected for
- * alignment).  `cu_count` is the number of compute units to plan for (0 =
+ * and an int32 result would use, without touching the device (pointers are
+ * only inspected for alignment).  `cu_count` is the number of compute units to plan for (0 =
  * 256, an MI355X).  Returns what the call would return for argument errors,
  * LPGEMM_ERR_UNSUPPORTED if a forced kernel cannot run this shape.
  */
