@@ -166,8 +166,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328431.4, "fetch_scale": 2.0, "write_kib": 362716.8,
-                  "write_scale": 1.0, "sources_sha256": "849678b62ace844732daa8d880da2fdced55cdbf4a20352eca12d227f3dd4db7"},
+    "i4i4_8192": {"fetch_kib": 328129.0, "fetch_scale": 2.0, "write_kib": 362581.7,
+                  "write_scale": 1.0, "sources_sha256": "257032c77f07e8dc676402e4aa91416ecff22635f1193f202e65b99a456db6f5"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",

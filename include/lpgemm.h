@@ -26,13 +26,14 @@
  * Conventions shared by every entry point
  *   - All data pointers are DEVICE pointers owned by the caller; the library
  *     keeps no pointer after the call returns.
- *   - Device memory: only the int4 x int4 FP6 path allocates.  Large int4 x
- *     int4 calls (LPGEMM_KERNEL_FP6, below) re-encode A and B into a
- *     temporary workspace of ((M+31)/32 + (N+31)/32) * ((K+63)/64) * 1536
- *     bytes, taken from a library-owned stream-ordered memory pool on the
- *     call's stream and returned to it on the same stream (the pool keeps the
- *     memory for reuse until the process ends).  If that allocation fails the
- *     call runs the int8 tiled kernel instead, with the same result.
+ *   - Device memory: two paths take a temporary workspace from a
+ *     library-owned stream-ordered memory pool on the call's stream and
+ *     return it on the same stream (the pool keeps the memory for reuse until
+ *     the process ends): large int4 x int4 calls (LPGEMM_KERNEL_FP6, below)
+ *     re-encode A and B into ((M+31)/32 + (N+31)/32) * ((K+63)/64) * 1536
+ *     bytes, and int32 calls split over S K ranges on 64 x 64 tiles keep
+ *     S * M * N int32 partial sums.  If that allocation fails the call runs
+ *     the int8 tiled kernel over all of K instead, with the same result.
  *   - Matrices are dense and row-major with no padding: A row stride is K/2
  *     bytes (packed) or K bytes (int8), B row stride K/2 bytes, C row stride
  *     N int32.
@@ -217,10 +218,12 @@ typedef enum lpgemm_kernel {
  * A it takes the tiled kernel with 128 x 128 or 64 x 64 tiles (B is read
  * once), or the narrow-M kernel for M <= 16, either format, and up to 64 rows
  * where the tiled kernel would have few workgroups.  With an int32 result and
- * K > 8192 on the narrow-M kernel, or long K over few 64-tiles (chosen by a
- * cost model), K is cut into ranges whose sums are added into C, which the call
- * zeroes first; scaled results with K > 8192 take each range in turn inside one
- * workgroup when there are enough strips, else the tiled kernel. */
+ * K > 8192 on the narrow-M kernel, K is cut into ranges whose sums are added
+ * into C, which the call zeroes first; scaled results with K > 8192 take each
+ * range in turn inside one workgroup when there are enough strips, else the
+ * tiled kernel.  With an int32 result, K >= 12288 and fewer 64 x 64 tiles than
+ * two per compute unit, the tiles are split over K ranges whose partial sums
+ * go to a workspace and are summed into C by a second kernel. */
 
 typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
 
@@ -232,9 +235,9 @@ typedef struct lpgemm_plan_info {
     int32_t k_split;       /* waves that split K inside one workgroup (skinny)   */
     int64_t workgroups;    /* workgroups launched                                */
     int32_t threads;       /* threads per workgroup                              */
-    int32_t k_chunks;      /* K ranges whose sums are added into C (narrow-M   */
-                           /* with K > 8192; 64-tiles with long K over few     */
-                           /* tiles), else 1                                   */
+    int32_t k_chunks;      /* K ranges contracted separately and summed into  */
+                           /* C (narrow-M with K > 8192; 64-tiles with long K */
+                           /* over few tiles), else 1                         */
 } lpgemm_plan_info;
 
 /*

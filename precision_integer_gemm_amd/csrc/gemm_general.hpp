@@ -78,6 +78,34 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t *__restrict__ C,
         C[i] = 0;
 }
 
+// C[i] = sum over c < slices of W[c * count + i]: the partial sums of K ranges
+// (exact in int32, any order).  Four elements per thread when count % 4 == 0
+// (16-byte aligned W and C), else one.
+__global__ __launch_bounds__(256) void sum_slices_kernel(const int32_t *__restrict__ W,
+                                                         int32_t *__restrict__ C, int64_t count,
+                                                         int slices)
+{
+    typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (count % 4 == 0) {
+        const i32x4v *w = reinterpret_cast<const i32x4v *>(W);
+        i32x4v *c4 = reinterpret_cast<i32x4v *>(C);
+        const int64_t n4 = count / 4;
+        for (int64_t i = t; i < n4; i += stride) {
+            i32x4v s = w[i];
+            for (int k = 1; k < slices; ++k) s += w[(int64_t)k * n4 + i];
+            c4[i] = s;
+        }
+    } else {
+        for (int64_t i = t; i < count; i += stride) {
+            int32_t s = W[i];
+            for (int k = 1; k < slices; ++k) s += W[(int64_t)k * count + i];
+            C[i] = s;
+        }
+    }
+}
+
 // packed[r][j] = (x[r][2j] & 0xF) | ((x[r][2j+1] & 0xF) << 4), one thread per
 // output byte (grid-stride over rows * K/2).
 __global__ __launch_bounds__(256) void pack_int4_kernel(const int8_t *__restrict__ logical,

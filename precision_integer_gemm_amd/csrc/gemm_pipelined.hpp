@@ -36,7 +36,8 @@
 //
 // Split K (SPLIT, int32 output, one tile per workgroup): the grid is the tiles
 // times `chunks` K ranges of kc; workgroup b contracts range b / tiles of tile
-// b % tiles and adds its sums into C, zeroed beforehand, with int32 atomics.
+// b % tiles and stores its sums into slice b / tiles of an M x N int32
+// workspace (epi.out), which a second kernel sums into C.
 //
 // Requirements (checked on the host): K % 32 == 0, 16-byte aligned bases,
 // M, N < 2^31, K <= 131070; with SPLIT kc % 256 == 0 and a grid of exactly
@@ -118,6 +119,9 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     const uint32_t a_len = (VAR == I4I4) ? (uint32_t)klen / 2 : (uint32_t)klen;
     const uint32_t b_len = (VAR == FP8) ? (uint32_t)klen : (uint32_t)klen / 2;
     const int ktiles = (klen + BK - 1) / BK;
+    // Where the tile's results go: C, or this range's workspace slice.
+    Epilogue epo = epi;
+    if (SPLIT) epo.out = static_cast<int32_t *>(epi.out) + (int64_t)chunk * M * N;
 
     // Per-lane source of each DMA instruction: tile row and 16-byte column.
     uint32_t a_off[NA], a_col[NA], b_off[NB], b_col[NB];
@@ -358,10 +362,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
                             const i32x4 c = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
                                                   acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
                                             Cfg::SHIFT;
-                            if constexpr (SPLIT)
-                                atomic_add_row4(epi, m, N, n, c);
-                            else
-                                store_row4<OUT>(epi, m, N, n, c, sa[fm], sb[fn][rg]);
+                            store_row4<OUT>(epo, m, N, n, c, sa[fm], sb[fn][rg]);
                         }
                     }
                 }

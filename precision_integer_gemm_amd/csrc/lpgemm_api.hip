@@ -84,8 +84,9 @@ constexpr int64_t kFp6MinK = 2048, kFp6LongK = 8192;
 // 64 x 65536 x 8192 int4 operands the FP6 path took 263 us against 80 us on
 // 64- or 128-tiles; with W4A8 64 x 65536 x 4096, 256-tiles 58 us against 48.
 constexpr int64_t kSmallM = 128;
-// Shortest K range of a split 64-tile call.
-constexpr int64_t kTiledMinRange = 1024;
+// Split 64-tile calls: K of at least kTiledSplitK, ranges of at least
+// kTiledMinRange.
+constexpr int64_t kTiledMinRange = 1024, kTiledSplitK = 12288;
 
 bool fp6_pays(int64_t K, int64_t tiles256, int cu_count)
 {
@@ -231,28 +232,26 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         p.tiles_n = (int)ceil_div(N, p.tile_n);
         p.workgroups = (int64_t)p.tiles_m * p.tiles_n;
         if (p.workgroups > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
-        // Automatic 64-tiles too few for two per compute unit, with long K
-        // (int32 result): K ranges of at least kTiledMinRange, each added into
-        // C with int32 atomics, at most two workgroups per compute unit.  The
-        // atomics are costly (device-scope adds are not served by one XCD's
-        // L2: about 17 us per million, measured), so the number of ranges S
-        // follows a cost model fitted on MI355X: one range takes about
-        // 6 + 0.0024 K us, S ranges 10 + 0.0024 K / S + 1.67e-5 M N S us
-        // (zero fill, the longest range, the adds); S = 12 sqrt(K / (M N)),
-        // taken only when it predicts 20% less time.  Measured with S ranges
-        // against one: 128 x 2048 x 65536 (S = 8) 161.6 -> 76.5 us, 300 x 300 x
-        // 32768 (S = 19) 86.8 -> 68.7 us; without the model 64 x 28672 x 8192
-        // went 47 -> 117 us and 1024 x 1024 x 4096 23.5 -> 59.6 us.
+        // Automatic 64-tiles too few for two per compute unit, with K of at
+        // least kTiledSplitK (int32 result): S K ranges of at least
+        // kTiledMinRange, each storing its partial tiles into its own M x N
+        // int32 workspace slice, summed into C by a second kernel; at most two
+        // workgroups per compute unit, S = 35 sqrt(K / (M N)) (the longest
+        // range against the slices' 2 S M N words).  Measured on MI355X, one
+        // range -> S ranges (W4A8): 128 x 8192 x 28672 113 -> 82 us (S = 2),
+        // 96 x 4096 x 14336 48 -> 40 us, 128 x 2048 x 65536 164 -> 53 us,
+        // 100 x 700 x 65536 163 -> 40 us, 200 x 100 x 131040 376 -> 53 us; at
+        // K = 8192 (130 x 1000) the workspace and the second kernel cost more
+        // (29 -> 38 us), hence the K bound.  Adding the ranges into C with
+        // int32 atomics instead costs about 17 us per million adds.
         if (k == LPGEMM_KERNEL_TILED && int_out && p.tile == 64 &&
-            p.workgroups < 2 * (int64_t)cu_count && K >= 2 * kTiledMinRange) {
+            p.workgroups < 2 * (int64_t)cu_count && K >= kTiledSplitK) {
             const double mn = (double)M * (double)N;
-            int64_t chunks = std::llround(12.0 * std::sqrt((double)K / mn));
-            chunks = std::max<int64_t>(1, std::min<int64_t>(
+            int64_t chunks = std::llround(35.0 * std::sqrt((double)K / mn));
+            chunks = std::max<int64_t>(2, std::min<int64_t>(
                 chunks, std::min<int64_t>(ceil_div(2 * (int64_t)cu_count, p.workgroups),
                                           K / kTiledMinRange)));
-            const double one = 6.0 + 2.4e-3 * (double)K;
-            const double split = 10.0 + 2.4e-3 * (double)K / (double)chunks + 1.67e-5 * mn * (double)chunks;
-            if (chunks > 1 && split < 0.8 * one) {
+            {
                 const int64_t kc = ceil_div(ceil_div(K, chunks), 256) * 256;
                 chunks = ceil_div(K, kc);
                 p.k_chunks = (int)chunks;
@@ -310,6 +309,33 @@ lpgemm_status launched()
     return hipGetLastError() == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
 }
 
+// Workspaces (the FP6 path's re-encoded operands, the split tiled path's
+// partial sums) come from one stream-ordered memory pool per
+// device, created on first use; freed blocks stay in the pool for reuse
+// (release threshold: never), so after the first calls an allocation costs no
+// driver round trip and never synchronizes.
+hipMemPool_t workspace_pool(int dev)
+{
+    static std::once_flag once[kMaxDevices];
+    static hipMemPool_t pools[kMaxDevices];
+    std::call_once(once[dev], [dev] {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        uint64_t keep = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        (void)hipGetLastError();
+        pools[dev] = pool;
+    });
+    return pools[dev];
+}
+
 // Launch a tiled configuration; the first launch on each device raises the
 // kernel's dynamic-LDS limit to the ring size (above the 64 KB default).
 // SPLIT: the plan's K ranges, each added into C, which a fill kernel zeroes
@@ -328,19 +354,37 @@ lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Ep
                                             TK::Cfg::LDS_BYTES);
     });
     if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
-    if (SPLIT) {
-        const int64_t count = (int64_t)m * n;
-        const int blocks = (int)std::min<int64_t>(ceil_div(count, 256), 65536);
-        hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream,
-                           static_cast<int32_t *>(epi.out), count);
-    }
     int tiles_m = p.tiles_m, tiles_n = p.tiles_n, xcds = kXcds;
     int kc = SPLIT ? p.kc : k;
-    void *args[] = {(void *)&a,       (void *)&b,       (void *)&epi,  (void *)&m,
+    void *ws = nullptr;
+    Epilogue e_gemm = epi;
+    const int64_t count = (int64_t)m * n;
+    if (SPLIT) {  // one int32 M x N slice per K range, from the stream-ordered pool
+        hipMemPool_t pool = workspace_pool(dev);
+        if (pool == nullptr ||
+            hipMallocFromPoolAsync(&ws, (size_t)(count * p.k_chunks * 4), pool, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            Plan one = p;  // no workspace: the same tiles over all of K
+            one.k_chunks = 1;
+            one.workgroups = (int64_t)p.tiles_m * p.tiles_n;
+            return launch_tiled<TK, OUT, false>(one, a, b, epi, m, n, k, stream);
+        }
+        e_gemm.out = ws;
+    }
+    void *args[] = {(void *)&a,       (void *)&b,       (void *)&e_gemm, (void *)&m,
                     (void *)&n,       (void *)&k,       (void *)&tiles_m, (void *)&tiles_n,
                     (void *)&xcds,    (void *)&kc};
-    const hipError_t e = hipLaunchKernel(TK::template fn<OUT, SPLIT>(), dim3((unsigned)p.workgroups),
-                                         dim3(TK::Cfg::kThreads), args, TK::Cfg::LDS_BYTES, stream);
+    hipError_t e = hipLaunchKernel(TK::template fn<OUT, SPLIT>(), dim3((unsigned)p.workgroups),
+                                   dim3(TK::Cfg::kThreads), args, TK::Cfg::LDS_BYTES, stream);
+    if (SPLIT) {
+        const int blocks = (int)std::min<int64_t>(ceil_div(count % 4 ? count : count / 4, 256), 4096);
+        hipLaunchKernelGGL(sum_slices_kernel, dim3(blocks), dim3(256), 0, stream,
+                           static_cast<const int32_t *>(ws), static_cast<int32_t *>(epi.out), count,
+                           p.k_chunks);
+        const hipError_t f = hipFreeAsync(ws, stream);
+        if (e == hipSuccess) e = f;
+        if (e == hipSuccess) e = hipGetLastError();
+    }
     return e == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
 }
 
@@ -413,31 +457,6 @@ lpgemm_status launch_skinny_steps(const Plan &p, const uint8_t *a, const uint8_t
     }
 }
 
-// The FP6 path's workspace comes from one stream-ordered memory pool per
-// device, created on first use; freed blocks stay in the pool for reuse
-// (release threshold: never), so after the first calls an allocation costs no
-// driver round trip and never synchronizes.
-hipMemPool_t fp6_pool(int dev)
-{
-    static std::once_flag once[kMaxDevices];
-    static hipMemPool_t pools[kMaxDevices];
-    std::call_once(once[dev], [dev] {
-        hipMemPoolProps props = {};
-        props.allocType = hipMemAllocationTypePinned;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t pool = nullptr;
-        if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
-            (void)hipGetLastError();
-            return;
-        }
-        uint64_t keep = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-        (void)hipGetLastError();
-        pools[dev] = pool;
-    });
-    return pools[dev];
-}
 
 // int4 x int4 on the FP6 matrix cores: re-encode A and B into a workspace,
 // multiply, release the workspace -- all on `stream`.  Without a workspace the
@@ -460,7 +479,7 @@ lpgemm_status launch_fp6(const Plan &p, const uint8_t *a, const uint8_t *b, Epil
 
     const int64_t bytes_a = (fp6_bytes(m, k) + 255) / 256 * 256;
     const int64_t bytes_b = fp6_bytes(n, k);
-    hipMemPool_t pool = fp6_pool(dev);
+    hipMemPool_t pool = workspace_pool(dev);
     void *ws = nullptr;
     if (pool == nullptr || hipMallocFromPoolAsync(&ws, (size_t)(bytes_a + bytes_b), pool, stream) != hipSuccess) {
         (void)hipGetLastError();

@@ -270,21 +270,22 @@ def test_narrow_m_row_groups_automatic_choice():
 
 
 def test_tiled_split_k_plan():
-    # automatic 64-tiles fewer than two per compute unit, K >= 2048: S = 12
-    # sqrt(K / (M N)) ranges (multiples of 256, at least 1024 k, at most two
-    # workgroups per compute unit) when the cost model predicts 20% less time
+    # automatic 64-tiles fewer than two per compute unit, K >= 12288: S = 35
+    # sqrt(K / (M N)) ranges (at least 2, multiples of 256, at least 1024 k, at
+    # most two workgroups per compute unit), each into its own workspace slice
     def plan(v, M, N, K):
         p = L.lpgemm_plan(v, M, N, K)
         return p["kernel"], p["tile_m"], p["k_chunks"], p["workgroups"]
-    assert plan(L.VARIANT_W4A8, 128, 2048, 65536) == ("tiled", 64, 6, 384)
-    assert plan(L.VARIANT_W4A8, 300, 300, 32768) == ("tiled", 64, 7, 175)
-    assert plan(L.VARIANT_I4I4, 80, 512, 32768) == ("tiled", 64, 11, 176)
-    # the adds would cost more than the shorter ranges save
-    assert plan(L.VARIANT_W4A8, 128, 8192, 28672) == ("tiled", 64, 1, 256)
-    assert plan(L.VARIANT_I4I4, 96, 4096, 14336) == ("tiled", 64, 1, 128)
-    assert plan(L.VARIANT_W4A8, 64, 28672, 8192) == ("tiled", 64, 1, 448)
+    assert plan(L.VARIANT_W4A8, 128, 8192, 28672) == ("tiled", 64, 2, 512)
+    assert plan(L.VARIANT_I4I4, 96, 4096, 14336) == ("tiled", 64, 4, 512)
+    assert plan(L.VARIANT_W4A8, 128, 2048, 65536) == ("tiled", 64, 8, 512)
+    assert plan(L.VARIANT_W4A8, 300, 300, 32768) == ("tiled", 64, 19, 475)
+    assert plan(L.VARIANT_I4I4, 200, 100, 131040) == ("tiled", 64, 64, 512)
+    # K below 12288, or enough tiles: one range
+    assert plan(L.VARIANT_I4I4, 130, 1000, 8192) == ("tiled", 64, 1, 48)
     assert plan(L.VARIANT_I4I4, 1024, 1024, 4096) == ("tiled", 64, 1, 256)
-    assert plan(L.VARIANT_I4I4, 200, 8192, 8192) == ("tiled", 64, 1, 512)    # enough tiles
+    assert plan(L.VARIANT_I4I4, 200, 8192, 8192) == ("tiled", 64, 1, 512)
+    assert plan(L.VARIANT_W4A8, 64, 28672, 8192) == ("tiled", 64, 1, 448)
     # a forced tile size never splits
     L.lpgemm_set_kernel_override(L.KERNEL_TILED_64)
     try:
