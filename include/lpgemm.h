@@ -31,8 +31,8 @@
  *     return it on the same stream (the pool keeps the memory for reuse until
  *     the process ends): large int4 x int4 calls (LPGEMM_KERNEL_FP6, below)
  *     re-encode A and B into ((M+31)/32 + (N+31)/32) * ((K+63)/64) * 1536
- *     bytes, and int32 calls split over S K ranges on 64 x 64 tiles keep
- *     S * M * N int32 partial sums.  If that allocation fails the call runs
+ *     bytes, and int32 calls split over S K ranges on 64 x 64 or 128 x 128
+ *     tiles keep S * M * N int32 partial sums.  If that allocation fails the call runs
  *     the int8 tiled kernel over all of K instead, with the same result.
  *   - Matrices are dense and row-major with no padding: A row stride is K/2
  *     bytes (packed) or K bytes (int8), B row stride K/2 bytes, C row stride
@@ -222,8 +222,9 @@ typedef enum lpgemm_kernel {
  * into C, which the call zeroes first; scaled results with K > 8192 take each
  * range in turn inside one workgroup when there are enough strips, else the
  * tiled kernel.  With an int32 result, K >= 12288 and fewer 64 x 64 tiles than
- * two per compute unit, the tiles are split over K ranges whose partial sums
- * go to a workspace and are summed into C by a second kernel. */
+ * two per compute unit (or fewer 128 x 128 tiles than two thirds of the
+ * compute units), the tiles are split over K ranges whose partial sums go to
+ * a workspace and are summed into C by a second kernel. */
 
 typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
 

@@ -84,8 +84,8 @@ constexpr int64_t kFp6MinK = 2048, kFp6LongK = 8192;
 // 64 x 65536 x 8192 int4 operands the FP6 path took 263 us against 80 us on
 // 64- or 128-tiles; with W4A8 64 x 65536 x 4096, 256-tiles 58 us against 48.
 constexpr int64_t kSmallM = 128;
-// Split 64-tile calls: K of at least kTiledSplitK, ranges of at least
-// kTiledMinRange.
+// Split 64-tile (and very few 128-tile) calls: K of at least kTiledSplitK,
+// ranges of at least kTiledMinRange.
 constexpr int64_t kTiledMinRange = 1024, kTiledSplitK = 12288;
 
 bool fp6_pays(int64_t K, int64_t tiles256, int cu_count)
@@ -243,8 +243,14 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         // 100 x 700 x 65536 163 -> 40 us, 200 x 100 x 131040 376 -> 53 us; at
         // K = 8192 (130 x 1000) the workspace and the second kernel cost more
         // (29 -> 38 us), hence the K bound.  Adding the ranges into C with
-        // int32 atomics instead costs about 17 us per million adds.
-        if (k == LPGEMM_KERNEL_TILED && int_out && p.tile == 64 &&
+        // int32 atomics instead costs about 17 us per million adds.  Automatic
+        // 128-tiles split only when fewer than two thirds of the compute units
+        // have one: 128 x 16384 x 28672 (128 tiles) 158 -> 99 us W4A8, 118 ->
+        // 92 us int4; 96 x 20000 x 16384 (157 tiles) 90 -> 76 us W4A8, even for
+        // int4; from 224 tiles on the single range is faster (100 x 28672 x
+        // 14336: 84 against 90 us).
+        const bool split_tile = p.tile == 64 || (p.tile == 128 && 3 * p.workgroups < 2 * (int64_t)cu_count);
+        if (k == LPGEMM_KERNEL_TILED && int_out && split_tile &&
             p.workgroups < 2 * (int64_t)cu_count && K >= kTiledSplitK) {
             const double mn = (double)M * (double)N;
             int64_t chunks = std::llround(35.0 * std::sqrt((double)K / mn));
@@ -523,7 +529,11 @@ lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, 
     }
     case LPGEMM_KERNEL_TILED:
         if constexpr (OUT == OUT_I32) {
-            if (p.k_chunks > 1) {  // K ranges on 64-tiles
+            if (p.k_chunks > 1) {  // K ranges on 64- or 128-tiles
+                if (p.tile == 128)
+                    return variant == LPGEMM_VARIANT_I4I4
+                               ? launch_tiled<I4Small, OUT, true>(p, a, b, epi, m, n, k, stream)
+                               : launch_tiled<W8Small, OUT, true>(p, a, b, epi, m, n, k, stream);
                 if (p.tile != 64) return LPGEMM_ERR_INVALID_ARG;
                 return variant == LPGEMM_VARIANT_I4I4
                            ? launch_tiled<I4Tiny, OUT, true>(p, a, b, epi, m, n, k, stream)

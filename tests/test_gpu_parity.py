@@ -181,6 +181,32 @@ def test_tiled_split_k(torch, variant, M, N, K):
     assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K), got)  # C zeroed per call
 
 
+# 128-tiles on fewer than two thirds of the compute units with long K: K ranges
+# into workspace slices.  M x N too large for the whole oracle product in
+# seconds: sampled elements, whole edge rows and columns, and every row sum.
+TILED_SPLIT_128 = [("i4i4", 128, 16384, 12288), ("w4a8", 96, 20000, 16384), ("i4i4", 72, 17000, 14016)]
+
+
+@pytest.mark.parametrize("variant,M,N,K", TILED_SPLIT_128)
+def test_tiled_split_k_128_tiles(torch, variant, M, N, K):
+    plan = L.lpgemm_plan(L.VARIANT_W4A8 if variant == "w4a8" else L.VARIANT_I4I4, M, N, K)
+    say(f"tiled split-K 128-tiles {variant} {M}x{N}x{K} plan={plan}")
+    assert (plan["kernel"], plan["tile_m"]) == ("tiled", 128) and plan["k_chunks"] > 1
+    A, B = custom_operands(variant, M, N, K, seed=M * 19 + N + K)
+    got = run_gpu(torch, variant, A, B, M, N, K)
+    rng = np.random.default_rng(M + N)
+    rows = np.array([0, 1, 63, 64, M - 2, M - 1])
+    cols = np.array([0, 127, 128, N // 2, N - 129, N - 1])
+    ms = np.concatenate([rng.integers(0, M, 8192), np.repeat(rows, N), np.tile(np.arange(M), len(cols))])
+    ns = np.concatenate([rng.integers(0, N, 8192), np.tile(np.arange(N), len(rows)), np.repeat(cols, M)])
+    at = oracle.gemm_i4i4_at if variant == "i4i4" else oracle.gemm_w4a8_at
+    assert np.array_equal(got[ms, ns], at(A, B, M, N, K, ms, ns))
+    a_log = _np_unpack(A) if variant == "i4i4" else A.astype(np.int64)
+    want_rows = a_log.astype(np.int64) @ _np_unpack(B).sum(axis=0, dtype=np.int64)
+    assert np.array_equal(got.astype(np.int64).sum(axis=1), want_rows)
+    assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K), got)  # C rebuilt per call
+
+
 @pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
 def test_unaligned_operand_takes_general_path(torch, variant):
     M, N, K = 40, 72, 256

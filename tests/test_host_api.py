@@ -286,6 +286,11 @@ def test_tiled_split_k_plan():
     assert plan(L.VARIANT_I4I4, 1024, 1024, 4096) == ("tiled", 64, 1, 256)
     assert plan(L.VARIANT_I4I4, 200, 8192, 8192) == ("tiled", 64, 1, 512)
     assert plan(L.VARIANT_W4A8, 64, 28672, 8192) == ("tiled", 64, 1, 448)
+    # automatic 128-tiles split only below two thirds of the compute units
+    assert plan(L.VARIANT_W4A8, 128, 16384, 28672) == ("tiled", 128, 4, 512)
+    assert plan(L.VARIANT_I4I4, 96, 20000, 16384) == ("tiled", 128, 3, 471)
+    assert plan(L.VARIANT_I4I4, 100, 28672, 14336) == ("tiled", 128, 1, 224)
+    assert plan(L.VARIANT_W4A8, 2048, 2048, 16384) == ("tiled", 128, 1, 256)
     # a forced tile size never splits
     L.lpgemm_set_kernel_override(L.KERNEL_TILED_64)
     try:
