@@ -166,8 +166,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328126.0, "fetch_scale": 2.0, "write_kib": 363268.5,
-                  "write_scale": 1.0, "sources_sha256": "8982465fc10426c6051111d0564c6e588803c483228eba28274dc44030403372"},
+    "i4i4_8192": {"fetch_kib": 328083.9, "fetch_scale": 2.0, "write_kib": 362950.6,
+                  "write_scale": 1.0, "sources_sha256": "77235a2a25fdbd427f87051efe3cc2410f86e735cacfe121d969b852ce0acec3"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",

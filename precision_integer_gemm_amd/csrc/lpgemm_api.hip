@@ -344,8 +344,10 @@ hipMemPool_t workspace_pool(int dev)
 
 // Launch a tiled configuration; the first launch on each device raises the
 // kernel's dynamic-LDS limit to the ring size (above the 64 KB default).
-// SPLIT: the plan's K ranges, each added into C, which a fill kernel zeroes
-// first on the same stream.
+// SPLIT: the plan's K ranges, each storing its partial tiles into its own
+// M x N int32 slice of a pool workspace; a second kernel sums the slices into
+// C and the workspace goes back to the pool on the same stream (without the
+// workspace, one range over all of K).
 template <class TK, int OUT, bool SPLIT = false>
 lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Epilogue epi, int m,
                            int n, int k, hipStream_t stream)
