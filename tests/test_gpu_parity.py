@@ -1,9 +1,8 @@
 """Bit-exact parity of the HIP kernels with the CPU oracle (needs an MI355X).
 
 Every case feeds the same seeded bytes to the GPU (through the C-ABI binding)
-and to the oracle, and compares every output element; the largest shape is
-compared on sampled elements plus full rows and columns, and through row sums.
-C sits between guard bands pre-filled with a sentinel, so a write outside
+and to the oracle, and compares every output element (the 8192^3 product
+included, against one oracle product computed per test module).  C sits between guard bands pre-filled with a sentinel, so a write outside
 [0, M) x [0, N) or an element left unwritten fails the test.
 """
 import sys
@@ -182,8 +181,8 @@ def test_tiled_split_k(torch, variant, M, N, K):
 
 
 # 128-tiles on fewer than two thirds of the compute units with long K: K ranges
-# into workspace slices.  M x N too large for the whole oracle product in
-# seconds: sampled elements, whole edge rows and columns, and every row sum.
+# into workspace slices; every element against the oracle (at most 3.2e10
+# multiply-adds, a fraction of a second on the host's cores)
 TILED_SPLIT_128 = [("i4i4", 128, 16384, 12288), ("w4a8", 96, 20000, 16384), ("i4i4", 72, 17000, 14016)]
 
 
@@ -194,16 +193,7 @@ def test_tiled_split_k_128_tiles(torch, variant, M, N, K):
     assert (plan["kernel"], plan["tile_m"]) == ("tiled", 128) and plan["k_chunks"] > 1
     A, B = custom_operands(variant, M, N, K, seed=M * 19 + N + K)
     got = run_gpu(torch, variant, A, B, M, N, K)
-    rng = np.random.default_rng(M + N)
-    rows = np.array([0, 1, 63, 64, M - 2, M - 1])
-    cols = np.array([0, 127, 128, N // 2, N - 129, N - 1])
-    ms = np.concatenate([rng.integers(0, M, 8192), np.repeat(rows, N), np.tile(np.arange(M), len(cols))])
-    ns = np.concatenate([rng.integers(0, N, 8192), np.tile(np.arange(N), len(rows)), np.repeat(cols, M)])
-    at = oracle.gemm_i4i4_at if variant == "i4i4" else oracle.gemm_w4a8_at
-    assert np.array_equal(got[ms, ns], at(A, B, M, N, K, ms, ns))
-    a_log = _np_unpack(A) if variant == "i4i4" else A.astype(np.int64)
-    want_rows = a_log.astype(np.int64) @ _np_unpack(B).sum(axis=0, dtype=np.int64)
-    assert np.array_equal(got.astype(np.int64).sum(axis=1), want_rows)
+    assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
     assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K), got)  # C rebuilt per call
 
 
@@ -345,33 +335,61 @@ def test_named_case_full_parity_fp6(torch, name):
     assert np.array_equal(got, oracle_full(c.variant, A, B, c.M, c.N, c.K))
 
 
-def _np_unpack(packed):
-    b = np.ascontiguousarray(packed).view(np.uint8)
-    lo = ((b << 4).astype(np.uint8)).view(np.int8) >> 4
-    hi = b.view(np.int8) >> 4
-    return np.stack([lo, hi], axis=-1).reshape(b.shape[0], -1)
+@pytest.fixture(scope="module")
+def largest_case():
+    # the 8192^3 int4 x int4 workload and its whole oracle product (5.5e11
+    # multiply-adds on the host's cores, computed once for the module)
+    c = CASES["i4i4_8192"]
+    A, B = operands(c)
+    say(f"case {c.name}: oracle product on {oracle.num_threads()} threads")
+    return c, A, B, oracle_full(c.variant, A, B, c.M, c.N, c.K)
 
 
 @pytest.mark.parametrize("kernel", [L.KERNEL_AUTO, L.KERNEL_TILED_256], ids=["auto-fp6", "int8-256"])
-def test_largest_case_sampled_rows_columns_and_row_sums(torch, kernel):
-    c = CASES["i4i4_8192"]
-    say(f"case {c.name}: sampled, kernel {kernel} plan={L.lpgemm_plan(L.VARIANT_I4I4, c.M, c.N, c.K)}")
-    A, B = operands(c)
+def test_largest_case_full_parity(torch, largest_case, kernel):
+    c, A, B, want = largest_case
+    say(f"case {c.name}: every element, kernel {kernel} "
+        f"plan={L.lpgemm_plan(L.VARIANT_I4I4, c.M, c.N, c.K)}")
     got = run_gpu(torch, c.variant, A, B, c.M, c.N, c.K, kernel=kernel)
-    rng = np.random.default_rng(2024)
-    # 8192 random elements, plus 8 whole rows and 8 whole columns (edges included)
-    ms = rng.integers(0, c.M, 8192)
-    ns = rng.integers(0, c.N, 8192)
-    rows = np.array([0, 1, 127, 128, 4095, 4096, c.M - 2, c.M - 1])
-    cols = np.array([0, 3, 255, 256, 5000, 8000, c.N - 4, c.N - 1])
-    ms = np.concatenate([ms, np.repeat(rows, c.N), np.tile(np.arange(c.M), len(cols))])
-    ns = np.concatenate([ns, np.tile(np.arange(c.N), len(rows)), np.repeat(cols, c.M)])
-    want = oracle.gemm_i4i4_at(A, B, c.M, c.N, c.K, ms, ns)
-    assert np.array_equal(got[ms, ns], want)
-    # every element through its row sum: sum_n C[m,n] = sum_k a(m,k) * sum_n b(n,k)
-    colsum_b = _np_unpack(B).astype(np.int64).sum(axis=0)
-    want_rows = _np_unpack(A).astype(np.int64) @ colsum_b
-    assert np.array_equal(got.astype(np.int64).sum(axis=1), want_rows)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+
+
+# The largest K with a single odd product per output next to partial sums of
+# up to 64 (K - 1) = 8386496: the fp32 accumulation of the FP6 path must keep
+# the low-order unit, wherever in K the odd product falls (first, middle, last
+# 64-k block; either lane half; either nibble).  The int8 kernels and the
+# general kernel are checked on the same operands.
+ODD_KERNELS = [("fp6", L.KERNEL_FP6, 64, 48), ("tiled256", L.KERNEL_TILED_256, 64, 48),
+               ("tiled64", L.KERNEL_TILED_64, 64, 48), ("skinny", L.KERNEL_SKINNY, 16, 48),
+               ("auto", L.KERNEL_AUTO, 64, 48)]
+
+
+@pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
+@pytest.mark.parametrize("name,kernel,M,N", ODD_KERNELS, ids=[k[0] for k in ODD_KERNELS])
+def test_largest_k_one_odd_term(torch, variant, name, kernel, M, N):
+    from closed_forms import odd_term_operands, odd_term_product
+    if kernel == L.KERNEL_FP6 and variant != "i4i4":
+        pytest.skip("the FP6 path serves int4 x int4 only")
+    K = L.MAX_K - L.MAX_K % 32
+    say(f"largest K one odd term {variant} {name} {M}x{N}x{K}")
+    A, B, p, q = odd_term_operands(variant, M, N, K)
+    want = odd_term_product(variant, K, p, q)
+    got = run_gpu(torch, variant, A, B, M, N, K, kernel=kernel)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (f"{len(bad)} mismatches, first at {bad[:4].tolist()}: "
+                           f"got {got[tuple(bad[0])]}, want {want[tuple(bad[0])]}")
+    if variant == "i4i4":
+        assert want.max() == 64 * K - 63 == 8386497
+
+
+def test_general_kernel_one_odd_term_at_max_k(torch):
+    from closed_forms import odd_term_operands, odd_term_product
+    K = L.MAX_K  # not a multiple of 32: the general kernel
+    say(f"general one odd term {K}")
+    A, B, p, q = odd_term_operands("i4i4", 12, 12, K)
+    got = run_gpu(torch, "i4i4", A, B, 12, 12, K)
+    assert np.array_equal(got, odd_term_product("i4i4", K, p, q))
 
 
 # ---- device pack / unpack ---------------------------------------------------------

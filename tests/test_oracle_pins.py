@@ -202,6 +202,23 @@ def test_closed_forms_constant_operands(K):
     assert (oracle.gemm_w4a8(np.ones((M, K), np.int8), _packed_const(N, K, 1), M, N, K) == K).all()
 
 
+@pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
+@pytest.mark.parametrize("K", [64, 256, 2080])
+def test_one_odd_term_closed_form(variant, K):
+    # extreme operands with a single 1 per row: 64 K - 144, or the odd 64 K - 63
+    # where the two positions meet (1024 K - 2184 / 1024 K - 1023 for W4A8);
+    # the GPU tests use the same family at the largest K
+    from closed_forms import odd_term_operands, odd_term_product
+    M, N = 13, 29
+    A, B, p, q = odd_term_operands(variant, M, N, K)
+    want = odd_term_product(variant, K, p, q)
+    assert (want[p[:, None] == q[None, :]] % 2 == 1).all() and (p[:, None] == q[None, :]).any()
+    fn = oracle.gemm_i4i4 if variant == "i4i4" else oracle.gemm_w4a8
+    assert np.array_equal(fn(A, B, M, N, K), want)
+    a_logical = np_unpack(A) if variant == "i4i4" else A
+    assert np.array_equal(np_gemm(a_logical, np_unpack(B)), want)
+
+
 def _identity_like_packed(N, K):
     # B[n][k] = 1 if n == k else 0
     logical = np.zeros((N, K), dtype=np.int8)
