@@ -288,18 +288,26 @@ def main() -> int:
         a = torch.from_numpy(np.ascontiguousarray(A).view(np.uint8)).to(dev)
         b = torch.from_numpy(B).to(dev)  # each workload owns its B copy
         C = torch.empty((c.M, c.N), dtype=torch.int32, device=dev)
-        fn = L.lib().lpgemm_int4_int4 if c.variant == "i4i4" else L.lib().lpgemm_w4a8
+        # the entry point with a caller-owned workspace, allocated here, outside
+        # the timed region (the FP6 path's re-encoded operands for 8192^3)
+        fn = L.lib().lpgemm_int4_int4_ws if c.variant == "i4i4" else L.lib().lpgemm_w4a8_ws
         variant = L.VARIANT_I4I4 if c.variant == "i4i4" else L.VARIANT_W4A8
-        plan = L.lpgemm_plan(variant, c.M, c.N, c.K, a.data_ptr(), b.data_ptr(), C.data_ptr())
-        work.append(dict(case=c, A=A, B=B, a=a, b=b, C=C, fn=fn, plan=plan))
+        nws = L.lpgemm_workspace_size(variant, c.M, c.N, c.K)
+        ws_t = torch.empty(nws + L.WORKSPACE_ALIGN, dtype=torch.uint8, device=dev)
+        ws = ws_t.data_ptr() + (-ws_t.data_ptr()) % L.WORKSPACE_ALIGN if nws else None
+        plan = L.lpgemm_plan(variant, c.M, c.N, c.K, a.data_ptr(), b.data_ptr(), C.data_ptr(),
+                             workspace_bytes=nws)
+        work.append(dict(case=c, A=A, B=B, a=a, b=b, C=C, fn=fn, plan=plan, ws=ws, nws=nws,
+                         ws_t=ws_t))
         print(f"# {name}: {c.variant} {c.M}x{c.N}x{c.K} plan {plan}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
     handle = stream.cuda_stream
 
-    def call(w):
+    def call(w, b=None):
         c = w["case"]
-        st = w["fn"](w["a"].data_ptr(), w["b"].data_ptr(), w["C"].data_ptr(), c.M, c.N, c.K, handle)
+        st = w["fn"](w["a"].data_ptr(), (b if b is not None else w["b"]).data_ptr(),
+                     w["C"].data_ptr(), c.M, c.N, c.K, w["ws"], w["nws"], handle)
         if st != L.OK:
             raise RuntimeError(f"{c.name}: {L.lpgemm_status_string(st)}")
 
@@ -359,11 +367,8 @@ def main() -> int:
             call(w)
             for j, (e0, e1) in enumerate(evs):
                 e0.record(stream)
-                st = w["fn"](w["a"].data_ptr(), copies[j % len(copies)].data_ptr(),
-                             w["C"].data_ptr(), c.M, c.N, c.K, handle)
+                call(w, copies[j % len(copies)])
                 e1.record(stream)
-                if st != L.OK:
-                    raise RuntimeError(f"{c.name}: {L.lpgemm_status_string(st)}")
             torch.cuda.synchronize()
             us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
             med = float(np.median(us))
@@ -405,7 +410,12 @@ def main() -> int:
             sa = torch.from_numpy(scale_vector(c.seed, 0, c.M)).to(dev)
             sb = torch.from_numpy(scale_vector(c.seed, 1, c.N)).to(dev)
             D = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
-            fn = L.lib().lpgemm_int4_int4_scaled if c.variant == "i4i4" else L.lib().lpgemm_w4a8_scaled
+            if c.variant == "i4i4":  # with the workspace (the FP6 path for 8192^3)
+                def fn(a_, b_, sa_, sb_, d_, o_, m_, n_, k_, h_, w=w):
+                    return L.lib().lpgemm_int4_int4_scaled_ws(a_, b_, sa_, sb_, d_, o_, m_, n_, k_,
+                                                              w["ws"], w["nws"], h_)
+            else:
+                fn = L.lib().lpgemm_w4a8_scaled
             copies = [w["b"]] + [w["b"].clone() for _ in range(2 if c.b_bytes > (64 << 20) else 0)]
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.isolated_reps)]

@@ -26,14 +26,14 @@
  * Conventions shared by every entry point
  *   - All data pointers are DEVICE pointers owned by the caller; the library
  *     keeps no pointer after the call returns.
- *   - Device memory: two paths take a temporary workspace from a
- *     library-owned stream-ordered memory pool on the call's stream and
- *     return it on the same stream (the pool keeps the memory for reuse until
- *     the process ends): large int4 x int4 calls (LPGEMM_KERNEL_FP6, below)
- *     re-encode A and B into ((M+31)/32 + (N+31)/32) * ((K+63)/64) * 1536
- *     bytes, and int32 calls split over S K ranges on 64 x 64 or 128 x 128
- *     tiles keep S * M * N int32 partial sums.  If that allocation fails the call runs
- *     the int8 tiled kernel over all of K instead, with the same result.
+ *   - The library never allocates device memory.  Two faster paths need
+ *     scratch memory, which only the "_ws" entry points take, from the
+ *     caller: large int4 x int4 calls (LPGEMM_KERNEL_FP6, below) re-encode A
+ *     and B into a workspace, and int32 calls with long K over few 64 x 64 or
+ *     128 x 128 tiles keep one M x N int32 slice of partial sums per K range.
+ *     lpgemm_workspace_size gives the bytes a call can use; with less (or
+ *     none, as in the entry points without "_ws") the call takes a path that
+ *     fits, with the same result.
  *   - Matrices are dense and row-major with no padding: A row stride is K/2
  *     bytes (packed) or K bytes (int8), B row stride K/2 bytes, C row stride
  *     N int32.
@@ -43,7 +43,8 @@
  *     execution surface at the caller's next synchronisation.
  *   - Argument checks happen on the host before any HIP call, so an invalid
  *     call touches no device state.
- *   - Calls are thread-safe.  Any alignment is accepted; 16-byte aligned
+ *   - Calls are thread-safe (lpgemm_set_kernel_override, a test hook,
+ *     acts on the calling thread only).  Any alignment is accepted; 16-byte aligned
  *     bases with K a multiple of 32 take the fast kernels, anything else a
  *     slower general kernel with the same results.
  *   - Exactness: the int8 kernels pre-scale 4-bit values by 16 inside int32,
@@ -111,6 +112,50 @@ lpgemm_status lpgemm_int4_int4(const void *A_packed, const void *B_packed, int32
 lpgemm_status lpgemm_w4a8(const int8_t *A, const uint8_t *B_packed, int32_t *C,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/* ---- caller-provided workspace -------------------------------------------- */
+
+/*
+ * Bytes of workspace that a call with these sizes can use: of
+ * lpgemm_int4_int4_ws / lpgemm_w4a8_ws (scaled == 0) or of
+ * lpgemm_int4_int4_scaled_ws (scaled == 1).  0 when the call's fastest path
+ * needs none.  Host only: no HIP call, no device access.  The planning
+ * assumes 16-byte aligned operands and `cu_count` compute units (0 = 256, an
+ * MI355X); a call on a device that plans differently still runs correctly
+ * with this workspace, taking only paths that fit in it.
+ *   variant   LPGEMM_VARIANT_I4I4 or LPGEMM_VARIANT_W4A8 (declared below)
+ *   bytes     written with the size
+ * Returns LPGEMM_ERR_INVALID_ARG for a null `bytes`, an unknown variant,
+ * `scaled` other than 0 or 1, or sizes the GEMM calls reject as invalid;
+ * LPGEMM_ERR_UNSUPPORTED for K above LPGEMM_MAX_K.
+ */
+typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
+
+lpgemm_status lpgemm_workspace_size(lpgemm_variant variant, int32_t scaled, int64_t M, int64_t N,
+                                    int64_t K, int32_t cu_count, size_t *bytes);
+
+/*
+ * lpgemm_int4_int4 / lpgemm_w4a8 with a caller-owned workspace:
+ *   workspace        device memory, 256-byte aligned, or NULL
+ *   workspace_bytes  its size in bytes (0 with NULL)
+ * The library uses the workspace during the call's kernels on `stream` only
+ * (the caller must not reuse it until the call's work on `stream` has
+ * finished, and two calls in flight at once need two workspaces); nothing
+ * has to be initialised and its contents afterwards are unspecified.  With
+ * workspace_bytes >= lpgemm_workspace_size(...) the call takes the fastest
+ * path for its shape; with less it takes the fastest path that fits (the FP6
+ * path needs the whole re-encoding, K ranges are cut to the slices that fit).
+ * Results are identical whatever the workspace.  Returns
+ * LPGEMM_ERR_INVALID_ARG for a NULL or misaligned workspace with
+ * workspace_bytes > 0, otherwise as the calls without workspace.
+ */
+lpgemm_status lpgemm_int4_int4_ws(const void *A_packed, const void *B_packed, int32_t *C,
+                                  int64_t M, int64_t N, int64_t K, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+lpgemm_status lpgemm_w4a8_ws(const int8_t *A, const uint8_t *B_packed, int32_t *C, int64_t M,
+                             int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* ---- per-channel scaled output ---------------------------------------------- */
 
 /* Element type of a scaled result. */
@@ -152,6 +197,17 @@ lpgemm_status lpgemm_int4_int4_scaled(const void *A_packed, const void *B_packed
 lpgemm_status lpgemm_w4a8_scaled(const int8_t *A, const uint8_t *B_packed, const float *scale_a,
                                  const float *scale_b, void *D, lpgemm_out_dtype out_dtype,
                                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * lpgemm_int4_int4_scaled with a caller-owned workspace (the FP6 path for
+ * large shapes), under the rules of lpgemm_int4_int4_ws.  The W4A8 scaled
+ * product has no path that uses a workspace.
+ */
+lpgemm_status lpgemm_int4_int4_scaled_ws(const void *A_packed, const void *B_packed,
+                                         const float *scale_a, const float *scale_b, void *D,
+                                         lpgemm_out_dtype out_dtype, int64_t M, int64_t N,
+                                         int64_t K, void *workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
 
 /*
  * fp8 GEMM (second workload):  C[m][n] = out( sum_k a(m,k) * b(n,k) )
@@ -213,7 +269,7 @@ typedef enum lpgemm_kernel {
     LPGEMM_KERNEL_AUTO = 0,      /* choose by shape and alignment (default)      */
     LPGEMM_KERNEL_GENERAL = 1,   /* any shape and alignment; slow                */
     LPGEMM_KERNEL_TILED = 2,     /* block-tiled MFMA kernel, tile size by shape   */
-    LPGEMM_KERNEL_SKINNY = 3,    /* narrow-M kernel (M <= 16) streaming B once   */
+    LPGEMM_KERNEL_SKINNY = 3,    /* narrow-M kernel (M <= 64) streaming B once   */
     LPGEMM_KERNEL_TILED_128 = 4, /* block-tiled, 128 x 128 output tiles          */
     LPGEMM_KERNEL_TILED_256 = 5, /* block-tiled, 256 x 256 output tiles          */
     LPGEMM_KERNEL_TILED_64 = 6,  /* block-tiled, 64 x 64 output tiles            */
@@ -221,9 +277,10 @@ typedef enum lpgemm_kernel {
                                  /* 256 x 256 tiles on the FP6 matrix cores       */
 } lpgemm_kernel;
 /* LPGEMM_KERNEL_AUTO picks FP6 for int4 x int4 when the fast path applies,
- * M > 128, K >= 2048, the 256 x 256 output tiles number at least the compute
- * units, and either twice the compute units or K >= 8192 (there the
- * re-encoding pass costs less than the matrix cores save).  Up to 128 rows of
+ * the call's workspace holds the re-encoded operands, M > 128, K >= 2048, the
+ * 256 x 256 output tiles number at least the compute units, and either twice
+ * the compute units or K >= 8192 (there the re-encoding pass costs less than
+ * the matrix cores save).  Up to 128 rows of
  * A it takes the tiled kernel with 128 x 128 or 64 x 64 tiles (B is read
  * once), or the narrow-M kernel for M <= 16, either format, and up to 64 rows
  * where the tiled kernel would have few workgroups.  With an int32 result and
@@ -233,9 +290,9 @@ typedef enum lpgemm_kernel {
  * tiled kernel.  With an int32 result, K >= 12288 and fewer 64 x 64 tiles than
  * two per compute unit (or fewer 128 x 128 tiles than two thirds of the
  * compute units), the tiles are split over K ranges whose partial sums go to
- * a workspace and are summed into C by a second kernel. */
-
-typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
+ * slices of the call's workspace (as many ranges as slices fit, none below
+ * two) and are summed into C by a second kernel.  LPGEMM_KERNEL_SKINNY serves
+ * up to 64 rows (row groups of 16). */
 
 /* How a call would be executed. */
 typedef struct lpgemm_plan_info {
@@ -246,26 +303,31 @@ typedef struct lpgemm_plan_info {
     int64_t workgroups;    /* workgroups launched                                */
     int32_t threads;       /* threads per workgroup                              */
     int32_t k_chunks;      /* K ranges contracted separately and summed into  */
-                           /* C (narrow-M with K > 8192; 64-tiles with long K */
-                           /* over few tiles), else 1                         */
+                           /* C (narrow-M with K > 8192; 64- or 128-tiles     */
+                           /* with long K over few tiles), else 1             */
+    int64_t workspace_bytes; /* workspace the call uses (0: none)             */
 } lpgemm_plan_info;
 
 /*
- * Fill *info with the kernel and launch shape a call with these arguments
- * and an int32 result would use, without touching the device (pointers are
- * only inspected for alignment).  `cu_count` is the number of compute units to plan for (0 =
- * 256, an MI355X).  Returns what the call would return for argument errors,
- * LPGEMM_ERR_UNSUPPORTED if a forced kernel cannot run this shape.
+ * Fill *info with the kernel and launch shape a call with these arguments,
+ * an int32 result and `workspace_bytes` of workspace (0: a call without
+ * workspace; SIZE_MAX: every path available) would use, without touching the
+ * device (pointers are only inspected for alignment).  `cu_count` is the
+ * number of compute units to plan for (0 = 256, an MI355X).  Returns what
+ * the call would return for argument errors, LPGEMM_ERR_UNSUPPORTED if a
+ * forced kernel cannot run this shape (LPGEMM_KERNEL_FP6 also without the
+ * workspace it needs).
  */
 lpgemm_status lpgemm_plan(lpgemm_variant variant, const void *A, const void *B, const void *C,
-                          int64_t M, int64_t N, int64_t K, int32_t cu_count,
-                          lpgemm_plan_info *info);
+                          int64_t M, int64_t N, int64_t K, size_t workspace_bytes,
+                          int32_t cu_count, lpgemm_plan_info *info);
 
 /*
- * Force a kernel for every later call in this process (LPGEMM_KERNEL_AUTO
- * restores the default).  A forced kernel that cannot serve a shape makes the
- * call return LPGEMM_ERR_UNSUPPORTED.  Returns LPGEMM_ERR_INVALID_ARG for an
- * unknown value.  Meant for tests and benchmarks.
+ * Force a kernel for the later calls made on the calling thread
+ * (LPGEMM_KERNEL_AUTO restores the default; other threads are not
+ * affected).  A forced kernel that cannot serve a shape makes the call return
+ * LPGEMM_ERR_UNSUPPORTED.  Returns LPGEMM_ERR_INVALID_ARG for an unknown
+ * value.  Meant for tests and benchmarks.
  */
 lpgemm_status lpgemm_set_kernel_override(lpgemm_kernel kernel);
 

@@ -16,4 +16,4 @@ from ._binding import (  # noqa: F401
     OK, OUT_BF16, OUT_F16, OUT_F32, OUT_FP8_E4M3, VARIANT_I4I4, VARIANT_W4A8, LpgemmError, lib,
     lpgemm_fp8_e4m3, lpgemm_int4_int4, lpgemm_int4_int4_scaled, lpgemm_pack_int4, lpgemm_plan,
     lpgemm_set_kernel_override, lpgemm_status_string, lpgemm_unpack_int4, lpgemm_w4a8,
-    lpgemm_w4a8_scaled)
+    lpgemm_w4a8_scaled, lpgemm_workspace_size, SIZE_MAX, WORKSPACE_ALIGN)

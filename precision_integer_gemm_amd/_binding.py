@@ -26,9 +26,13 @@ VARIANT_I4I4, VARIANT_W4A8 = 0, 1
 OUT_F32, OUT_BF16, OUT_F16, OUT_FP8_E4M3 = 0, 1, 2, 3
 MAX_K = 131070
 
-EXPORTS = ("lpgemm_int4_int4", "lpgemm_w4a8", "lpgemm_int4_int4_scaled", "lpgemm_w4a8_scaled",
-           "lpgemm_fp8_e4m3", "lpgemm_pack_int4", "lpgemm_unpack_int4", "lpgemm_status_string",
-           "lpgemm_plan", "lpgemm_set_kernel_override")
+EXPORTS = ("lpgemm_int4_int4", "lpgemm_w4a8", "lpgemm_int4_int4_ws", "lpgemm_w4a8_ws",
+           "lpgemm_workspace_size", "lpgemm_int4_int4_scaled", "lpgemm_w4a8_scaled",
+           "lpgemm_int4_int4_scaled_ws", "lpgemm_fp8_e4m3", "lpgemm_pack_int4",
+           "lpgemm_unpack_int4", "lpgemm_status_string", "lpgemm_plan",
+           "lpgemm_set_kernel_override")
+SIZE_MAX = 2 ** 64 - 1
+WORKSPACE_ALIGN = 256
 
 
 class LpgemmError(RuntimeError):
@@ -41,13 +45,13 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("k_split", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("threads", ctypes.c_int32),
-                ("k_chunks", ctypes.c_int32)]
+                ("k_chunks", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {"kernel": KERNEL_NAMES.get(self.kernel, self.kernel), "tile_m": self.tile_m,
                 "tile_n": self.tile_n, "k_split": self.k_split,
                 "workgroups": self.workgroups, "threads": self.threads,
-                "k_chunks": self.k_chunks}
+                "k_chunks": self.k_chunks, "workspace_bytes": self.workspace_bytes}
 
 
 _lib = None
@@ -63,14 +67,23 @@ def lib() -> ctypes.CDLL:
                           "`python -m precision_integer_gemm_amd.build` (or __graft_entry__.build())")
     L = ctypes.CDLL(LIB_PATH)
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    sz = ctypes.c_size_t
     for name in ("lpgemm_int4_int4", "lpgemm_w4a8"):
         f = getattr(L, name)
         f.argtypes = [p, p, p, i64, i64, i64, p]
         f.restype = ctypes.c_int
+    for name in ("lpgemm_int4_int4_ws", "lpgemm_w4a8_ws"):
+        f = getattr(L, name)
+        f.argtypes = [p, p, p, i64, i64, i64, p, sz, p]
+        f.restype = ctypes.c_int
+    L.lpgemm_workspace_size.argtypes = [ctypes.c_int, i32, i64, i64, i64, i32, ctypes.POINTER(sz)]
+    L.lpgemm_workspace_size.restype = ctypes.c_int
     for name in ("lpgemm_int4_int4_scaled", "lpgemm_w4a8_scaled"):
         f = getattr(L, name)
         f.argtypes = [p, p, p, p, p, ctypes.c_int, i64, i64, i64, p]
         f.restype = ctypes.c_int
+    L.lpgemm_int4_int4_scaled_ws.argtypes = [p, p, p, p, p, ctypes.c_int, i64, i64, i64, p, sz, p]
+    L.lpgemm_int4_int4_scaled_ws.restype = ctypes.c_int
     L.lpgemm_fp8_e4m3.argtypes = [p, p, p, ctypes.c_int, i64, i64, i64, p]
     L.lpgemm_fp8_e4m3.restype = ctypes.c_int
     for name in ("lpgemm_pack_int4", "lpgemm_unpack_int4"):
@@ -79,7 +92,7 @@ def lib() -> ctypes.CDLL:
         f.restype = ctypes.c_int
     L.lpgemm_status_string.argtypes = [ctypes.c_int]
     L.lpgemm_status_string.restype = ctypes.c_char_p
-    L.lpgemm_plan.argtypes = [ctypes.c_int, p, p, p, i64, i64, i64, i32, ctypes.POINTER(PlanInfo)]
+    L.lpgemm_plan.argtypes = [ctypes.c_int, p, p, p, i64, i64, i64, sz, i32, ctypes.POINTER(PlanInfo)]
     L.lpgemm_plan.restype = ctypes.c_int
     L.lpgemm_set_kernel_override.argtypes = [ctypes.c_int]
     L.lpgemm_set_kernel_override.restype = ctypes.c_int
@@ -97,13 +110,24 @@ def _raise(status: int, what: str) -> None:
 
 
 def lpgemm_plan(variant: int, M: int, N: int, K: int, A: int = 256, B: int = 256, C: int = 256,
-                cu_count: int = 0) -> dict:
+                cu_count: int = 0, workspace_bytes: int | None = None) -> dict:
     """Kernel and launch shape a call would use (host only; pointers are plain
-    integers, inspected only for alignment)."""
+    integers, inspected only for alignment).  workspace_bytes None: a call
+    given all the workspace it can use; 0: a call without workspace."""
     info = PlanInfo()
-    _raise(lib().lpgemm_plan(variant, A, B, C, M, N, K, cu_count, ctypes.byref(info)),
+    ws = SIZE_MAX if workspace_bytes is None else int(workspace_bytes)
+    _raise(lib().lpgemm_plan(variant, A, B, C, M, N, K, ws, cu_count, ctypes.byref(info)),
            "lpgemm_plan")
     return info.as_dict()
+
+
+def lpgemm_workspace_size(variant: int, M: int, N: int, K: int, scaled: bool = False,
+                          cu_count: int = 0) -> int:
+    """Bytes of workspace a "_ws" call with these sizes can use (host only)."""
+    n = ctypes.c_size_t(0)
+    _raise(lib().lpgemm_workspace_size(variant, int(bool(scaled)), M, N, K, cu_count,
+                                       ctypes.byref(n)), "lpgemm_workspace_size")
+    return int(n.value)
 
 
 def lpgemm_set_kernel_override(kernel: int) -> None:
@@ -136,6 +160,30 @@ def _check_dev(t, name: str, dtypes):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _workspace(workspace, variant, M, N, K, scaled, device):
+    """(pointer, bytes) of the workspace for a tensor-level call: "auto"
+    allocates what the call can use through PyTorch's allocator (none when the
+    call needs none), None passes none, a uint8 tensor on the device is used
+    as given (aligned to 256 bytes inside it)."""
+    torch = _torch()
+    if workspace is None:
+        return None, 0, None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a uint8 tensor')
+        n = lpgemm_workspace_size(variant, M, N, K, scaled=scaled)
+        if n == 0:
+            return None, 0, None
+        workspace = torch.empty(n + WORKSPACE_ALIGN, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or \
+            workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor on a GPU device")
+    base = workspace.data_ptr()
+    skip = (-base) % WORKSPACE_ALIGN
+    n = max(0, workspace.numel() - skip)
+    return (base + skip if n else None), n, workspace
+
+
 def _out(out, M, N, device):
     torch = _torch()
     if out is None:
@@ -146,8 +194,10 @@ def _out(out, M, N, device):
     return out
 
 
-def lpgemm_int4_int4(A_packed, B_packed, *, out=None, stream=None):
-    """C[M,N] int32 = A . B^T with both operands packed int4 ([M,K/2], [N,K/2])."""
+def lpgemm_int4_int4(A_packed, B_packed, *, out=None, workspace="auto", stream=None):
+    """C[M,N] int32 = A . B^T with both operands packed int4 ([M,K/2], [N,K/2]).
+    workspace: "auto" (allocated through PyTorch when the call can use one),
+    None (the entry point without workspace) or a uint8 device tensor."""
     torch = _torch()
     _check_dev(A_packed, "A_packed", (torch.int8, torch.uint8))
     _check_dev(B_packed, "B_packed", (torch.int8, torch.uint8))
@@ -156,13 +206,20 @@ def lpgemm_int4_int4(A_packed, B_packed, *, out=None, stream=None):
     if half != half_b:
         raise ValueError(f"packed K mismatch: A has {half} bytes per row, B {half_b}")
     C = _out(out, M, N, A_packed.device)
-    _raise(lib().lpgemm_int4_int4(A_packed.data_ptr(), B_packed.data_ptr(), C.data_ptr(),
-                                  M, N, 2 * half, _stream_handle(stream)), "lpgemm_int4_int4")
+    ws, nws, _keep = _workspace(workspace, VARIANT_I4I4, M, N, 2 * half, False, A_packed.device)
+    if nws:
+        _raise(lib().lpgemm_int4_int4_ws(A_packed.data_ptr(), B_packed.data_ptr(), C.data_ptr(),
+                                         M, N, 2 * half, ws, nws, _stream_handle(stream)),
+               "lpgemm_int4_int4_ws")
+    else:
+        _raise(lib().lpgemm_int4_int4(A_packed.data_ptr(), B_packed.data_ptr(), C.data_ptr(),
+                                      M, N, 2 * half, _stream_handle(stream)), "lpgemm_int4_int4")
     return C
 
 
-def lpgemm_w4a8(A, B_packed, *, out=None, stream=None):
-    """C[M,N] int32 = A . B^T with A int8 [M,K] and B packed int4 [N,K/2]."""
+def lpgemm_w4a8(A, B_packed, *, out=None, workspace="auto", stream=None):
+    """C[M,N] int32 = A . B^T with A int8 [M,K] and B packed int4 [N,K/2];
+    workspace as for lpgemm_int4_int4."""
     torch = _torch()
     _check_dev(A, "A", (torch.int8,))
     _check_dev(B_packed, "B_packed", (torch.uint8, torch.int8))
@@ -171,8 +228,13 @@ def lpgemm_w4a8(A, B_packed, *, out=None, stream=None):
     if K != 2 * half:
         raise ValueError(f"K mismatch: A has K={K}, B_packed holds {2 * half}")
     C = _out(out, M, N, A.device)
-    _raise(lib().lpgemm_w4a8(A.data_ptr(), B_packed.data_ptr(), C.data_ptr(), M, N, K,
-                             _stream_handle(stream)), "lpgemm_w4a8")
+    ws, nws, _keep = _workspace(workspace, VARIANT_W4A8, M, N, K, False, A.device)
+    if nws:
+        _raise(lib().lpgemm_w4a8_ws(A.data_ptr(), B_packed.data_ptr(), C.data_ptr(), M, N, K,
+                                    ws, nws, _stream_handle(stream)), "lpgemm_w4a8_ws")
+    else:
+        _raise(lib().lpgemm_w4a8(A.data_ptr(), B_packed.data_ptr(), C.data_ptr(), M, N, K,
+                                 _stream_handle(stream)), "lpgemm_w4a8")
     return C
 
 
@@ -204,8 +266,9 @@ def _check_scales(scale_a, scale_b, M, N):
 
 
 def lpgemm_int4_int4_scaled(A_packed, B_packed, scale_a, scale_b, *, dtype=None, out=None,
-                            stream=None):
-    """D[M,N] = out(((float)C * scale_a[m]) * scale_b[n]) of the int4 x int4 product C."""
+                            workspace="auto", stream=None):
+    """D[M,N] = out(((float)C * scale_a[m]) * scale_b[n]) of the int4 x int4 product C;
+    workspace as for lpgemm_int4_int4."""
     torch = _torch()
     _check_dev(A_packed, "A_packed", (torch.int8, torch.uint8))
     _check_dev(B_packed, "B_packed", (torch.int8, torch.uint8))
@@ -216,10 +279,19 @@ def lpgemm_int4_int4_scaled(A_packed, B_packed, scale_a, scale_b, *, dtype=None,
     _check_scales(scale_a, scale_b, M, N)
     dtype = dtype or (out.dtype if out is not None else torch.bfloat16)
     D = _scaled_out(out, dtype, M, N, A_packed.device)
-    _raise(lib().lpgemm_int4_int4_scaled(A_packed.data_ptr(), B_packed.data_ptr(),
-                                         scale_a.data_ptr(), scale_b.data_ptr(), D.data_ptr(),
-                                         _out_code(dtype), M, N, 2 * half, _stream_handle(stream)),
-           "lpgemm_int4_int4_scaled")
+    ws, nws, _keep = _workspace(workspace, VARIANT_I4I4, M, N, 2 * half, True, A_packed.device)
+    if nws:
+        _raise(lib().lpgemm_int4_int4_scaled_ws(A_packed.data_ptr(), B_packed.data_ptr(),
+                                                scale_a.data_ptr(), scale_b.data_ptr(),
+                                                D.data_ptr(), _out_code(dtype), M, N, 2 * half,
+                                                ws, nws, _stream_handle(stream)),
+               "lpgemm_int4_int4_scaled_ws")
+    else:
+        _raise(lib().lpgemm_int4_int4_scaled(A_packed.data_ptr(), B_packed.data_ptr(),
+                                             scale_a.data_ptr(), scale_b.data_ptr(), D.data_ptr(),
+                                             _out_code(dtype), M, N, 2 * half,
+                                             _stream_handle(stream)),
+               "lpgemm_int4_int4_scaled")
     return D
 
 

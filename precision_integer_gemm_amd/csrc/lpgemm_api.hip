@@ -3,7 +3,6 @@
 // contract are in include/lpgemm.h).
 #include "lpgemm.h"
 
-#include <atomic>
 #include <cmath>
 #include <mutex>
 
@@ -16,7 +15,8 @@ using namespace lpgemm;
 
 namespace {
 
-std::atomic<int> g_override{LPGEMM_KERNEL_AUTO};
+// Kernel forced by lpgemm_set_kernel_override for calls made on this thread.
+thread_local int t_override = LPGEMM_KERNEL_AUTO;
 
 constexpr int kDefaultCUs = 256;  // MI355X
 constexpr int kMaxDevices = 64;
@@ -120,7 +120,17 @@ struct Plan {
     bool k_seq = false;        // skinny: each workgroup takes every range of its strips
     int tiles_m = 0, tiles_n = 0;
     int tile = 0;  // tiled kernels: 256, 128 or 64 (square tiles)
+    int64_t ws_bytes = 0;  // workspace the launch uses (FP6 copies or K-range slices)
 };
+
+constexpr uint64_t kWsAlign = 256;  // workspace base alignment, and of the B copy inside it
+uint64_t align_ws(uint64_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Workspace of the FP6 path: A's FP6 copy (padded to kWsAlign), then B's.
+int64_t fp6_workspace(int64_t M, int64_t N, int64_t K)
+{
+    return (int64_t)align_ws((uint64_t)fp6_bytes(M, K)) + fp6_bytes(N, K);
+}
 
 lpgemm_status check_args(const void *A, const void *B, const void *C, int64_t M, int64_t N,
                          int64_t K)
@@ -158,9 +168,12 @@ bool skinny_seq_fits(int64_t M, int64_t N, int cu_count)
 }
 
 // int_out: the result is the int32 C (split K is available), not a scaled one.
+// ws_bytes: the workspace the caller provides; paths that need more are not
+// taken (a forced FP6 kernel is then unsupported), and K ranges are limited to
+// the slices that fit.
 lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, const void *C,
                         int64_t M, int64_t N, int64_t K, int cu_count, lpgemm_kernel forced,
-                        bool int_out, Plan *plan)
+                        bool int_out, uint64_t ws_bytes, Plan *plan)
 {
     const bool fast_ok = (K % 32 == 0) && aligned16(A) && aligned16(B) && aligned16(C);
     const bool skinny_ok = fast_ok && M <= kSkinnyMaxM &&
@@ -168,6 +181,7 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
                            N * (K / 2) < INT32_MAX;
 
     const bool fp6_ok = fast_ok && variant == LPGEMM_VARIANT_I4I4;
+    const bool fp6_ws = (uint64_t)fp6_workspace(M, N, K) <= ws_bytes;
     const int64_t large_tiles = ceil_div(M, 256) * ceil_div(N, 256);
 
     lpgemm_kernel k = forced;
@@ -177,7 +191,7 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         else if (skinny_ok && (M <= kSkinnyAutoM || K > kSkinnyMaxK ||
                                ceil_div(M, 64) * ceil_div(N, 64) < cu_count))
             k = LPGEMM_KERNEL_SKINNY;
-        else if (fp6_ok && M > kSmallM && fp6_pays(K, large_tiles, cu_count))
+        else if (fp6_ok && fp6_ws && M > kSmallM && fp6_pays(K, large_tiles, cu_count))
             k = LPGEMM_KERNEL_FP6;
         else
             k = LPGEMM_KERNEL_TILED;
@@ -185,7 +199,7 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
     const bool tiled = k == LPGEMM_KERNEL_TILED || k == LPGEMM_KERNEL_TILED_128 ||
                        k == LPGEMM_KERNEL_TILED_256 || k == LPGEMM_KERNEL_TILED_64;
     if ((tiled && !fast_ok) || (k == LPGEMM_KERNEL_SKINNY && !skinny_ok) ||
-        (k == LPGEMM_KERNEL_FP6 && !fp6_ok))
+        (k == LPGEMM_KERNEL_FP6 && !(fp6_ok && fp6_ws)))
         return LPGEMM_ERR_UNSUPPORTED;
 
     Plan p;
@@ -257,12 +271,16 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
             chunks = std::max<int64_t>(2, std::min<int64_t>(
                 chunks, std::min<int64_t>(ceil_div(2 * (int64_t)cu_count, p.workgroups),
                                           K / kTiledMinRange)));
-            {
-                const int64_t kc = ceil_div(ceil_div(K, chunks), 256) * 256;
-                chunks = ceil_div(K, kc);
+            // no more ranges than the workspace has slices for (none below two)
+            const uint64_t slice = (uint64_t)M * (uint64_t)N * 4u;
+            chunks = std::min<int64_t>(chunks, (int64_t)std::min<uint64_t>(ws_bytes / slice, 1u << 20));
+            const int64_t kc = ceil_div(ceil_div(K, std::max<int64_t>(chunks, 1)), 256) * 256;
+            chunks = ceil_div(K, kc);
+            if (chunks >= 2) {
                 p.k_chunks = (int)chunks;
                 p.kc = (int)kc;
                 p.workgroups *= chunks;
+                p.ws_bytes = (int64_t)(chunks * slice);
             }
         }
         // Large tiles run one persistent workgroup per compute unit (their LDS
@@ -279,6 +297,7 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         p.tiles_n = (int)ceil_div(N, Fp6Tile::BN);
         if ((int64_t)p.tiles_m * p.tiles_n > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
         p.workgroups = std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, cu_count);
+        p.ws_bytes = fp6_workspace(M, N, K);
         break;
     }
     case LPGEMM_KERNEL_SKINNY: {
@@ -315,42 +334,14 @@ lpgemm_status launched()
     return hipGetLastError() == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
 }
 
-// Workspaces (the FP6 path's re-encoded operands, the split tiled path's
-// partial sums) come from one stream-ordered memory pool per
-// device, created on first use; freed blocks stay in the pool for reuse
-// (release threshold: never), so after the first calls an allocation costs no
-// driver round trip and never synchronizes.
-hipMemPool_t workspace_pool(int dev)
-{
-    static std::once_flag once[kMaxDevices];
-    static hipMemPool_t pools[kMaxDevices];
-    std::call_once(once[dev], [dev] {
-        hipMemPoolProps props = {};
-        props.allocType = hipMemAllocationTypePinned;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t pool = nullptr;
-        if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
-            (void)hipGetLastError();
-            return;
-        }
-        uint64_t keep = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-        (void)hipGetLastError();
-        pools[dev] = pool;
-    });
-    return pools[dev];
-}
-
 // Launch a tiled configuration; the first launch on each device raises the
 // kernel's dynamic-LDS limit to the ring size (above the 64 KB default).
 // SPLIT: the plan's K ranges, each storing its partial tiles into its own
-// M x N int32 slice of a pool workspace; a second kernel sums the slices into
-// C and the workspace goes back to the pool on the same stream (without the
-// workspace, one range over all of K).
+// M x N int32 slice of the caller's workspace `ws`; a second kernel sums the
+// slices into C.
 template <class TK, int OUT, bool SPLIT = false>
 lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Epilogue epi, int m,
-                           int n, int k, hipStream_t stream)
+                           int n, int k, void *ws, hipStream_t stream)
 {
     static std::once_flag once[kMaxDevices];
     static hipError_t attr_err[kMaxDevices];
@@ -364,19 +355,10 @@ lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Ep
     if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
     int tiles_m = p.tiles_m, tiles_n = p.tiles_n, xcds = kXcds;
     int kc = SPLIT ? p.kc : k;
-    void *ws = nullptr;
     Epilogue e_gemm = epi;
     const int64_t count = (int64_t)m * n;
-    if (SPLIT) {  // one int32 M x N slice per K range, from the stream-ordered pool
-        hipMemPool_t pool = workspace_pool(dev);
-        if (pool == nullptr ||
-            hipMallocFromPoolAsync(&ws, (size_t)(count * p.k_chunks * 4), pool, stream) != hipSuccess) {
-            (void)hipGetLastError();
-            Plan one = p;  // no workspace: the same tiles over all of K
-            one.k_chunks = 1;
-            one.workgroups = (int64_t)p.tiles_m * p.tiles_n;
-            return launch_tiled<TK, OUT, false>(one, a, b, epi, m, n, k, stream);
-        }
+    if (SPLIT) {  // one int32 M x N slice per K range
+        if (ws == nullptr) return LPGEMM_ERR_INVALID_ARG;
         e_gemm.out = ws;
     }
     void *args[] = {(void *)&a,       (void *)&b,       (void *)&e_gemm, (void *)&m,
@@ -384,14 +366,12 @@ lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Ep
                     (void *)&xcds,    (void *)&kc};
     hipError_t e = hipLaunchKernel(TK::template fn<OUT, SPLIT>(), dim3((unsigned)p.workgroups),
                                    dim3(TK::Cfg::kThreads), args, TK::Cfg::LDS_BYTES, stream);
-    if (SPLIT) {
+    if (SPLIT && e == hipSuccess) {  // the slices hold partial sums only if the GEMM went out
         const int blocks = (int)std::min<int64_t>(ceil_div(count % 4 ? count : count / 4, 256), 4096);
         hipLaunchKernelGGL(sum_slices_kernel, dim3(blocks), dim3(256), 0, stream,
                            static_cast<const int32_t *>(ws), static_cast<int32_t *>(epi.out), count,
                            p.k_chunks);
-        const hipError_t f = hipFreeAsync(ws, stream);
-        if (e == hipSuccess) e = f;
-        if (e == hipSuccess) e = hipGetLastError();
+        e = hipGetLastError();
     }
     return e == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
 }
@@ -466,12 +446,11 @@ lpgemm_status launch_skinny_steps(const Plan &p, const uint8_t *a, const uint8_t
 }
 
 
-// int4 x int4 on the FP6 matrix cores: re-encode A and B into a workspace,
-// multiply, release the workspace -- all on `stream`.  Without a workspace the
-// same plan runs on the int8 256-tile kernel.
+// int4 x int4 on the FP6 matrix cores: re-encode A and B into the caller's
+// workspace `ws` (the plan's ws_bytes), then multiply -- all on `stream`.
 template <int OUT>
 lpgemm_status launch_fp6(const Plan &p, const uint8_t *a, const uint8_t *b, Epilogue epi, int m,
-                         int n, int k, hipStream_t stream)
+                         int n, int k, void *ws, hipStream_t stream)
 {
     constexpr auto kernel = &gemm_fp6_kernel<kFp6FM, kFp6FN, kFp6WM, kFp6WN, kFp6KS, kFp6Stages, OUT>;
     static std::once_flag once[kMaxDevices];
@@ -485,14 +464,8 @@ lpgemm_status launch_fp6(const Plan &p, const uint8_t *a, const uint8_t *b, Epil
     });
     if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
 
-    const int64_t bytes_a = (fp6_bytes(m, k) + 255) / 256 * 256;
-    const int64_t bytes_b = fp6_bytes(n, k);
-    hipMemPool_t pool = workspace_pool(dev);
-    void *ws = nullptr;
-    if (pool == nullptr || hipMallocFromPoolAsync(&ws, (size_t)(bytes_a + bytes_b), pool, stream) != hipSuccess) {
-        (void)hipGetLastError();
-        return launch_tiled<I4Large, OUT>(p, a, b, epi, m, n, k, stream);
-    }
+    if (ws == nullptr) return LPGEMM_ERR_INVALID_ARG;
+    const int64_t bytes_a = (int64_t)align_ws((uint64_t)fp6_bytes(m, k));
     uint8_t *a6 = static_cast<uint8_t *>(ws);
     uint8_t *b6 = a6 + bytes_a;
     const unsigned kgroups = (unsigned)ceil_div(ceil_div(k, 64), 32);
@@ -507,15 +480,14 @@ lpgemm_status launch_fp6(const Plan &p, const uint8_t *a, const uint8_t *b, Epil
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel),
                                          dim3((unsigned)p.workgroups), dim3(Fp6Tile::kThreads),
                                          args, Fp6Tile::LDS_BYTES, stream);
-    const hipError_t f = hipFreeAsync(ws, stream);
-    return (e == hipSuccess && f == hipSuccess && hipGetLastError() == hipSuccess) ? LPGEMM_OK
-                                                                                   : LPGEMM_ERR_HIP;
+    return (e == hipSuccess && hipGetLastError() == hipSuccess) ? LPGEMM_OK : LPGEMM_ERR_HIP;
 }
 
 // Launch the planned kernel for output format OUT.
 template <int OUT>
 lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, const void *B,
-                          Epilogue epi, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+                          Epilogue epi, int64_t M, int64_t N, int64_t K, void *ws,
+                          hipStream_t stream)
 {
     const uint8_t *a = static_cast<const uint8_t *>(A);
     const uint8_t *b = static_cast<const uint8_t *>(B);
@@ -534,23 +506,23 @@ lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, 
             if (p.k_chunks > 1) {  // K ranges on 64- or 128-tiles
                 if (p.tile == 128)
                     return variant == LPGEMM_VARIANT_I4I4
-                               ? launch_tiled<I4Small, OUT, true>(p, a, b, epi, m, n, k, stream)
-                               : launch_tiled<W8Small, OUT, true>(p, a, b, epi, m, n, k, stream);
+                               ? launch_tiled<I4Small, OUT, true>(p, a, b, epi, m, n, k, ws, stream)
+                               : launch_tiled<W8Small, OUT, true>(p, a, b, epi, m, n, k, ws, stream);
                 if (p.tile != 64) return LPGEMM_ERR_INVALID_ARG;
                 return variant == LPGEMM_VARIANT_I4I4
-                           ? launch_tiled<I4Tiny, OUT, true>(p, a, b, epi, m, n, k, stream)
-                           : launch_tiled<W8Tiny, OUT, true>(p, a, b, epi, m, n, k, stream);
+                           ? launch_tiled<I4Tiny, OUT, true>(p, a, b, epi, m, n, k, ws, stream)
+                           : launch_tiled<W8Tiny, OUT, true>(p, a, b, epi, m, n, k, ws, stream);
             }
         }
         if (variant == LPGEMM_VARIANT_I4I4)
-            return p.tile == 256 ? launch_tiled<I4Large, OUT>(p, a, b, epi, m, n, k, stream)
-                   : p.tile == 128 ? launch_tiled<I4Small, OUT>(p, a, b, epi, m, n, k, stream)
-                                   : launch_tiled<I4Tiny, OUT>(p, a, b, epi, m, n, k, stream);
-        return p.tile == 256 ? launch_tiled<W8Large, OUT>(p, a, b, epi, m, n, k, stream)
-               : p.tile == 128 ? launch_tiled<W8Small, OUT>(p, a, b, epi, m, n, k, stream)
-                               : launch_tiled<W8Tiny, OUT>(p, a, b, epi, m, n, k, stream);
+            return p.tile == 256 ? launch_tiled<I4Large, OUT>(p, a, b, epi, m, n, k, ws, stream)
+                   : p.tile == 128 ? launch_tiled<I4Small, OUT>(p, a, b, epi, m, n, k, ws, stream)
+                                   : launch_tiled<I4Tiny, OUT>(p, a, b, epi, m, n, k, ws, stream);
+        return p.tile == 256 ? launch_tiled<W8Large, OUT>(p, a, b, epi, m, n, k, ws, stream)
+               : p.tile == 128 ? launch_tiled<W8Small, OUT>(p, a, b, epi, m, n, k, ws, stream)
+                               : launch_tiled<W8Tiny, OUT>(p, a, b, epi, m, n, k, ws, stream);
     case LPGEMM_KERNEL_FP6:
-        return launch_fp6<OUT>(p, a, b, epi, m, n, k, stream);
+        return launch_fp6<OUT>(p, a, b, epi, m, n, k, ws, stream);
     case LPGEMM_KERNEL_SKINNY:
         return variant == LPGEMM_VARIANT_I4I4
                    ? launch_skinny_steps<I4I4, OUT>(p, a, b, epi, m, n, k, stream)
@@ -560,13 +532,23 @@ lpgemm_status launch_gemm(const Plan &p, lpgemm_variant variant, const void *A, 
     }
 }
 
+// Workspace arguments: none (nullptr, 0), or device memory aligned to kWsAlign.
+lpgemm_status check_workspace(const void *ws, size_t ws_bytes)
+{
+    if (ws_bytes == 0) return LPGEMM_OK;
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kWsAlign - 1))) return LPGEMM_ERR_INVALID_ARG;
+    return LPGEMM_OK;
+}
+
 // out_format: OUT_I32 for the plain entry points; scale pointers are used by
-// the scaled formats only.
+// the scaled formats only.  ws / ws_bytes: the caller's workspace (nullptr and
+// 0 for the entry points without one).
 lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, void *C,
                        const float *scale_a, const float *scale_b, int out_format, int64_t M,
-                       int64_t N, int64_t K, hipStream_t stream)
+                       int64_t N, int64_t K, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     lpgemm_status st = check_args(A, B, C, M, N, K);
+    if (st == LPGEMM_OK) st = check_workspace(ws, ws_bytes);
     if (st != LPGEMM_OK || M == 0 || N == 0) return st;
     if (out_format != OUT_I32) {
         if (scale_a == nullptr || scale_b == nullptr) return LPGEMM_ERR_INVALID_ARG;
@@ -590,20 +572,20 @@ lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, voi
         Plan p;
         p.kernel = LPGEMM_KERNEL_GENERAL;
         switch (out_format) {
-        case OUT_F32: return launch_gemm<OUT_F32>(p, variant, A, B, epi, M, N, K, stream);
-        case OUT_BF16: return launch_gemm<OUT_BF16>(p, variant, A, B, epi, M, N, K, stream);
-        default: return launch_gemm<OUT_F16>(p, variant, A, B, epi, M, N, K, stream);
+        case OUT_F32: return launch_gemm<OUT_F32>(p, variant, A, B, epi, M, N, K, nullptr, stream);
+        case OUT_BF16: return launch_gemm<OUT_BF16>(p, variant, A, B, epi, M, N, K, nullptr, stream);
+        default: return launch_gemm<OUT_F16>(p, variant, A, B, epi, M, N, K, nullptr, stream);
         }
     }
     Plan p;
-    st = make_plan(variant, A, B, C, M, N, K, device_cu_count(),
-                   (lpgemm_kernel)g_override.load(std::memory_order_relaxed), out_format == OUT_I32, &p);
+    st = make_plan(variant, A, B, C, M, N, K, device_cu_count(), (lpgemm_kernel)t_override,
+                   out_format == OUT_I32, ws_bytes, &p);
     if (st != LPGEMM_OK) return st;
     switch (out_format) {
-    case OUT_I32: return launch_gemm<OUT_I32>(p, variant, A, B, epi, M, N, K, stream);
-    case OUT_F32: return launch_gemm<OUT_F32>(p, variant, A, B, epi, M, N, K, stream);
-    case OUT_BF16: return launch_gemm<OUT_BF16>(p, variant, A, B, epi, M, N, K, stream);
-    default: return launch_gemm<OUT_F16>(p, variant, A, B, epi, M, N, K, stream);
+    case OUT_I32: return launch_gemm<OUT_I32>(p, variant, A, B, epi, M, N, K, ws, stream);
+    case OUT_F32: return launch_gemm<OUT_F32>(p, variant, A, B, epi, M, N, K, ws, stream);
+    case OUT_BF16: return launch_gemm<OUT_BF16>(p, variant, A, B, epi, M, N, K, ws, stream);
+    default: return launch_gemm<OUT_F16>(p, variant, A, B, epi, M, N, K, ws, stream);
     }
 }
 
@@ -617,7 +599,7 @@ lpgemm_status launch_fp8(const uint8_t *A, const uint8_t *B, void *C, int64_t M,
     const uintptr_t c_align = OUT == OUT_F32 ? 16u : 4u;
     const bool fast = K > 0 && K % 16 == 0 && aligned16(A) && aligned16(B) &&
                       (reinterpret_cast<uintptr_t>(C) & (c_align - 1)) == 0;
-    const int forced = g_override.load(std::memory_order_relaxed);
+    const int forced = t_override;
     if (forced == LPGEMM_KERNEL_SKINNY || forced == LPGEMM_KERNEL_FP6) return LPGEMM_ERR_UNSUPPORTED;
     const bool tiled_forced = forced == LPGEMM_KERNEL_TILED || forced == LPGEMM_KERNEL_TILED_128 ||
                               forced == LPGEMM_KERNEL_TILED_256 || forced == LPGEMM_KERNEL_TILED_64;
@@ -648,9 +630,9 @@ lpgemm_status launch_fp8(const uint8_t *A, const uint8_t *B, void *C, int64_t M,
     if (p.workgroups > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
     if (p.tile == 256) p.workgroups = std::min<int64_t>(p.workgroups, cu);
     const int m = (int)M, n = (int)N, k = (int)K;
-    return p.tile == 256 ? launch_tiled<F8Large, OUT>(p, A, B, epi, m, n, k, stream)
-           : p.tile == 128 ? launch_tiled<F8Small, OUT>(p, A, B, epi, m, n, k, stream)
-                           : launch_tiled<F8Tiny, OUT>(p, A, B, epi, m, n, k, stream);
+    return p.tile == 256 ? launch_tiled<F8Large, OUT>(p, A, B, epi, m, n, k, nullptr, stream)
+           : p.tile == 128 ? launch_tiled<F8Small, OUT>(p, A, B, epi, m, n, k, nullptr, stream)
+                           : launch_tiled<F8Tiny, OUT>(p, A, B, epi, m, n, k, nullptr, stream);
 }
 
 lpgemm_status run_fp8(const uint8_t *A, const uint8_t *B, void *C, lpgemm_out_dtype out_dtype,
@@ -706,14 +688,30 @@ lpgemm_status lpgemm_int4_int4(const void *A_packed, const void *B_packed, int32
                                int64_t N, int64_t K, hipStream_t stream)
 {
     return run_gemm(LPGEMM_VARIANT_I4I4, A_packed, B_packed, C, nullptr, nullptr, OUT_I32, M, N, K,
-                    stream);
+                    nullptr, 0, stream);
 }
 
 lpgemm_status lpgemm_w4a8(const int8_t *A, const uint8_t *B_packed, int32_t *C, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream)
 {
     return run_gemm(LPGEMM_VARIANT_W4A8, A, B_packed, C, nullptr, nullptr, OUT_I32, M, N, K,
-                    stream);
+                    nullptr, 0, stream);
+}
+
+lpgemm_status lpgemm_int4_int4_ws(const void *A_packed, const void *B_packed, int32_t *C, int64_t M,
+                                  int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream)
+{
+    return run_gemm(LPGEMM_VARIANT_I4I4, A_packed, B_packed, C, nullptr, nullptr, OUT_I32, M, N, K,
+                    workspace, workspace_bytes, stream);
+}
+
+lpgemm_status lpgemm_w4a8_ws(const int8_t *A, const uint8_t *B_packed, int32_t *C, int64_t M,
+                             int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream)
+{
+    return run_gemm(LPGEMM_VARIANT_W4A8, A, B_packed, C, nullptr, nullptr, OUT_I32, M, N, K,
+                    workspace, workspace_bytes, stream);
 }
 
 lpgemm_status lpgemm_int4_int4_scaled(const void *A_packed, const void *B_packed,
@@ -724,7 +722,18 @@ lpgemm_status lpgemm_int4_int4_scaled(const void *A_packed, const void *B_packed
     const int f = out_format_of(out_dtype);
     if (f < 0) return LPGEMM_ERR_INVALID_ARG;
     return run_gemm(LPGEMM_VARIANT_I4I4, A_packed, B_packed, D, scale_a, scale_b, f, M, N, K,
-                    stream);
+                    nullptr, 0, stream);
+}
+
+lpgemm_status lpgemm_int4_int4_scaled_ws(const void *A_packed, const void *B_packed,
+                                         const float *scale_a, const float *scale_b, void *D,
+                                         lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                                         void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const int f = out_format_of(out_dtype);
+    if (f < 0) return LPGEMM_ERR_INVALID_ARG;
+    return run_gemm(LPGEMM_VARIANT_I4I4, A_packed, B_packed, D, scale_a, scale_b, f, M, N, K,
+                    workspace, workspace_bytes, stream);
 }
 
 lpgemm_status lpgemm_w4a8_scaled(const int8_t *A, const uint8_t *B_packed, const float *scale_a,
@@ -733,7 +742,8 @@ lpgemm_status lpgemm_w4a8_scaled(const int8_t *A, const uint8_t *B_packed, const
 {
     const int f = out_format_of(out_dtype);
     if (f < 0) return LPGEMM_ERR_INVALID_ARG;
-    return run_gemm(LPGEMM_VARIANT_W4A8, A, B_packed, D, scale_a, scale_b, f, M, N, K, stream);
+    return run_gemm(LPGEMM_VARIANT_W4A8, A, B_packed, D, scale_a, scale_b, f, M, N, K, nullptr, 0,
+                    stream);
 }
 
 lpgemm_status lpgemm_fp8_e4m3(const uint8_t *A, const uint8_t *B, void *C,
@@ -767,8 +777,8 @@ const char *lpgemm_status_string(lpgemm_status status)
 }
 
 lpgemm_status lpgemm_plan(lpgemm_variant variant, const void *A, const void *B, const void *C,
-                          int64_t M, int64_t N, int64_t K, int32_t cu_count,
-                          lpgemm_plan_info *info)
+                          int64_t M, int64_t N, int64_t K, size_t workspace_bytes,
+                          int32_t cu_count, lpgemm_plan_info *info)
 {
     if (info == nullptr || (variant != LPGEMM_VARIANT_I4I4 && variant != LPGEMM_VARIANT_W4A8))
         return LPGEMM_ERR_INVALID_ARG;
@@ -778,7 +788,7 @@ lpgemm_status lpgemm_plan(lpgemm_variant variant, const void *A, const void *B, 
     if (M == 0 || N == 0 || K == 0) return LPGEMM_OK;  // nothing, or a zero fill
     Plan p;
     st = make_plan(variant, A, B, C, M, N, K, cu_count > 0 ? cu_count : kDefaultCUs,
-                   (lpgemm_kernel)g_override.load(std::memory_order_relaxed), true, &p);
+                   (lpgemm_kernel)t_override, true, workspace_bytes, &p);
     if (st != LPGEMM_OK) return st;
     info->kernel = p.kernel;
     info->tile_m = p.tile_m;
@@ -787,13 +797,33 @@ lpgemm_status lpgemm_plan(lpgemm_variant variant, const void *A, const void *B, 
     info->workgroups = p.workgroups;
     info->threads = p.threads;
     info->k_chunks = p.k_chunks;
+    info->workspace_bytes = p.ws_bytes;
+    return LPGEMM_OK;
+}
+
+lpgemm_status lpgemm_workspace_size(lpgemm_variant variant, int32_t scaled, int64_t M, int64_t N,
+                                    int64_t K, int32_t cu_count, size_t *bytes)
+{
+    if (bytes == nullptr || (variant != LPGEMM_VARIANT_I4I4 && variant != LPGEMM_VARIANT_W4A8) ||
+        (scaled != 0 && scaled != 1))
+        return LPGEMM_ERR_INVALID_ARG;
+    *bytes = 0;
+    // any 256-byte aligned addresses: the fast kernels' conditions on them hold
+    const void *dev = reinterpret_cast<const void *>(uintptr_t{256});
+    lpgemm_status st = check_args(dev, dev, dev, M, N, K);
+    if (st != LPGEMM_OK || M == 0 || N == 0 || K == 0) return st;
+    Plan p;
+    st = make_plan(variant, dev, dev, dev, M, N, K, cu_count > 0 ? cu_count : kDefaultCUs,
+                   LPGEMM_KERNEL_AUTO, scaled == 0, UINT64_MAX, &p);
+    if (st != LPGEMM_OK) return st;
+    *bytes = (size_t)p.ws_bytes;
     return LPGEMM_OK;
 }
 
 lpgemm_status lpgemm_set_kernel_override(lpgemm_kernel kernel)
 {
     if (kernel < LPGEMM_KERNEL_AUTO || kernel > LPGEMM_KERNEL_FP6) return LPGEMM_ERR_INVALID_ARG;
-    g_override.store(kernel, std::memory_order_relaxed);
+    t_override = kernel;
     return LPGEMM_OK;
 }
 

@@ -40,8 +40,19 @@ def _auto_kernel():
     L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
 
 
-def run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_AUTO, a_offset=0):
-    """Run one call through the C ABI; returns C as numpy and checks guards."""
+def workspace_for(torch, plan_bytes):
+    """A 256-byte aligned device workspace of plan_bytes (pointer, bytes, owner)."""
+    if plan_bytes == 0:
+        return None, 0, None
+    buf = torch.empty(plan_bytes + L.WORKSPACE_ALIGN, dtype=torch.uint8, device="cuda:0")
+    skip = (-buf.data_ptr()) % L.WORKSPACE_ALIGN
+    return buf.data_ptr() + skip, plan_bytes, buf
+
+
+def run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_AUTO, a_offset=0, workspace=None):
+    """Run one call through the C ABI; returns C as numpy and checks guards.
+    workspace None: the "_ws" entry point with the workspace its plan uses;
+    False: the entry point without workspace; an int: that many bytes."""
     dev = torch.device("cuda:0")
     a_t = torch.from_numpy(np.ascontiguousarray(A).view(np.uint8).reshape(-1)).to(dev)
     if a_offset:  # shift A to an unaligned address
@@ -52,9 +63,18 @@ def run_gpu(torch, variant, A, B, M, N, K, kernel=L.KERNEL_AUTO, a_offset=0):
     cbuf = torch.full((M * N + 2 * GUARD,), SENTINEL, dtype=torch.int32, device=dev)
     c_t = cbuf[GUARD:GUARD + M * N]
     L.lpgemm_set_kernel_override(kernel)
-    fn = L.lib().lpgemm_int4_int4 if variant == "i4i4" else L.lib().lpgemm_w4a8
-    st = fn(a_t.data_ptr(), b_t.data_ptr(), c_t.data_ptr(), M, N, K,
-            torch.cuda.current_stream().cuda_stream)
+    s = torch.cuda.current_stream().cuda_stream
+    if workspace is False:
+        fn = L.lib().lpgemm_int4_int4 if variant == "i4i4" else L.lib().lpgemm_w4a8
+        st = fn(a_t.data_ptr(), b_t.data_ptr(), c_t.data_ptr(), M, N, K, s)
+    else:
+        if workspace is None:
+            v = L.VARIANT_I4I4 if variant == "i4i4" else L.VARIANT_W4A8
+            workspace = L.lpgemm_plan(v, M, N, K, a_t.data_ptr(), b_t.data_ptr(),
+                                      c_t.data_ptr())["workspace_bytes"] if M and N and K else 0
+        ws, nws, _keep = workspace_for(torch, workspace)
+        fn = L.lib().lpgemm_int4_int4_ws if variant == "i4i4" else L.lib().lpgemm_w4a8_ws
+        st = fn(a_t.data_ptr(), b_t.data_ptr(), c_t.data_ptr(), M, N, K, ws, nws, s)
     assert st == L.OK, L.lpgemm_status_string(st)
     torch.cuda.synchronize()
     host = cbuf.cpu().numpy()
@@ -178,6 +198,9 @@ def test_tiled_split_k(torch, variant, M, N, K):
     got = run_gpu(torch, variant, A, B, M, N, K)
     assert np.array_equal(got, oracle_full(variant, A, B, M, N, K))
     assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K), got)  # C zeroed per call
+    # a workspace with room for two slices only (two ranges), and none (one range)
+    assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K, workspace=2 * M * N * 4), got)
+    assert np.array_equal(run_gpu(torch, variant, A, B, M, N, K, workspace=False), got)
 
 
 # 128-tiles on fewer than two thirds of the compute units with long K: K ranges
@@ -345,12 +368,15 @@ def largest_case():
     return c, A, B, oracle_full(c.variant, A, B, c.M, c.N, c.K)
 
 
-@pytest.mark.parametrize("kernel", [L.KERNEL_AUTO, L.KERNEL_TILED_256], ids=["auto-fp6", "int8-256"])
-def test_largest_case_full_parity(torch, largest_case, kernel):
+@pytest.mark.parametrize("kernel,ws", [(L.KERNEL_AUTO, None), (L.KERNEL_AUTO, False),
+                                       (L.KERNEL_TILED_256, None)],
+                         ids=["auto-fp6", "auto-no-workspace", "int8-256"])
+def test_largest_case_full_parity(torch, largest_case, kernel, ws):
     c, A, B, want = largest_case
-    say(f"case {c.name}: every element, kernel {kernel} "
-        f"plan={L.lpgemm_plan(L.VARIANT_I4I4, c.M, c.N, c.K)}")
-    got = run_gpu(torch, c.variant, A, B, c.M, c.N, c.K, kernel=kernel)
+    L.lpgemm_set_kernel_override(kernel)
+    say(f"case {c.name}: every element, kernel {kernel} workspace {ws} "
+        f"plan={L.lpgemm_plan(L.VARIANT_I4I4, c.M, c.N, c.K, workspace_bytes=0 if ws is False else None)}")
+    got = run_gpu(torch, c.variant, A, B, c.M, c.N, c.K, kernel=kernel, workspace=ws)
     bad = np.argwhere(got != want)
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
 
@@ -411,9 +437,8 @@ def test_device_pack_unpack_match_oracle(torch):
 
 
 def test_fp6_workspace_on_two_streams(torch):
-    # Two FP6-path calls in flight on different streams at once: each call takes
-    # its own workspace from the stream-ordered pool, so neither sees the other's
-    # re-encoded operands.
+    # Two FP6-path calls in flight on different streams at once, each with its
+    # own workspace: neither sees the other's re-encoded operands.
     say("fp6 two streams")
     dev = torch.device("cuda:0")
     shapes = [(640, 768, 4160), (512, 1024, 4096)]
@@ -424,12 +449,15 @@ def test_fp6_workspace_on_two_streams(torch):
                       torch.from_numpy(B).to(dev)))
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = [torch.full((M, N), SENTINEL, dtype=torch.int32, device=dev) for M, N, *_ in cases]
-    torch.cuda.synchronize()
     L.lpgemm_set_kernel_override(L.KERNEL_FP6)
+    wss = [workspace_for(torch, L.lpgemm_plan(L.VARIANT_I4I4, M, N, K)["workspace_bytes"])
+           for M, N, K, *_ in cases]
+    assert all(n > 0 for _, n, _ in wss)
+    torch.cuda.synchronize()
     for rep in range(3):
-        for (M, N, K, A, B, a_t, b_t), s, c_t in zip(cases, streams, outs):
-            st = L.lib().lpgemm_int4_int4(a_t.data_ptr(), b_t.data_ptr(), c_t.data_ptr(), M, N, K,
-                                          s.cuda_stream)
+        for (M, N, K, A, B, a_t, b_t), s, c_t, (ws, nws, _) in zip(cases, streams, outs, wss):
+            st = L.lib().lpgemm_int4_int4_ws(a_t.data_ptr(), b_t.data_ptr(), c_t.data_ptr(), M, N, K,
+                                             ws, nws, s.cuda_stream)
             assert st == L.OK, L.lpgemm_status_string(st)
     torch.cuda.synchronize()
     for (M, N, K, A, B, *_), c_t in zip(cases, outs):

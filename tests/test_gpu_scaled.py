@@ -66,9 +66,19 @@ def run_scaled(torch, variant, A, B, sa, sb, M, N, K, fmt, kernel=L.KERNEL_AUTO)
     dbuf = torch.full((M * N + 2 * GUARD,), sentinel, dtype=tdt, device=dev)
     d_t = dbuf[GUARD:GUARD + M * N]
     L.lpgemm_set_kernel_override(kernel)
-    fn = L.lib().lpgemm_int4_int4_scaled if variant == "i4i4" else L.lib().lpgemm_w4a8_scaled
-    st = fn(a_t.data_ptr(), b_t.data_ptr(), sa_t.data_ptr(), sb_t.data_ptr(), d_t.data_ptr(),
-            FORMATS[fmt][0], M, N, K, torch.cuda.current_stream().cuda_stream)
+    s = torch.cuda.current_stream().cuda_stream
+    if variant == "i4i4":
+        # the "_ws" entry point with the workspace the call can use (the FP6
+        # path's re-encoded operands; none for the other kernels)
+        nws = L.lpgemm_plan(L.VARIANT_I4I4, M, N, K)["workspace_bytes"] if M and N and K else 0
+        ws = torch.empty(nws + L.WORKSPACE_ALIGN, dtype=torch.uint8, device=dev)
+        ptr = ws.data_ptr() + (-ws.data_ptr()) % L.WORKSPACE_ALIGN if nws else None
+        st = L.lib().lpgemm_int4_int4_scaled_ws(a_t.data_ptr(), b_t.data_ptr(), sa_t.data_ptr(),
+                                                sb_t.data_ptr(), d_t.data_ptr(), FORMATS[fmt][0],
+                                                M, N, K, ptr, nws, s)
+    else:
+        st = L.lib().lpgemm_w4a8_scaled(a_t.data_ptr(), b_t.data_ptr(), sa_t.data_ptr(),
+                                        sb_t.data_ptr(), d_t.data_ptr(), FORMATS[fmt][0], M, N, K, s)
     assert st == L.OK, L.lpgemm_status_string(st)
     torch.cuda.synchronize()
     host = dbuf.cpu().numpy().view(elem)

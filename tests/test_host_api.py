@@ -364,3 +364,88 @@ def test_stream_read_probe_checks_arguments():
     assert run(blocks=0) == -1
     assert run(out=None) == -1
     assert run(out_ints=1023) == -1    # shorter than one int per thread
+
+
+# ---- caller-provided workspace --------------------------------------------------
+def _fp6_ws(M, N, K):
+    frag = lambda R: ((R + 31) // 32) * ((K + 63) // 64) * 1536
+    return (frag(M) + 255) // 256 * 256 + frag(N)
+
+
+def test_workspace_size_query():
+    ws = L.lpgemm_workspace_size
+    assert ws(L.VARIANT_I4I4, 8192, 8192, 8192) == _fp6_ws(8192, 8192, 8192) == 100663296
+    assert ws(L.VARIANT_I4I4, 8192, 8192, 8192, scaled=True) == 100663296  # FP6 serves scaled too
+    assert ws(L.VARIANT_W4A8, 4096, 4096, 4096) == 0                       # int8 256-tiles
+    assert ws(L.VARIANT_W4A8, 16, 28672, 8192) == 0                        # narrow-M
+    assert ws(L.VARIANT_I4I4, 3000, 5120, 6144) == 0                       # one tile per CU
+    assert ws(L.VARIANT_I4I4, 0, 5, 64) == 0 and ws(L.VARIANT_I4I4, 5, 5, 0) == 0
+    # long K over few tiles: one int32 M x N slice per K range (int32 result only)
+    p = L.lpgemm_plan(L.VARIANT_W4A8, 128, 2048, 65536)
+    assert p["k_chunks"] > 1
+    assert ws(L.VARIANT_W4A8, 128, 2048, 65536) == p["workspace_bytes"] == p["k_chunks"] * 128 * 2048 * 4
+    assert ws(L.VARIANT_W4A8, 128, 2048, 65536, scaled=True) == 0
+    assert ws(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=2048) == 0        # too few tiles for FP6
+    with pytest.raises(L.LpgemmError):
+        ws(L.VARIANT_I4I4, 4, 4, 33)
+    with pytest.raises(L.LpgemmError):
+        ws(L.VARIANT_I4I4, 4, 4, L.MAX_K + 2)
+    raw = L.lib().lpgemm_workspace_size
+    n = ctypes.c_size_t(7)
+    assert raw(2, 0, 4, 4, 32, 0, ctypes.byref(n)) == L.ERR_INVALID_ARG    # unknown variant
+    assert raw(0, 2, 4, 4, 32, 0, ctypes.byref(n)) == L.ERR_INVALID_ARG    # scaled not 0 / 1
+    assert raw(0, 0, 4, 4, 32, 0, None) == L.ERR_INVALID_ARG
+
+
+def test_plan_follows_the_workspace():
+    need = _fp6_ws(8192, 8192, 8192)
+    plan = lambda b: L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, workspace_bytes=b)
+    assert plan(0)["kernel"] == "tiled" and plan(0)["workspace_bytes"] == 0
+    assert plan(need - 1)["kernel"] == "tiled"
+    assert plan(need)["kernel"] == "fp6" and plan(need)["workspace_bytes"] == need
+    # K ranges cut to the slices that fit; none below two
+    full = L.lpgemm_plan(L.VARIANT_W4A8, 128, 2048, 65536)
+    slice_ = 128 * 2048 * 4
+    assert full["k_chunks"] >= 4
+    cut = L.lpgemm_plan(L.VARIANT_W4A8, 128, 2048, 65536, workspace_bytes=3 * slice_ + 5)
+    assert 2 <= cut["k_chunks"] <= 3 and cut["workspace_bytes"] <= 3 * slice_
+    one = L.lpgemm_plan(L.VARIANT_W4A8, 128, 2048, 65536, workspace_bytes=2 * slice_ - 1)
+    assert one["k_chunks"] == 1 and one["workspace_bytes"] == 0
+    # a forced FP6 kernel needs its workspace
+    L.lpgemm_set_kernel_override(L.KERNEL_FP6)
+    try:
+        assert L.lpgemm_plan(L.VARIANT_I4I4, 300, 300, 64)["kernel"] == "fp6"
+        with pytest.raises(L.LpgemmError) as e:
+            L.lpgemm_plan(L.VARIANT_I4I4, 300, 300, 64, workspace_bytes=0)
+        assert e.value.status == L.ERR_UNSUPPORTED
+    finally:
+        L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
+
+
+@pytest.mark.parametrize("fn", ["lpgemm_int4_int4_ws", "lpgemm_w4a8_ws"])
+def test_workspace_argument_errors(fn):
+    f = getattr(L.lib(), fn)
+    assert f(P, P, P, 4, 4, 32, None, 1024, None) == L.ERR_INVALID_ARG     # null, bytes > 0
+    assert f(P, P, P, 4, 4, 32, P + 16, 1024, None) == L.ERR_INVALID_ARG   # not 256-byte aligned
+    assert f(P, P, P, 4, 4, 33, P, 1024, None) == L.ERR_INVALID_ARG        # odd K still first
+    assert f(P, P, P, 4, 4, L.MAX_K + 2, P, 1024, None) == L.ERR_UNSUPPORTED
+    assert f(None, None, None, 0, 4, 32, None, 0, None) == L.OK             # empty
+    g = L.lib().lpgemm_int4_int4_scaled_ws
+    assert g(P, P, P, P, P, L.OUT_BF16, 4, 4, 32, P + 8, 64, None) == L.ERR_INVALID_ARG
+    assert g(P, P, P, P, P, 9, 4, 4, 32, None, 0, None) == L.ERR_INVALID_ARG
+
+
+def test_kernel_override_is_per_thread():
+    import threading
+    seen = {}
+
+    def other():
+        L.lpgemm_set_kernel_override(L.KERNEL_GENERAL)
+        seen["other"] = L.lpgemm_plan(L.VARIANT_W4A8, 4096, 4096, 4096)["kernel"]
+
+    L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["other"] == "general"
+    assert L.lpgemm_plan(L.VARIANT_W4A8, 4096, 4096, 4096)["kernel"] == "tiled"
