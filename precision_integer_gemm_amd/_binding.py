@@ -65,6 +65,14 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"the HIP library {LIB_PATH} is not built; run "
                           "`python -m precision_integer_gemm_amd.build` (or __graft_entry__.build())")
+    # PyTorch brings its own HIP runtime: load it first, so that the library
+    # binds to the same runtime as the streams and device pointers PyTorch
+    # hands over (a second runtime loaded ahead of it leaves PyTorch without
+    # a device).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     sz = ctypes.c_size_t
