@@ -78,7 +78,9 @@ typedef enum lpgemm_status {
     LPGEMM_OK = 0,
     LPGEMM_ERR_INVALID_ARG = 1, /* negative size, odd K, null pointer, bad enum  */
     LPGEMM_ERR_UNSUPPORTED = 2, /* valid request the library cannot serve        */
-    LPGEMM_ERR_HIP = 3          /* the HIP runtime reported an error at launch   */
+    LPGEMM_ERR_HIP = 3,         /* the HIP runtime reported an error at launch   */
+    LPGEMM_ERR_SCRATCH_LIMIT = 4 /* lpgemm_int4_int4_noalloc: the call needs more */
+                                 /* than LPGEMM_STATIC_SCRATCH_BYTES of scratch   */
 } lpgemm_status;
 
 /* Largest supported K (logical elements); see "Exactness" above. */
@@ -155,6 +157,28 @@ lpgemm_status lpgemm_int4_int4_ws(const void *A_packed, const void *B_packed, in
 lpgemm_status lpgemm_w4a8_ws(const int8_t *A, const uint8_t *B_packed, int32_t *C, int64_t M,
                              int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * lpgemm_int4_int4_ws for callers that cannot allocate device memory at all
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is the library's own static scratch, a device
+ * array of LPGEMM_STATIC_SCRATCH_BYTES that each GPU the library runs on
+ * holds from the library's load until the process ends.  The call allocates
+ * nothing and calls no allocating routine; the caller still provides A, B
+ * and C.  It takes the path lpgemm_int4_int4_ws takes with unlimited
+ * workspace and returns LPGEMM_ERR_SCRATCH_LIMIT, before any launch, when
+ * that path needs more scratch than the array holds (lpgemm_workspace_size
+ * gives the need: 8192^3 needs 96 MiB and fits, 16384 x 16384 x 8192 needs
+ * 192 MiB and is rejected).  Every call on one GPU shares that GPU's scratch, which
+ * keeps the last call's contents (nothing in it needs to start at zero):
+ * calls that overlap on one GPU -- on different streams, or from different
+ * threads -- race and must be serialised by the caller.  Other arguments,
+ * sizes and return codes as for lpgemm_int4_int4.
+ */
+#define LPGEMM_STATIC_SCRATCH_BYTES (128u << 20)
+
+lpgemm_status lpgemm_int4_int4_noalloc(const void *A_packed, const void *B_packed, int32_t *C,
+                                       int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /* ---- per-channel scaled output ---------------------------------------------- */
 

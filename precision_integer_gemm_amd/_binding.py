@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "_lpgemm.so")
 
 # lpgemm_status
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 # lpgemm_kernel
 KERNEL_AUTO, KERNEL_GENERAL, KERNEL_TILED, KERNEL_SKINNY = 0, 1, 2, 3
 KERNEL_TILED_128, KERNEL_TILED_256, KERNEL_TILED_64, KERNEL_FP6 = 4, 5, 6, 7
@@ -27,11 +27,13 @@ OUT_F32, OUT_BF16, OUT_F16, OUT_FP8_E4M3 = 0, 1, 2, 3
 MAX_K = 131070
 
 EXPORTS = ("lpgemm_int4_int4", "lpgemm_w4a8", "lpgemm_int4_int4_ws", "lpgemm_w4a8_ws",
+           "lpgemm_int4_int4_noalloc",
            "lpgemm_workspace_size", "lpgemm_int4_int4_scaled", "lpgemm_w4a8_scaled",
            "lpgemm_int4_int4_scaled_ws", "lpgemm_fp8_e4m3", "lpgemm_pack_int4",
            "lpgemm_unpack_int4", "lpgemm_status_string", "lpgemm_plan",
            "lpgemm_set_kernel_override")
 SIZE_MAX = 2 ** 64 - 1
+STATIC_SCRATCH_BYTES = 128 << 20  # LPGEMM_STATIC_SCRATCH_BYTES
 WORKSPACE_ALIGN = 256
 
 
@@ -76,7 +78,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     sz = ctypes.c_size_t
-    for name in ("lpgemm_int4_int4", "lpgemm_w4a8"):
+    for name in ("lpgemm_int4_int4", "lpgemm_w4a8", "lpgemm_int4_int4_noalloc"):
         f = getattr(L, name)
         f.argtypes = [p, p, p, i64, i64, i64, p]
         f.restype = ctypes.c_int

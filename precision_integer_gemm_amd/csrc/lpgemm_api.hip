@@ -329,6 +329,33 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
     return LPGEMM_OK;
 }
 
+// Scratch of the allocation-free entry point (lpgemm_int4_int4_noalloc): a
+// file-scope device array, one copy per device, held from the library's load
+// on that device until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in): the device address
+// comes from static_scratch().
+static __device__ __align__(256) uint8_t scratch[LPGEMM_STATIC_SCRATCH_BYTES];
+
+// This device's address of `scratch`, looked up once per device with that
+// device current.
+lpgemm_status static_scratch(void **ptr)
+{
+    static std::once_flag once[kMaxDevices];
+    static void *addr[kMaxDevices];
+    static hipError_t err[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERR_HIP;
+    std::call_once(once[dev], [dev] {
+        void *p = nullptr;
+        err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err[dev] == hipSuccess && p == nullptr) err[dev] = hipErrorInvalidSymbol;
+        addr[dev] = p;
+    });
+    if (err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
+    *ptr = addr[dev];
+    return LPGEMM_OK;
+}
+
 lpgemm_status launched()
 {
     return hipGetLastError() == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
@@ -706,6 +733,29 @@ lpgemm_status lpgemm_int4_int4_ws(const void *A_packed, const void *B_packed, in
                     workspace, workspace_bytes, stream);
 }
 
+lpgemm_status lpgemm_int4_int4_noalloc(const void *A_packed, const void *B_packed, int32_t *C,
+                                       int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    lpgemm_status st = check_args(A_packed, B_packed, C, M, N, K);
+    if (st != LPGEMM_OK || M == 0 || N == 0 || K == 0)
+        return st != LPGEMM_OK ? st
+                               : run_gemm(LPGEMM_VARIANT_I4I4, A_packed, B_packed, C, nullptr,
+                                          nullptr, OUT_I32, M, N, K, nullptr, 0, stream);
+    // the scratch the call would use with unlimited workspace
+    Plan p;
+    st = make_plan(LPGEMM_VARIANT_I4I4, A_packed, B_packed, C, M, N, K, device_cu_count(),
+                   (lpgemm_kernel)t_override, true, UINT64_MAX, &p);
+    if (st != LPGEMM_OK) return st;
+    if ((uint64_t)p.ws_bytes > LPGEMM_STATIC_SCRATCH_BYTES) return LPGEMM_ERR_SCRATCH_LIMIT;
+    void *ws = nullptr;
+    if (p.ws_bytes > 0) {
+        st = static_scratch(&ws);
+        if (st != LPGEMM_OK) return st;
+    }
+    return run_gemm(LPGEMM_VARIANT_I4I4, A_packed, B_packed, C, nullptr, nullptr, OUT_I32, M, N, K,
+                    ws, ws ? (size_t)LPGEMM_STATIC_SCRATCH_BYTES : 0, stream);
+}
+
 lpgemm_status lpgemm_w4a8_ws(const int8_t *A, const uint8_t *B_packed, int32_t *C, int64_t M,
                              int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
                              hipStream_t stream)
@@ -772,6 +822,7 @@ const char *lpgemm_status_string(lpgemm_status status)
     case LPGEMM_ERR_INVALID_ARG: return "invalid argument";
     case LPGEMM_ERR_UNSUPPORTED: return "unsupported";
     case LPGEMM_ERR_HIP: return "HIP runtime error";
+    case LPGEMM_ERR_SCRATCH_LIMIT: return "needs more scratch than the library's static scratch holds";
     }
     return "unknown status";
 }
