@@ -63,7 +63,7 @@ STEP_ORDER = ["w4a8_skinny_m16", "i4i4_8192", "w4a8_skinny_m1", "w4a8_4096", "i4
 
 KERNEL_SYMBOL = {"tiled": "gemm_pipelined_kernel", "skinny": "gemm_skinny_kernel",
                  "general": "gemm_general_kernel",
-                 "fp6": "fp6_convert_kernel (A, B) + gemm_fp6_kernel"}
+                 "fp6": "fp6_convert_pair_kernel + gemm_fp6_kernel"}
 
 
 def mfma_peak(kernel: str) -> float:

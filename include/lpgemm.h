@@ -301,10 +301,10 @@ typedef enum lpgemm_kernel {
                                  /* 256 x 256 tiles on the FP6 matrix cores       */
 } lpgemm_kernel;
 /* LPGEMM_KERNEL_AUTO picks FP6 for int4 x int4 when the fast path applies,
- * the call's workspace holds the re-encoded operands, M > 128, K >= 2048, the
- * 256 x 256 output tiles number at least the compute units, and either twice
- * the compute units or K >= 8192 (there the re-encoding pass costs less than
- * the matrix cores save).  Up to 128 rows of
+ * the call's workspace holds the re-encoded operands, M > 128, and either the
+ * 256 x 256 output tiles number at least twice the compute units with
+ * K >= 2048, or three quarters of them with K >= 3072 (there the re-encoding
+ * pass costs less than the matrix cores save).  Up to 128 rows of
  * A it takes the tiled kernel with 128 x 128 or 64 x 64 tiles (B is read
  * once), or the narrow-M kernel for M <= 16, either format, and up to 64 rows
  * where the tiled kernel would have few workgroups.  With an int32 result and

@@ -70,14 +70,18 @@ using F8Tiny = TiledKernel<FP8, 1, 1, 2, 2, 128, 2>;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 // FP6 path (gemm_fp6.hpp): 256 x 256 tiles, 8 waves of 128 (m) x 64 (n), three
-// LDS stages of 128 k (144 KB).  Chosen automatically for int4 x int4 when the
-// re-encoding pass pays for itself (measured against the int8 256-tile kernel,
-// interleaved): at least one 256-tile per compute unit and K >= 2048, with
-// either two tiles per compute unit or K >= 8192 (8192^2 x 2048: 6% faster,
-// 4096^2 x 16384: 8% faster; 4096^3 and 3000 x 5120 x 6144: 5-8% slower).
+// LDS stages of 128 k (144 KB), after one launch that re-encodes both
+// operands.  Chosen automatically for int4 x int4 where the re-encoding pays
+// for itself, measured against the int8 tiled kernel (interleaved, outputs
+// identical): with the 256-tiles covering three quarters of the compute units
+// and K >= 3072 (3000 x 5120 x 6144, 240 tiles: 89.0 -> 78.0 us; 4096^3 64.9
+// -> 60.5; 4096 x 3584 x 4096 +9%; 2560 x 5120 x 8192 +17%), or two tiles
+// per compute unit and K >= 2048 (8192^2 x 2048 +20%, 8192^3 472 -> 371 us);
+// not below (4096^2 x 2048 even; 3072^2 x 4096, 144 tiles, +2.5%;
+// 2048 x 4096 x 4096, 128 tiles, -14%; 2048^2 x 8192 -38%).
 constexpr int kFp6FM = 4, kFp6FN = 2, kFp6WM = 2, kFp6WN = 4, kFp6KS = 2, kFp6Stages = 3;
 using Fp6Tile = Fp6Cfg<kFp6FM, kFp6FN, kFp6WM, kFp6WN, kFp6KS, kFp6Stages>;
-constexpr int64_t kFp6MinK = 2048, kFp6LongK = 8192;
+constexpr int64_t kFp6MinK = 2048, kFp6OneTileK = 3072;
 
 // Up to this many rows of A the product is bound by reading B once: no
 // 256-tiles and no FP6 re-encoding (which alone moves 2.5x B's bytes).  With
@@ -90,8 +94,8 @@ constexpr int64_t kTiledMinRange = 1024, kTiledSplitK = 12288;
 
 bool fp6_pays(int64_t K, int64_t tiles256, int cu_count)
 {
-    return K >= kFp6MinK && tiles256 >= cu_count &&
-           (tiles256 >= 2 * (int64_t)cu_count || K >= kFp6LongK);
+    return (K >= kFp6MinK && tiles256 >= 2 * (int64_t)cu_count) ||
+           (K >= kFp6OneTileK && 4 * tiles256 >= 3 * (int64_t)cu_count);
 }
 
 // Skinny (both formats, M <= 16): 16 waves split K (up to 4 steps of 128 k
@@ -296,6 +300,9 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         p.tiles_m = (int)ceil_div(M, Fp6Tile::BM);
         p.tiles_n = (int)ceil_div(N, Fp6Tile::BN);
         if ((int64_t)p.tiles_m * p.tiles_n > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+        // the conversion grid: one workgroup per row block and four k blocks
+        if ((ceil_div(M, 32) + ceil_div(N, 32)) * ceil_div(ceil_div(K, 64), 4) > INT32_MAX)
+            return LPGEMM_ERR_UNSUPPORTED;
         p.workgroups = std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, cu_count);
         p.ws_bytes = fp6_workspace(M, N, K);
         break;
@@ -495,11 +502,10 @@ lpgemm_status launch_fp6(const Plan &p, const uint8_t *a, const uint8_t *b, Epil
     const int64_t bytes_a = (int64_t)align_ws((uint64_t)fp6_bytes(m, k));
     uint8_t *a6 = static_cast<uint8_t *>(ws);
     uint8_t *b6 = a6 + bytes_a;
-    const unsigned kgroups = (unsigned)ceil_div(ceil_div(k, 64), 32);
-    hipLaunchKernelGGL(fp6_convert_kernel, dim3((unsigned)ceil_div(m, 32), kgroups), dim3(512), 0,
-                       stream, a, a6, (int64_t)m, k);
-    hipLaunchKernelGGL(fp6_convert_kernel, dim3((unsigned)ceil_div(n, 32), kgroups), dim3(512), 0,
-                       stream, b, b6, (int64_t)n, k);
+    const int64_t kgroups = ceil_div(ceil_div(k, 64), 4);
+    const int64_t ga = ceil_div(m, 32) * kgroups, gb = ceil_div(n, 32) * kgroups;  // < 2^31 (plan)
+    hipLaunchKernelGGL(fp6_convert_pair_kernel, dim3((unsigned)(ga + gb)), dim3(256), 0, stream, a, a6,
+                       (int64_t)m, b, b6, (int64_t)n, k, ga);
     const uint8_t *ca6 = a6, *cb6 = b6;
     int tiles_m = p.tiles_m, tiles_n = p.tiles_n, xcds = kXcds;
     void *args[] = {(void *)&ca6, (void *)&cb6, (void *)&epi, (void *)&m,       (void *)&n,

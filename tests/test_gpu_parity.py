@@ -347,14 +347,16 @@ def test_named_case_full_parity(torch, name):
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
 
 
-@pytest.mark.parametrize("name", ["i4i4_ragged", "i4i4_1024"])
-def test_named_case_full_parity_fp6(torch, name):
-    # the FP6 path on named int4 x int4 workloads the automatic choice gives to
-    # the int8 kernel (ragged edges in M; a single k group of 1024)
+@pytest.mark.parametrize("name,kernel", [("i4i4_ragged", L.KERNEL_TILED_256), ("i4i4_1024", L.KERNEL_FP6)],
+                         ids=["ragged-int8-256", "1024-fp6"])
+def test_named_case_full_parity_other_path(torch, name, kernel):
+    # the path the automatic choice does not take for the workload: the
+    # ragged case (FP6 automatically) on the int8 256-tile kernel, and the
+    # single k group of 1024 (int8 64-tiles automatically) on the FP6 path
     c = CASES[name]
-    say(f"case {name} forced fp6")
+    say(f"case {name} forced kernel {kernel}")
     A, B = operands(c)
-    got = run_gpu(torch, c.variant, A, B, c.M, c.N, c.K, kernel=L.KERNEL_FP6)
+    got = run_gpu(torch, c.variant, A, B, c.M, c.N, c.K, kernel=kernel)
     assert np.array_equal(got, oracle_full(c.variant, A, B, c.M, c.N, c.K))
 
 

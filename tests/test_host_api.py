@@ -109,14 +109,15 @@ def test_kernel_override_rejects_unknown_values():
     (L.VARIANT_W4A8, 16, 28672, 8192, "skinny"),
     (L.VARIANT_W4A8, 1, 28672, 8192, "skinny"),
     (L.VARIANT_W4A8, 4096, 4096, 4096, "tiled"),
-    (L.VARIANT_I4I4, 8192, 8192, 8192, "fp6"),     # 1024 tiles >= 2 x 256 CUs, K >= 4096
-    (L.VARIANT_I4I4, 3000, 5120, 6144, "tiled"),   # 240 tiles: too few for the FP6 pass
+    (L.VARIANT_I4I4, 8192, 8192, 8192, "fp6"),     # 1024 tiles >= 2 x 256 CUs
+    (L.VARIANT_I4I4, 3000, 5120, 6144, "fp6"),     # 240 tiles >= 3/4 of the CUs, K >= 3072
     (L.VARIANT_I4I4, 8192, 8192, 2048, "fp6"),     # 1024 tiles, K = 2048
     (L.VARIANT_I4I4, 8192, 8192, 1024, "tiled"),   # K below 2048
     (L.VARIANT_I4I4, 8192, 4096, 4096, "fp6"),     # 512 tiles
-    (L.VARIANT_I4I4, 4096, 4096, 4096, "tiled"),   # 256 tiles, K below 8192
-    (L.VARIANT_I4I4, 4096, 4096, 16384, "fp6"),    # 256 tiles, K >= 8192
-    (L.VARIANT_I4I4, 3840, 4096, 16384, "tiled"),  # 240 tiles: fewer than the CUs
+    (L.VARIANT_I4I4, 4096, 4096, 4096, "fp6"),     # 256 tiles, K >= 3072
+    (L.VARIANT_I4I4, 4096, 4096, 2048, "tiled"),   # 256 tiles, K below 3072
+    (L.VARIANT_I4I4, 3840, 4096, 16384, "fp6"),    # 240 tiles
+    (L.VARIANT_I4I4, 3072, 3072, 4096, "tiled"),   # 144 tiles: under 3/4 of the CUs
     (L.VARIANT_W4A8, 8192, 8192, 8192, "tiled"),   # FP6 is int4 x int4 only
     (L.VARIANT_I4I4, 256, 256, 256, "tiled"),
     (L.VARIANT_I4I4, 17, 33, 34, "general"),     # K % 32 != 0
@@ -131,9 +132,9 @@ def test_fp6_plan():
     assert (p["kernel"], p["tile_m"], p["tile_n"], p["workgroups"], p["threads"]) == ("fp6", 256, 256, 256, 512)
     # fewer CUs: the same shape has enough tiles; more CUs: not enough
     assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=304)["kernel"] == "fp6"
-    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=1024)["kernel"] == "fp6"   # K >= 8192
-    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 4096, cu_count=1024)["kernel"] == "tiled"
-    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=1100)["kernel"] == "tiled"
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=1024)["kernel"] == "fp6"   # K >= 3072
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 2048, cu_count=1024)["kernel"] == "tiled"
+    assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, cu_count=1400)["kernel"] == "tiled"
     # the FP6 path needs the fast-path conditions (K % 32, 16-byte alignment)
     assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8194)["kernel"] == "general"
     assert L.lpgemm_plan(L.VARIANT_I4I4, 8192, 8192, 8192, B=P + 8)["kernel"] == "general"
@@ -378,7 +379,8 @@ def test_workspace_size_query():
     assert ws(L.VARIANT_I4I4, 8192, 8192, 8192, scaled=True) == 100663296  # FP6 serves scaled too
     assert ws(L.VARIANT_W4A8, 4096, 4096, 4096) == 0                       # int8 256-tiles
     assert ws(L.VARIANT_W4A8, 16, 28672, 8192) == 0                        # narrow-M
-    assert ws(L.VARIANT_I4I4, 3000, 5120, 6144) == 0                       # one tile per CU
+    assert ws(L.VARIANT_I4I4, 3000, 5120, 6144) == _fp6_ws(3000, 5120, 6144)  # FP6 from 3/4 tile per CU
+    assert ws(L.VARIANT_I4I4, 2048, 4096, 4096) == 0                       # 128 tiles: int8 tiles
     assert ws(L.VARIANT_I4I4, 0, 5, 64) == 0 and ws(L.VARIANT_I4I4, 5, 5, 0) == 0
     # long K over few tiles: one int32 M x N slice per K range (int32 result only)
     p = L.lpgemm_plan(L.VARIANT_W4A8, 128, 2048, 65536)
