@@ -117,3 +117,31 @@ def test_gemm_nan_operand_gives_nan():
     A[1, 3] = 0x7F
     C, _ = oracle.gemm_fp8(A, np.full((2, 8), 0x38, np.uint8), 2, 2, 8)
     assert not np.isnan(C[0]).any() and np.isnan(C[1]).all()
+
+
+def test_group_exponent_bound_helper():
+    # the matrix-core error bound used by the GPU tests, against a hand-worked
+    # value and a per-group brute force over the products' exponent sums
+    import sys, os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from fp8_bounds import group_exponent_bound
+    a = np.zeros((1, 16)); b = np.zeros((1, 16))
+    a[0, 0], a[0, 3], b[0, 1], b[0, 9] = 448.0, 1.0, 448.0, 2.0 ** -9   # group 1 of A is empty
+    A, B = oracle.fp8_e4m3_encode(a).reshape(1, 16), oracle.fp8_e4m3_encode(b).reshape(1, 16)
+    assert group_exponent_bound(A, B, 16)[0, 0] == 7 * 2.0 ** (8 + 8 - 13)
+    rng = np.random.default_rng(3)
+    M, N, K = 5, 6, 40
+    A = rng.integers(0, 256, (M, K)).astype(np.uint8); B = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    A[(A & 0x7F) == 0x7F] &= 0xF8; B[(B & 0x7F) == 0x7F] &= 0xF8
+    A[:, 8:16] = 0                                                     # an empty group
+    ex = lambda c: np.where(((c >> 3) & 15) == 0, -6, ((c >> 3) & 15).astype(int) - 7)
+    got = group_exponent_bound(A, B, K)
+    for m in range(M):
+        for n in range(N):
+            exact = 0.0   # with the per-product exponent sum E of each group
+            for g in range(K // 8):
+                ks = [k for k in range(8 * g, 8 * g + 8) if (A[m, k] & 0x7F) and (B[n, k] & 0x7F)]
+                if ks:
+                    exact += 7 * 2.0 ** (max(int(ex(A[m, k])) + int(ex(B[n, k])) for k in ks) - 13)
+            assert got[m, n] >= exact
+            assert got[m, n] <= 2.0 ** 14 * max(exact, 2.0 ** -30)
