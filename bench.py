@@ -79,41 +79,105 @@ PROBES = [("fp6_mfma", 0, 24000), ("int8_mfma", 1, 24000), ("fp8_mfma", 2, 12000
           ("lds_read", 3, 40000), ("fp6_gemm_inner_loop", 4, 12000)]
 
 
-# The HBM counterpart: one plain streaming read (16-byte non-temporal loads)
-# over a buffer of the decode shapes' packed weights (N * K / 2 bytes), rotated
-# over three copies like the isolated decode timing so that every pass reads
-# HBM rather than the 256 MB MALL; 16 workgroups of 256 threads per compute unit.
-STREAM_COPIES, STREAM_WG_PER_CU, STREAM_REPS = 3, 16, 21
+# The HBM counterpart: one streaming pass over a buffer of the decode shapes'
+# packed weights (N * K / 2 bytes), rotated over three copies like the
+# isolated decode timing so that every pass reads HBM rather than the 256 MB
+# MALL.  The default run times the best configurations of the sweep below
+# (`bench.py --stream-sweep`, kept in profiles/) and reports the fastest:
+# direct-to-LDS loads of 1 KB per wave instruction with the non-temporal hint,
+# one 1024-thread workgroup per compute unit, two pieces in flight per wave;
+# buffer loads, 8 x 256 threads per compute unit, one 16-byte non-temporal
+# load in flight; the same with 2 x 256 threads and four in flight.
+STREAM_COPIES, STREAM_REPS = 3, 21
+STREAM_BEST = [(1, 1, 1024, 2, 2), (0, 8, 256, 1, 2), (0, 2, 256, 4, 2)]  # mode, wg/CU, threads, in flight, policy
 
 
 def stream_read_ceiling(torch, dev, stream, lib, nbytes: int, cus: int) -> dict:
     import ctypes
 
-    lib.ceiling_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
-                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    lib.ceiling_probe_stream_read.restype = ctypes.c_int
-    lib.ceiling_probe_stream_out_ints.argtypes = [ctypes.c_int]
-    lib.ceiling_probe_stream_out_ints.restype = ctypes.c_int64
-    blocks = STREAM_WG_PER_CU * cus
-    n_out = lib.ceiling_probe_stream_out_ints(blocks)
+    lib.ceiling_probe_stream_sweep.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.c_void_p]
+    lib.ceiling_probe_stream_sweep.restype = ctypes.c_int
+    n_out = 8 * cus * 1024
     out = torch.empty(n_out, dtype=torch.int32, device=dev)
     bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(STREAM_COPIES)]
-    us = []
-    for r in range(STREAM_REPS + STREAM_COPIES):  # the first pass over each copy is a warm-up
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        st = lib.ceiling_probe_stream_read(bufs[r % STREAM_COPIES].data_ptr(), nbytes, blocks,
-                                           out.data_ptr(), n_out, stream.cuda_stream)
-        e1.record(stream)
-        if st != 0:
-            raise RuntimeError(f"stream-read probe: status {st}")
-        torch.cuda.synchronize()
-        if r >= STREAM_COPIES:
-            us.append(e0.elapsed_time(e1) * 1e3)
-    med = float(np.median(us))
+    best = None
+    for mode, wpc, threads, inflight, pol in STREAM_BEST:
+        us = []
+        for r in range(STREAM_REPS + STREAM_COPIES):  # the first pass over each copy is a warm-up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = lib.ceiling_probe_stream_sweep(bufs[r % STREAM_COPIES].data_ptr(), nbytes, mode,
+                                                wpc * cus, threads, inflight, pol, out.data_ptr(),
+                                                n_out, stream.cuda_stream)
+            e1.record(stream)
+            if st != 0:
+                raise RuntimeError(f"stream-read probe: status {st}")
+            torch.cuda.synchronize()
+            if r >= STREAM_COPIES:
+                us.append(e0.elapsed_time(e1) * 1e3)
+        med = float(np.median(us))
+        rec = {"bytes": nbytes, "median_us": round(med, 3), "min_us": round(float(np.min(us)), 3),
+               "gb_s": round(nbytes / (med * 1e-6) / 1e9, 1),
+               "config": {"loads": "to_lds" if mode else "buffer", "wg_per_cu": wpc,
+                          "threads": threads, "in_flight": inflight, "policy": "nt"}}
+        if best is None or med < best["median_us"]:
+            best = rec
     del bufs
-    return {"bytes": nbytes, "median_us": round(med, 3), "min_us": round(float(np.min(us)), 3),
-            "gb_s": round(nbytes / (med * 1e-6) / 1e9, 1), "workgroups": blocks}
+    return best
+
+
+# The sweep of single streaming passes over the decode shapes' 117 MB: buffer
+# loads (workgroups per compute unit, loads in flight per thread, cache
+# policy) and direct-to-LDS loads (workgroups, 1 KB pieces in flight per
+# wave, non-temporal or not), each over three rotated copies.
+SWEEP_BUF = [(w, 256, f, pol) for w in (2, 4, 8, 16, 32) for f in (1, 2, 4, 8) for pol in (0, 2, 1, 16, 18)]
+SWEEP_DMA = [(1, 1024, f, pol) for f in (2, 4, 8) for pol in (0, 2)] + \
+            [(2, 512, f, pol) for f in (4, 8) for pol in (0, 2)] + \
+            [(4, 256, f, pol) for f in (4, 8, 16) for pol in (0, 2)] + \
+            [(8, 256, f, 2) for f in (4, 8)]
+
+
+def stream_sweep(torch, dev, stream, nbytes: int) -> dict:
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "precision_integer_gemm_amd", "_ceiling.so"))
+    lib.ceiling_probe_stream_sweep.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.c_void_p]
+    lib.ceiling_probe_stream_sweep.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(STREAM_COPIES)]
+    n_out = 32 * cus * 1024
+    out = torch.empty(n_out, dtype=torch.int32, device=dev)
+    rows = []
+    for mode, table in ((0, SWEEP_BUF), (1, SWEEP_DMA)):
+        for wpc, threads, inflight, pol in table:
+            us = []
+            for r in range(STREAM_REPS + STREAM_COPIES):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                st = lib.ceiling_probe_stream_sweep(bufs[r % STREAM_COPIES].data_ptr(), nbytes, mode,
+                                                    wpc * cus, threads, inflight, pol, out.data_ptr(),
+                                                    n_out, stream.cuda_stream)
+                e1.record(stream)
+                if st != 0:
+                    raise RuntimeError(f"stream sweep {mode} {wpc} {threads} {inflight} {pol}: {st}")
+                torch.cuda.synchronize()
+                if r >= STREAM_COPIES:
+                    us.append(e0.elapsed_time(e1) * 1e3)
+            med = float(np.median(us))
+            rows.append({"loads": "buffer" if mode == 0 else "to_lds", "wg_per_cu": wpc,
+                         "threads": threads, "in_flight": inflight,
+                         "policy": {0: "-", 1: "sc0", 2: "nt", 16: "sc1", 18: "sc1 nt"}[pol],
+                         "median_us": round(med, 2), "min_us": round(float(np.min(us)), 2),
+                         "gb_s": round(nbytes / (med * 1e-6) / 1e9, 1)})
+            print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    best = min(rows, key=lambda r: r["median_us"])
+    return {"bytes": nbytes, "configs": len(rows), "best": best, "rows": rows}
 
 
 def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0) -> dict:
@@ -124,7 +188,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
         raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
     lib = ctypes.CDLL(path)
     lib.ceiling_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                     ctypes.c_int64, ctypes.c_void_p]
+                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ceiling_probe_wall_clock_khz.restype = ctypes.c_int
     lib.ceiling_probe_run.restype = ctypes.c_int
     lib.ceiling_probe_work.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.ceiling_probe_work.restype = ctypes.c_double
@@ -133,19 +198,29 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
     blocks = torch.cuda.get_device_properties(dev).multi_processor_count
     n_out = max(lib.ceiling_probe_out_floats(k, blocks) for _, k, _ in PROBES)
     out = torch.empty(n_out, dtype=torch.float32, device=dev)
-    res = {"compute_units": blocks}
+    clk = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    wall_khz = lib.ceiling_probe_wall_clock_khz()
+    lib.ceiling_probe_max_clock_khz.restype = ctypes.c_int
+    max_khz = lib.ceiling_probe_max_clock_khz()
+    res = {"compute_units": blocks, "max_sclk_mhz": round(max_khz / 1000.0, 1) if max_khz > 0 else None}
     for name, kind, iters in PROBES:
-        ms = []
+        ms, mhz = [], []
         for r in range(reps + 1):  # the first launch is a warm-up
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            st = lib.ceiling_probe_run(kind, blocks, iters, out.data_ptr(), n_out, stream.cuda_stream)
+            st = lib.ceiling_probe_run(kind, blocks, iters, out.data_ptr(), n_out, clk.data_ptr(),
+                                       stream.cuda_stream)
             e1.record(stream)
             if st != 0:
                 raise RuntimeError(f"ceiling probe {name}: status {st}")
             torch.cuda.synchronize()
             if r:
                 ms.append(e0.elapsed_time(e1))
+                # shader clock over the loop: shader-clock ticks per constant-rate
+                # tick, averaged over the workgroups
+                c = clk.cpu().numpy().reshape(blocks, 2).astype(np.float64)
+                if wall_khz > 0 and (c[:, 1] > 0).all():
+                    mhz.append(float(np.mean(c[:, 0] / c[:, 1])) * wall_khz / 1000.0)
         t = float(np.median(ms)) * 1e-3
         work = lib.ceiling_probe_work(kind, blocks, iters)
         if name == "lds_read":
@@ -153,21 +228,23 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
                          "gb_s_per_cu": round(work / t / 1e9 / blocks, 1), "ms": round(t * 1e3, 3)}
         else:
             res[name] = {"tops": round(work / t / 1e12, 1), "ms": round(t * 1e3, 3)}
+        if mhz:
+            res[name]["sclk_mhz"] = round(float(np.median(mhz)), 1)
     if stream_bytes:
         res["hbm_stream_read"] = stream_read_ceiling(torch, dev, stream, lib, stream_bytes, blocks)
     return res
 
 
 # HBM traffic of the dominant call, from two rocprofv3 --pmc runs (FETCH_SIZE,
-# then WRITE_SIZE, KiB per dispatch, summed over the call's dispatches: the two
-# FP6 re-encodings and the GEMM), each scaled by what the same counter
+# then WRITE_SIZE, KiB per dispatch, summed over the call's dispatches: the
+# FP6 re-encoding of both operands and the GEMM), each scaled by what the same counter
 # reads for a plain 256 MiB device copy (bench.py --copy-calibration 256):
 # FETCH_SIZE reads 131072 KiB for 256 MiB read (x2.0), WRITE_SIZE 262144 KiB
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328083.9, "fetch_scale": 2.0, "write_kib": 362950.6,
-                  "write_scale": 1.0, "sources_sha256": "77235a2a25fdbd427f87051efe3cc2410f86e735cacfe121d969b852ce0acec3"},
+    "i4i4_8192": {"fetch_kib": 328134.0, "fetch_scale": 2.0, "write_kib": 364860.1,
+                  "write_scale": 1.0, "sources_sha256": "d8dcb8a5b05d453781ccc2fed9c1dc55e3b85ee3be7d365a5b910ebb5d04ebdf"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",
@@ -210,6 +287,8 @@ def parse():
     ap.add_argument("--ceiling", action="store_true",
                     help="run only the sustained-ceiling probes and print their JSON")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the sustained-ceiling probes")
+    ap.add_argument("--stream-sweep", action="store_true",
+                    help="only sweep the streaming-read probe over the decode weights' size")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="summarise a rocprofv3 kernel_trace.csv per kernel and grid (no GPU use)")
     return ap.parse_args()
@@ -233,6 +312,18 @@ def trace_summary(path: str) -> int:
     for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         print(f"| {name} | {grid} | {wg} | {len(d)} | {sum(d) / len(d):.0f} | {min(d)} | {max(d)} |")
     return 0
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def roofline_time_s(case, kernel: str = "tiled") -> tuple[float, str]:
@@ -278,6 +369,10 @@ def main() -> int:
     if args.ceiling:
         print(json.dumps({"ceiling": sustained_ceilings(torch, dev, torch.cuda.current_stream(),
                                                         stream_bytes=stream_bytes)}))
+        return 0
+    if args.stream_sweep:
+        print(json.dumps({"stream_sweep": stream_sweep(torch, dev, torch.cuda.current_stream(),
+                                                       stream_bytes)}))
         return 0
 
     names = [n for n in STEP_ORDER if args.case is None or n in args.case]
@@ -594,6 +689,13 @@ def main() -> int:
         "per_config_long_k": long_k,
         "ceiling": ceiling,
     }
+    if ceiling is not None:
+        # the shader clock measured under sustained matrix-core load (the
+        # probes' own clock counters), and the device's maximum
+        result["sclk_mhz"] = {"max": ceiling.get("max_sclk_mhz"),
+                              **{f"under_{k}": ceiling[k]["sclk_mhz"] for k in
+                                 ("int8_mfma", "fp6_mfma", "fp8_mfma", "fp6_gemm_inner_loop")
+                                 if "sclk_mhz" in ceiling.get(k, {})}}
 
     if not args.no_cpu:
         import oracle
@@ -616,11 +718,27 @@ def main() -> int:
             sample.append(f"{c.name}[:{rows}]")
             print(f"# cpu oracle {c.name} rows {rows}: {dt:.2f} s, parity "
                   f"{np.array_equal(got, ref)}", file=sys.stderr, flush=True)
+        # one host thread on the two small workloads, whole
+        threads = oracle.num_threads()
+        one_thread = {}
+        oracle.set_num_threads(1)
+        try:
+            for w in work:
+                c = w["case"]
+                if c.name not in ("i4i4_256", "i4i4_1024"):
+                    continue
+                t = time.perf_counter()
+                oracle.gemm_i4i4(w["A"], w["B"], c.M, c.N, c.K)
+                dt = time.perf_counter() - t
+                one_thread[c.name] = {"s": round(dt, 4), "tops": round(c.ops / dt / 1e12, 6)}
+        finally:
+            oracle.set_num_threads(threads)
         result["cpu_baseline"] = {
             "value": round(total_ops / total_t / 1e12, 5), "unit": "TOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "first rows of every workload (" + ", ".join(sample) +
-                      f"), {total_t:.1f} s wall on {oracle.num_threads()} threads"}
+                      f"), {total_t:.1f} s wall on {threads} threads",
+            "one_thread": one_thread}
         result["parity_sampled_rows"] = parity_ok
 
     print(json.dumps(result))

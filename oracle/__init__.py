@@ -65,6 +65,8 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     i64, p = ctypes.c_int64, ctypes.c_void_p
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     for name in ("oracle_unpack_int4", "oracle_pack_int4"):
         f = getattr(lib, name)
         f.argtypes = [p, i64, i64, p]
@@ -112,6 +114,11 @@ def _ptr(a: np.ndarray):
 def num_threads() -> int:
     """OpenMP threads the oracle's row loop uses."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for later calls (for timing; results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def unpack_int4(packed, K: int) -> np.ndarray:

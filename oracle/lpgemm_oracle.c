@@ -70,6 +70,16 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads for the later calls (timing only; the results do not depend on it). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Unpack rows x K logical int4 from packed bytes [rows][K/2] into int8 [rows][K]. */
 int oracle_unpack_int4(const uint8_t *packed, int64_t rows, int64_t K, int8_t *out)
 {

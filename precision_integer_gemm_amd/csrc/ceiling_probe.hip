@@ -22,13 +22,22 @@
 // Work per launch (ceiling_probe_work): kinds 0-2 and 4 in operations
 // (2 x MACs), kind 3 in LDS bytes read.
 //
-// ceiling_probe_stream_read is the HBM counterpart: one plain pass over a
-// caller's buffer with 16-byte non-temporal loads, four in flight per thread,
-// every byte read once (what a single streaming pass of that size reaches,
-// launch and ramp included, for the memory-bound GEMM shapes).
+// Kinds 0-2 and 4 also report the shader clock they ran at: thread 0 of each
+// workgroup reads the shader-clock counter (s_memtime) and the constant-rate
+// counter (s_memrealtime) before and after its loop.
+//
+// ceiling_probe_stream_sweep is the HBM counterpart: one pass over a caller's
+// buffer, every byte read once (what a single streaming pass of that size
+// reaches, launch and ramp included, for the memory-bound GEMM shapes), in one
+// configuration of a family: buffer loads with a chosen cache policy and
+// loads in flight per thread, or direct-to-LDS loads of 1 KB per wave
+// instruction (the narrow-M GEMM's way of streaming its weights), with a
+// chosen number of workgroups.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+
+#include "device_common.hpp"
 
 namespace {
 
@@ -53,9 +62,30 @@ __device__ inline i32x8 operand(uint32_t seed, uint32_t mask)
     return v;
 }
 
-template <int KIND>
-__global__ __launch_bounds__(256) void mfma_loop(float *out, int iters)
+// Shader-clock and constant-rate counters at the start of a probe loop.
+struct Clocks {
+    uint64_t shader, real;
+};
+
+__device__ inline Clocks clocks_now()
 {
+    return Clocks{__builtin_amdgcn_s_memtime(), __builtin_amdgcn_s_memrealtime()};
+}
+
+// Thread 0 writes its workgroup's shader-clock and constant-rate ticks.
+__device__ inline void clocks_store(int64_t *clk, const Clocks &t0)
+{
+    if (clk != nullptr && threadIdx.x == 0) {
+        const Clocks t1 = clocks_now();
+        clk[2 * blockIdx.x] = (int64_t)(t1.shader - t0.shader);
+        clk[2 * blockIdx.x + 1] = (int64_t)(t1.real - t0.real);
+    }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void mfma_loop(float *out, int iters, int64_t *clk)
+{
+    const Clocks t0 = clocks_now();
     const uint32_t seed = threadIdx.x * 977u + blockIdx.x;
     const uint32_t mask = KIND == 2 ? 0x77777777u : 0xFFFFFFFFu;
     const i32x8 a = operand(seed, mask), b = operand(seed ^ 0x5555u, mask);
@@ -85,6 +115,7 @@ __global__ __launch_bounds__(256) void mfma_loop(float *out, int iters)
         for (int c = 0; c < kChains; ++c) s += acc[c][threadIdx.x & 15];
     }
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+    clocks_store(clk, t0);
 }
 
 // LDS image shared by kinds 3 and 4: four buffers of six fragments (36 KB),
@@ -107,8 +138,9 @@ __device__ inline i32x8 frag_at(const uint8_t *lds, int buf, int f, int lane)
     return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, 0, 0};
 }
 
-__global__ __launch_bounds__(512) void lds_loop(float *out, int iters)
+__global__ __launch_bounds__(512) void lds_loop(float *out, int iters, int64_t *clk)
 {
+    const Clocks t0 = clocks_now();
     extern __shared__ __align__(16) uint8_t lds[];
     fill_image(lds);
     const int lane = threadIdx.x & 63;
@@ -119,10 +151,12 @@ __global__ __launch_bounds__(512) void lds_loop(float *out, int iters)
         for (int f = 0; f < kFrags; ++f) x ^= frag_at(lds, buf, f, lane);
     }
     out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(x[0] ^ x[3] ^ x[5]);
+    clocks_store(clk, t0);
 }
 
-__global__ __launch_bounds__(512) void lds_mfma_loop(float *out, int iters)
+__global__ __launch_bounds__(512) void lds_mfma_loop(float *out, int iters, int64_t *clk)
 {
+    const Clocks t0 = clocks_now();
     constexpr int FM = 4, FN = 2;
     static_assert(FM + FN == kFrags, "one buffer holds one step's fragments");
     extern __shared__ __align__(16) uint8_t lds[];
@@ -155,32 +189,58 @@ __global__ __launch_bounds__(512) void lds_mfma_loop(float *out, int iters)
 #pragma unroll
         for (int j = 0; j < FM; ++j) s += acc[i][j][lane & 15];
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+    clocks_store(clk, t0);
 }
 
 int threads_of(int kind) { return kind >= 3 ? 512 : 256; }
 
-constexpr int kStreamThreads = 256;
-constexpr int kStreamInFlight = 4;
-
-// Thread t folds 16-byte elements t, t + S, t + 2S, ... (S = grid threads),
-// kStreamInFlight loads issued before any is used, and writes one int.
-__global__ __launch_bounds__(kStreamThreads) void stream_read(const i32x4 *__restrict__ p, int64_t n,
-                                                              int32_t *out)
+// Buffer-load pass: thread t folds 16-byte elements t, t + S, ... (S = grid
+// threads), F loads issued before any is used, each with cache policy POL
+// (the buffer instruction's sc0 / nt / sc1 bits).
+template <int F, int POL>
+__global__ void stream_buf(const void *base, int bytes, int64_t n, int32_t *out)
 {
-    const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-    const int64_t t = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const __amdgpu_buffer_rsrc_t r = lpgemm::buffer_rsrc(base, (uint32_t)bytes);
     int32_t fold = 0;
-    for (int64_t base = t; base < n; base += stride * kStreamInFlight) {
-        i32x4 v[kStreamInFlight];
+    for (int64_t base = t; base < n; base += stride * F) {
+        i32x4 v[F];
 #pragma unroll
-        for (int u = 0; u < kStreamInFlight; ++u) {
+        for (int u = 0; u < F; ++u) {
             const int64_t i = base + u * stride;
-            v[u] = i < n ? __builtin_nontemporal_load(p + i) : i32x4{0, 0, 0, 0};
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, i < n ? (uint32_t)(i * 16) : lpgemm::kOutOfRange, 0, POL);
         }
 #pragma unroll
-        for (int u = 0; u < kStreamInFlight; ++u) fold ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        for (int u = 0; u < F; ++u) fold ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     out[t] = fold;
+}
+
+// Direct-to-LDS pass: wave w of the grid copies 1 KB pieces w, w + W, ...
+// (W = grid waves) into its own F-slot LDS ring, keeping F in flight; the
+// data is not read back.  NT: the non-temporal hint of the narrow-M kernel.
+template <int F, bool NT>
+__global__ void stream_dma(i32x4 rsrc, int64_t pieces, int32_t *out)
+{
+    extern __shared__ __align__(1024) uint8_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int waves = blockDim.x >> 6;
+    const uint32_t ring = (uint32_t)reinterpret_cast<uintptr_t>(lds) + (uint32_t)(wave * F) * 1024u;
+    const int64_t total = (int64_t)gridDim.x * waves;
+    int slot = 0;
+    for (int64_t p = (int64_t)blockIdx.x * waves + wave; p < pieces; p += total) {
+        const uint32_t off = (uint32_t)(p * 1024) + 16u * (uint32_t)lane;
+        if (NT)
+            lpgemm::dma16_nt(rsrc, off, ring + (uint32_t)slot * 1024u);
+        else
+            lpgemm::dma16(rsrc, off, ring + (uint32_t)slot * 1024u);
+        slot = slot + 1 == F ? 0 : slot + 1;
+        lpgemm::wait_vmcnt<F - 1>();
+    }
+    lpgemm::wait_vmcnt<0>();
+    if (lane == 0) out[(int64_t)blockIdx.x * waves + wave] = slot;
 }
 
 }  // namespace
@@ -207,8 +267,10 @@ extern "C" int64_t ceiling_probe_out_floats(int kind, int blocks)
 // `stream`; `out` is device memory of ceiling_probe_out_floats(kind, blocks)
 // floats (`out_floats` says how many the caller has).  Returns 0, -1 for
 // bad arguments, or -2 if the launch failed.
+// `clocks`: NULL, or device memory of 2 * blocks int64 for each workgroup's
+// shader-clock and constant-rate ticks over its loop.
 extern "C" int ceiling_probe_run(int kind, int blocks, int iters, float *out, int64_t out_floats,
-                                hipStream_t stream)
+                                int64_t *clocks, hipStream_t stream)
 {
     if (kind < 0 || kind > 4 || blocks < 1 || iters < 1 || out == nullptr ||
         out_floats < ceiling_probe_out_floats(kind, blocks))
@@ -220,31 +282,84 @@ extern "C" int ceiling_probe_run(int kind, int blocks, int iters, float *out, in
                                  : (const void *)lds_mfma_loop;
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsRequest) != hipSuccess)
         return -2;
-    void *args[] = {&out, &iters};
+    void *args[] = {&out, &iters, &clocks};
     if (hipLaunchKernel(fn, dim3((unsigned)blocks), dim3((unsigned)threads_of(kind)), args, kLdsRequest,
                         stream) != hipSuccess)
         return -2;
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
-// Ints of `out` one stream_read launch of `blocks` workgroups writes.
-extern "C" int64_t ceiling_probe_stream_out_ints(int blocks)
+// The device's maximum shader clock, in kHz.
+extern "C" int ceiling_probe_max_clock_khz(void)
 {
-    return (int64_t)blocks * kStreamThreads;
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, dev) != hipSuccess)
+        return -1;
+    return khz;
 }
 
-// One streaming pass over `bytes` bytes of device memory at `buf` (16-byte
-// aligned, bytes a multiple of 16) with `blocks` workgroups on `stream`; `out`
-// holds `out_ints` >= ceiling_probe_stream_out_ints(blocks) ints.  Returns 0,
-// -1 for bad arguments, or -2 if the launch failed.
-extern "C" int ceiling_probe_stream_read(const void *buf, int64_t bytes, int blocks, int32_t *out,
-                                         int64_t out_ints, hipStream_t stream)
+// Rate of the constant-rate counter read by the probes, in kHz.
+extern "C" int ceiling_probe_wall_clock_khz(void)
 {
-    if (buf == nullptr || out == nullptr || bytes <= 0 || (bytes & 15) ||
-        (reinterpret_cast<uintptr_t>(buf) & 15u) || blocks < 1 ||
-        out_ints < ceiling_probe_stream_out_ints(blocks))
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
         return -1;
-    hipLaunchKernelGGL(stream_read, dim3((unsigned)blocks), dim3(kStreamThreads), 0, stream,
-                       static_cast<const i32x4 *>(buf), bytes / 16, out);
+    return khz;
+}
+
+// One configuration of the streaming-read family over `bytes` (a multiple of
+// 1024, below 4 GiB, 16-byte aligned) at `buf`:
+//   mode 0  buffer loads: `blocks` x `threads` threads, `inflight` in {1, 2,
+//           4, 8} loads per thread, `policy` in {0, 1 (sc0), 2 (nt), 16 (sc1),
+//           18 (sc1 nt)};
+//   mode 1  direct-to-LDS: `blocks` x `threads` threads, `inflight` in {2, 4,
+//           8, 16} 1 KB pieces per wave, `policy` 0 or 2 (nt); each workgroup
+//           holds threads / 64 * inflight KB of LDS (at most 160 KB).
+// `out` holds at least blocks * threads ints.  Returns 0, -1 for arguments
+// outside these sets, -2 if the launch failed.
+extern "C" int ceiling_probe_stream_sweep(const void *buf, int64_t bytes, int mode, int blocks,
+                                          int threads, int inflight, int policy, int32_t *out,
+                                          int64_t out_ints, hipStream_t stream)
+{
+    if (buf == nullptr || out == nullptr || bytes <= 0 || (bytes & 1023) || bytes >= (int64_t(1) << 32) ||
+        (reinterpret_cast<uintptr_t>(buf) & 15u) || blocks < 1 || threads < 64 || threads > 1024 ||
+        (threads & 63) || out_ints < (int64_t)blocks * threads)
+        return -1;
+    const i32x4 rsrc = {(int32_t)(uint32_t)reinterpret_cast<uintptr_t>(buf),
+                        (int32_t)((reinterpret_cast<uintptr_t>(buf) >> 32) & 0xFFFFu), (int32_t)bytes,
+                        0x00020000};
+    const void *fn = nullptr;
+    int lds = 0;
+    int64_t n = 0;
+    if (mode == 0) {
+        n = bytes / 16;
+#define LPG_BUF(F, P) (inflight == F && policy == P) ? (const void *)stream_buf<F, P>
+        fn = LPG_BUF(1, 0) : LPG_BUF(2, 0) : LPG_BUF(4, 0) : LPG_BUF(8, 0)
+           : LPG_BUF(1, 1) : LPG_BUF(2, 1) : LPG_BUF(4, 1) : LPG_BUF(8, 1)
+           : LPG_BUF(1, 2) : LPG_BUF(2, 2) : LPG_BUF(4, 2) : LPG_BUF(8, 2)
+           : LPG_BUF(1, 16) : LPG_BUF(2, 16) : LPG_BUF(4, 16) : LPG_BUF(8, 16)
+           : LPG_BUF(1, 18) : LPG_BUF(2, 18) : LPG_BUF(4, 18) : LPG_BUF(8, 18) : nullptr;
+#undef LPG_BUF
+    } else if (mode == 1) {
+        n = bytes / 1024;
+        lds = threads / 64 * inflight * 1024;
+        if (lds > 160 * 1024) return -1;
+#define LPG_DMA(F, P) (inflight == F && policy == (P ? 2 : 0)) ? (const void *)stream_dma<F, P>
+        fn = LPG_DMA(2, false) : LPG_DMA(4, false) : LPG_DMA(8, false) : LPG_DMA(16, false)
+           : LPG_DMA(2, true) : LPG_DMA(4, true) : LPG_DMA(8, true) : LPG_DMA(16, true) : nullptr;
+#undef LPG_DMA
+    }
+    if (fn == nullptr) return -1;
+    if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+        return -2;
+    i32x4 r = rsrc;
+    int nbytes = (int)(uint32_t)bytes;
+    void *args_buf[] = {const_cast<void **>(&buf), &nbytes, &n, &out};
+    void *args_dma[] = {&r, &n, &out};
+    void **args = mode == 0 ? args_buf : args_dma;
+    if (hipLaunchKernel(fn, dim3((unsigned)blocks), dim3((unsigned)threads), args, lds, stream) != hipSuccess)
+        return -2;
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }

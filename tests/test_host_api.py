@@ -343,28 +343,35 @@ def test_ceiling_probe_library_loads_and_checks_arguments():
     assert probe.ceiling_probe_run(0, 4, 1, 16, 1023, None) == -1
 
 
-def test_stream_read_probe_checks_arguments():
-    # the HBM streaming-read probe rejects bad arguments before any HIP call
+def test_stream_probe_checks_arguments():
+    # the HBM streaming-pass probe rejects bad arguments before any HIP call
     probe = ctypes.CDLL(os.path.join(ROOT, "precision_integer_gemm_amd", "_ceiling.so"))
-    probe.ceiling_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
-                                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    probe.ceiling_probe_stream_out_ints.argtypes = [ctypes.c_int]
-    probe.ceiling_probe_stream_out_ints.restype = ctypes.c_int64
-    assert probe.ceiling_probe_stream_out_ints(4096) == 4096 * 256
-    ok = dict(buf=256, nbytes=1 << 20, blocks=4, out=256, out_ints=1024)
+    probe.ceiling_probe_stream_sweep.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                                 ctypes.c_void_p]
+    ok = dict(buf=256, nbytes=1 << 20, mode=0, blocks=4, threads=256, inflight=4, policy=2,
+              out=256, out_ints=1024)
 
     def run(**kw):
         a = {**ok, **kw}
-        return probe.ceiling_probe_stream_read(a["buf"], a["nbytes"], a["blocks"], a["out"],
-                                               a["out_ints"], None)
+        return probe.ceiling_probe_stream_sweep(a["buf"], a["nbytes"], a["mode"], a["blocks"],
+                                                a["threads"], a["inflight"], a["policy"], a["out"],
+                                                a["out_ints"], None)
 
     assert run(buf=None) == -1
-    assert run(buf=264) == -1          # not 16-byte aligned
+    assert run(buf=264) == -1               # not 16-byte aligned
     assert run(nbytes=0) == -1
-    assert run(nbytes=(1 << 20) + 8) == -1  # not whole 16-byte elements
+    assert run(nbytes=(1 << 20) + 16) == -1  # not whole 1 KB pieces
+    assert run(nbytes=1 << 32) == -1        # beyond a 32-bit buffer range
     assert run(blocks=0) == -1
+    assert run(threads=100) == -1           # not whole waves
     assert run(out=None) == -1
-    assert run(out_ints=1023) == -1    # shorter than one int per thread
+    assert run(out_ints=1023) == -1         # shorter than one int per thread
+    assert run(inflight=3) == -1            # not an instantiated configuration
+    assert run(policy=5) == -1
+    assert run(mode=1, inflight=16, threads=1024) == -1   # 256 KB of LDS
+    assert run(mode=2) == -1
 
 
 # ---- caller-provided workspace --------------------------------------------------
