@@ -74,7 +74,16 @@
 extern "C" {
 #endif
 
-typedef enum lpgemm_status {
+/* The enumerations are int-sized in C and C++ alike; compiled as C++ they have
+ * int as their underlying type, so any int a C caller passes is a value of the
+ * type and an unknown one can be rejected. */
+#ifdef __cplusplus
+#define LPGEMM_ENUM_BASE : int
+#else
+#define LPGEMM_ENUM_BASE
+#endif
+
+typedef enum lpgemm_status LPGEMM_ENUM_BASE {
     LPGEMM_OK = 0,
     LPGEMM_ERR_INVALID_ARG = 1, /* negative size, odd K, null pointer, bad enum  */
     LPGEMM_ERR_UNSUPPORTED = 2, /* valid request the library cannot serve        */
@@ -130,7 +139,7 @@ lpgemm_status lpgemm_w4a8(const int8_t *A, const uint8_t *B_packed, int32_t *C,
  * `scaled` other than 0 or 1, or sizes the GEMM calls reject as invalid;
  * LPGEMM_ERR_UNSUPPORTED for K above LPGEMM_MAX_K.
  */
-typedef enum lpgemm_variant { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
+typedef enum lpgemm_variant LPGEMM_ENUM_BASE { LPGEMM_VARIANT_I4I4 = 0, LPGEMM_VARIANT_W4A8 = 1 } lpgemm_variant;
 
 lpgemm_status lpgemm_workspace_size(lpgemm_variant variant, int32_t scaled, int64_t M, int64_t N,
                                     int64_t K, int32_t cu_count, size_t *bytes);
@@ -183,7 +192,7 @@ lpgemm_status lpgemm_int4_int4_noalloc(const void *A_packed, const void *B_packe
 /* ---- per-channel scaled output ---------------------------------------------- */
 
 /* Element type of a scaled result. */
-typedef enum lpgemm_out_dtype {
+typedef enum lpgemm_out_dtype LPGEMM_ENUM_BASE {
     LPGEMM_OUT_F32 = 0,     /* IEEE binary32                               */
     LPGEMM_OUT_BF16 = 1,    /* bfloat16 bits (upper half of a binary32)    */
     LPGEMM_OUT_F16 = 2,     /* IEEE binary16                               */
@@ -302,7 +311,7 @@ const char *lpgemm_status_string(lpgemm_status status);
 
 /* ---- kernel selection: host-only, for tests and measurement -------------- */
 
-typedef enum lpgemm_kernel {
+typedef enum lpgemm_kernel LPGEMM_ENUM_BASE {
     LPGEMM_KERNEL_AUTO = 0,      /* choose by shape and alignment (default)      */
     LPGEMM_KERNEL_GENERAL = 1,   /* any shape and alignment; slow                */
     LPGEMM_KERNEL_TILED = 2,     /* block-tiled MFMA kernel, tile size by shape   */
