@@ -65,6 +65,14 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     i64, p = ctypes.c_int64, ctypes.c_void_p
     lib.oracle_num_threads.restype = ctypes.c_int
+    for name in ("oracle_fp8_e5m2_decode",):
+        f = getattr(lib, name)
+        f.argtypes = [p, i64, p]
+        f.restype = ctypes.c_int
+    lib.oracle_fp8_e5m2_encode.argtypes = [p, i64, p]
+    lib.oracle_fp8_e5m2_encode.restype = ctypes.c_int
+    lib.oracle_gemm_fp8_e5m2.argtypes = [p, p, i64, i64, i64, p, p]
+    lib.oracle_gemm_fp8_e5m2.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.oracle_set_num_threads.restype = None
     for name in ("oracle_unpack_int4", "oracle_pack_int4"):
@@ -251,4 +259,32 @@ def gemm_fp8(A, B, M: int, N: int, K: int):
     C = np.zeros((M, N), dtype=np.float64)
     Cabs = np.zeros((M, N), dtype=np.float64)
     _check(_load().oracle_gemm_fp8(_ptr(a), _ptr(b), M, N, K, _ptr(C), _ptr(Cabs)), "gemm_fp8")
+    return C, Cabs
+
+
+def fp8_e5m2_decode(codes) -> np.ndarray:
+    """Value of each e5m2 byte (float64; +-inf and NaN for those codes)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _check(_load().oracle_fp8_e5m2_decode(_ptr(c), c.size, _ptr(out)), "fp8_e5m2_decode")
+    return out
+
+
+def fp8_e5m2_encode(x) -> np.ndarray:
+    """Nearest e5m2 code of each value, ties to even, infinity from 61440 on."""
+    v = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _check(_load().oracle_fp8_e5m2_encode(_ptr(v), v.size, _ptr(out)), "fp8_e5m2_encode")
+    return out
+
+
+def gemm_fp8_e5m2(A, B, M: int, N: int, K: int):
+    """(C, Cabs) of decoded e5m2 operands: the exact sums C = A . B^T (as the
+    nearest float64) and the sums of the products' magnitudes, [M, N] each."""
+    a = _bytes2d(A, M, K, "A")
+    b = _bytes2d(B, N, K, "B")
+    C = np.zeros((M, N), dtype=np.float64)
+    Cabs = np.zeros((M, N), dtype=np.float64)
+    _check(_load().oracle_gemm_fp8_e5m2(_ptr(a), _ptr(b), M, N, K, _ptr(C), _ptr(Cabs)),
+           "gemm_fp8_e5m2")
     return C, Cabs

@@ -374,3 +374,113 @@ int oracle_gemm_fp8(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, in
     free(b);
     return ORACLE_OK;
 }
+
+/* ---- fp8 GEMM with e5m2 operands ---------------------------------------------
+ * [tutorial] gemm_fp8's "e4m3 / e5m2, fp32 accumulation": the same product with
+ * the other fp8 dtype.
+ *
+ * E5M2 (the OCP 8-bit format with infinities; the top byte of an IEEE
+ * binary16): bit 7 sign, bits 6..2 exponent with bias 15, bits 1..0 mantissa.
+ * Exponent 0 is subnormal (m/4 * 2^-14); exponent 31 is infinity (m = 0) or
+ * NaN (m != 0); every other code is (1 + m/4) * 2^(e-15), so the largest finite
+ * magnitude is 1.75 * 2^15 = 57344.  Each finite value is an integer times a
+ * power of two: (4 + m) * 2^(e-17), or m * 2^-16 for subnormals. */
+static int e5m2_int(uint8_t c, int64_t *im, int *ie)
+{
+    const int e = (c >> 2) & 31, m = c & 3;
+    if (e == 31) return 0;                     /* infinity or NaN */
+    *im = e == 0 ? m : 4 + m;
+    *ie = e == 0 ? -16 : e - 17;
+    if (c & 0x80) *im = -*im;
+    return 1;
+}
+
+static double e5m2_value(uint8_t c)
+{
+    const int s = c >> 7, e = (c >> 2) & 31, m = c & 3;
+    if (e == 31) return m ? NAN : (s ? -INFINITY : INFINITY);
+    const double v = e == 0 ? ldexp((double)m, -16) : ldexp(4.0 + m, e - 17);
+    return s ? -v : v;   /* -0.0 for the code 0x80 */
+}
+
+int oracle_fp8_e5m2_decode(const uint8_t *codes, int64_t n, double *out)
+{
+    if (n < 0) return ORACLE_ERR_ARG;
+    if (n == 0) return ORACLE_OK;
+    if (!codes || !out) return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) out[i] = e5m2_value(codes[i]);
+    return ORACLE_OK;
+}
+
+/* Nearest e5m2 code of x, ties to the even code, as for any IEEE format with
+ * infinities: magnitudes from the midpoint between the largest finite value and
+ * 2^16 (61440) on become infinity; NaN -> S.11111.11.  A search over the 124
+ * non-negative finite codes, which are ordered by value. */
+static uint8_t e5m2_encode(double x)
+{
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x)) return sign | 0x7F;
+    const double ax = fabs(x);
+    if (ax >= 61440.0) return sign | 0x7C;
+    int lo = 0;
+    for (int c = 1; c <= 0x7B; ++c)
+        if (e5m2_value((uint8_t)c) <= ax) lo = c;
+    if (e5m2_value((uint8_t)lo) == ax) return sign | (uint8_t)lo;
+    if (lo == 0x7B) return sign | 0x7B;        /* between 57344 and 61440 */
+    const int hi = lo + 1;
+    const double dlo = ax - e5m2_value((uint8_t)lo), dhi = e5m2_value((uint8_t)hi) - ax;
+    if (dlo < dhi) return sign | (uint8_t)lo;
+    if (dhi < dlo) return sign | (uint8_t)hi;
+    return sign | (uint8_t)((lo & 1) ? hi : lo);
+}
+
+int oracle_fp8_e5m2_encode(const double *x, int64_t n, uint8_t *out)
+{
+    if (n < 0) return ORACLE_ERR_ARG;
+    if (n == 0) return ORACLE_OK;
+    if (!x || !out) return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) out[i] = e5m2_encode(x[i]);
+    return ORACLE_OK;
+}
+
+/* C[m][n] = sum_k a(m,k) * b(n,k) over the decoded e5m2 values, and Cabs the
+ * sum of the products' magnitudes.  Products are integers times 2^-32 below
+ * 2^64 in those units; both sums are formed exactly in 128-bit integers and
+ * returned as the nearest double.  An infinite or NaN operand makes the sum
+ * follow IEEE arithmetic in double instead (a NaN or infinite result). */
+int oracle_gemm_fp8_e5m2(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K,
+                         double *C, double *Cabs)
+{
+    if (M < 0 || N < 0 || K < 0 || K >= ((int64_t)1 << 17)) return ORACLE_ERR_ARG;
+    if (M == 0 || N == 0) return ORACLE_OK;
+    if (!C || !Cabs || (K > 0 && (!A || !B))) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            __int128 s = 0, sa = 0;
+            int finite = 1;
+            for (int64_t k = 0; k < K && finite; ++k) {
+                int64_t ia, ib;
+                int ea, eb;
+                finite = e5m2_int(A[m * K + k], &ia, &ea) && e5m2_int(B[n * K + k], &ib, &eb);
+                if (!finite) break;
+                const __int128 p = (__int128)(ia * ib) << (ea + eb + 32);   /* units of 2^-32 */
+                s += p;
+                sa += p < 0 ? -p : p;
+            }
+            if (finite) {
+                C[m * N + n] = ldexp((double)s, -32);
+                Cabs[m * N + n] = ldexp((double)sa, -32);
+            } else {
+                double ds = 0.0, dsa = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const double p = e5m2_value(A[m * K + k]) * e5m2_value(B[n * K + k]);
+                    ds += p;
+                    dsa += fabs(p);
+                }
+                C[m * N + n] = ds;
+                Cabs[m * N + n] = dsa;
+            }
+        }
+    return ORACLE_OK;
+}

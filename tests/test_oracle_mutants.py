@@ -63,11 +63,29 @@ FP8_MUTANTS = [
 ]
 
 
+# Mistakes in the e5m2 oracle, caught by test_oracle_fp8_e5m2.py.
+E5M2_MUTANTS = [
+    ("e5m2 bias 16", "ldexp(4.0 + m, e - 17);\n    return s ? -v : v;",
+     "ldexp(4.0 + m, e - 18);\n    return s ? -v : v;"),
+    ("e5m2 integer bias", "*ie = e == 0 ? -16 : e - 17;", "*ie = e == 0 ? -16 : e - 16;"),
+    ("e5m2 subnormal scale", "const double v = e == 0 ? ldexp((double)m, -16)",
+     "const double v = e == 0 ? ldexp((double)m, -15)"),
+    ("e5m2 overflow saturates", "if (ax >= 61440.0) return sign | 0x7C;", "if (ax >= 61440.0) return sign | 0x7B;"),
+    ("e5m2 overflow early", "if (ax >= 61440.0) return sign | 0x7C;", "if (ax > 57344.0) return sign | 0x7C;"),
+    ("e5m2 ties up", "if (dhi < dlo) return sign | (uint8_t)hi;\n    return sign | (uint8_t)((lo & 1) ? hi : lo);\n}\n\nint oracle_fp8_e5m2_encode",
+     "if (dhi <= dlo) return sign | (uint8_t)hi;\n    return sign | (uint8_t)((lo & 1) ? hi : lo);\n}\n\nint oracle_fp8_e5m2_encode"),
+    ("e5m2 sum in 2^-31 units", "<< (ea + eb + 32);", "<< (ea + eb + 31);"),
+    ("e5m2 product sign lost", "const __int128 p = (__int128)(ia * ib)", "const __int128 p = (__int128)(ia * ib < 0 ? -ia * ib : ia * ib)"),
+    ("e5m2 inf not special", "if (e == 31) return 0;                     /* infinity or NaN */", ";"),
+]
+
+
 @pytest.mark.parametrize("what,old,new,pins",
                          [m + ("tests/test_oracle_pins.py",) for m in MUTANTS] +
                          [m + ("tests/test_oracle_scaled.py",) for m in SCALED_MUTANTS] +
-                         [m + ("tests/test_oracle_fp8.py",) for m in FP8_MUTANTS],
-                         ids=[m[0] for m in MUTANTS + SCALED_MUTANTS + FP8_MUTANTS])
+                         [m + ("tests/test_oracle_fp8.py",) for m in FP8_MUTANTS] +
+                         [m + ("tests/test_oracle_fp8_e5m2.py",) for m in E5M2_MUTANTS],
+                         ids=[m[0] for m in MUTANTS + SCALED_MUTANTS + FP8_MUTANTS + E5M2_MUTANTS])
 def test_pins_catch_planted_mistake(tmp_path, what, old, new, pins):
     for d in ("oracle", "tests", "precision_integer_gemm_amd"):
         shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
