@@ -464,7 +464,7 @@ int oracle_gemm_fp8_e5m2(const uint8_t *A, const uint8_t *B, int64_t M, int64_t 
                 int ea, eb;
                 finite = e5m2_int(A[m * K + k], &ia, &ea) && e5m2_int(B[n * K + k], &ib, &eb);
                 if (!finite) break;
-                const __int128 p = (__int128)(ia * ib) << (ea + eb + 32);   /* units of 2^-32 */
+                const __int128 p = (__int128)(ia * ib) * ((__int128)1 << (ea + eb + 32));   /* units of 2^-32 */
                 s += p;
                 sa += p < 0 ? -p : p;
             }

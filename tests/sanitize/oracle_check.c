@@ -29,6 +29,10 @@ int oracle_fp8_e4m3_decode(const uint8_t *codes, int64_t n, double *out);
 int oracle_fp8_e4m3_encode(const double *x, int64_t n, uint8_t *out);
 int oracle_gemm_fp8(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K, double *C,
                     double *Cabs);
+int oracle_fp8_e5m2_decode(const uint8_t *codes, int64_t n, double *out);
+int oracle_fp8_e5m2_encode(const double *x, int64_t n, uint8_t *out);
+int oracle_gemm_fp8_e5m2(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K,
+                         double *C, double *Cabs);
 
 static uint64_t state = 0x9E3779B97F4A7C15ull;
 static uint64_t next(void)
@@ -99,6 +103,11 @@ static void fp8(int64_t M, int64_t N, int64_t K)
     CHECK(oracle_gemm_fp8(A, B, M, N, K, C, Cabs) == 0);
     uint8_t *enc = alloc((size_t)(M * N));
     CHECK(oracle_fp8_e4m3_encode(C, M * N, enc) == 0);
+    /* e5m2: every byte is a code (infinities and NaNs included) */
+    for (int64_t i = 0; i < M * K; ++i) A[i] = (uint8_t)next();
+    for (int64_t i = 0; i < N * K; ++i) B[i] = (uint8_t)next();
+    CHECK(oracle_gemm_fp8_e5m2(A, B, M, N, K, C, Cabs) == 0);
+    CHECK(oracle_fp8_e5m2_encode(C, M * N, enc) == 0);
     free(A); free(B); free(C); free(Cabs); free(enc);
 }
 
@@ -113,6 +122,8 @@ int main(void)
     CHECK(oracle_fp8_e4m3_decode(all, 256, v) == 0);
     for (int i = 0; i < 256; ++i) if (isnan(v[i])) v[i] = 0.0;
     CHECK(oracle_fp8_e4m3_encode(v, 256, back) == 0);
+    CHECK(oracle_fp8_e5m2_decode(all, 256, v) == 0);
+    CHECK(oracle_fp8_e5m2_encode(v, 256, back) == 0);
     int8_t lg[512];
     CHECK(oracle_unpack_int4(all, 1, 512, lg) == 0);
     CHECK(oracle_pack_int4(lg, 1, 512, back) == 0);
