@@ -20,7 +20,8 @@ write-back a previous workload leaves behind; `per_config_cold` times each
 workload after a 512 MiB read that evicts its operands from L2 and MALL;
 `per_config_scaled_bf16` times the scaled product (per-row and per-column
 scales, bf16 output) of each workload alone; `per_config_fp8` times the second
-workload, the fp8 (e4m3) GEMM with fp32 output, at 4096^3 and 8192^3, and
+workload, the fp8 GEMM (e4m3 and e5m2 operands) with fp32 output, at 4096^3
+and 8192^3, and
 `per_config_long_k` W4A8 decode shapes with K = 28672 on the narrow-M kernel's
 split-K path (both outside the step and `value`).  `ceiling` holds what the chip sustains, measured
 live by the probe kernels of _ceiling.so (matrix cores only, per format; LDS
@@ -536,32 +537,33 @@ def main() -> int:
                               "roofline_frac": round(max(t_mfma, t_hbm) / (med * 1e-6), 4)}
             del copies, D
 
-    # The second workload, the fp8 (e4m3) GEMM with fp32 accumulation and
-    # fp32 output, alone (not part of the step or of `value`): priced at the
+    # The second workload, the fp8 GEMM (e4m3 and e5m2 operands) with fp32
+    # accumulation and fp32 output, alone (not part of the step or of `value`): priced at the
     # 5.0 PFLOP/s dense fp8 peak.
     fp8 = {}
     if args.isolated_reps > 0:
         from precision_integer_gemm_amd.inputs import fp8_codes
-        for (fm, fn_, fk) in ((4096, 4096, 4096), (8192, 8192, 8192)):
-            a8 = torch.from_numpy(fp8_codes(fm + fk, 0, fm, fk)).to(dev)
-            b8 = torch.from_numpy(fp8_codes(fm + fk, 1, fn_, fk)).to(dev)
+        for fmt, (fm, fn_, fk) in [(f, s) for f in ("e4m3", "e5m2")
+                                   for s in ((4096, 4096, 4096), (8192, 8192, 8192))]:
+            a8 = torch.from_numpy(fp8_codes(fm + fk, 0, fm, fk, fmt)).to(dev)
+            b8 = torch.from_numpy(fp8_codes(fm + fk, 1, fn_, fk, fmt)).to(dev)
             c8 = torch.empty((fm, fn_), dtype=torch.float32, device=dev)
+            entry = L.lib().lpgemm_fp8_e4m3 if fmt == "e4m3" else L.lib().lpgemm_fp8_e5m2
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.isolated_reps)]
             for j in range(-1, args.isolated_reps):
                 if j >= 0:
                     evs[j][0].record(stream)
-                st = L.lib().lpgemm_fp8_e4m3(a8.data_ptr(), b8.data_ptr(), c8.data_ptr(), L.OUT_F32,
-                                             fm, fn_, fk, handle)
+                st = entry(a8.data_ptr(), b8.data_ptr(), c8.data_ptr(), L.OUT_F32, fm, fn_, fk, handle)
                 if j >= 0:
                     evs[j][1].record(stream)
                 if st != L.OK:
-                    raise RuntimeError(f"fp8 {fm}x{fn_}x{fk}: {L.lpgemm_status_string(st)}")
+                    raise RuntimeError(f"fp8 {fmt} {fm}x{fn_}x{fk}: {L.lpgemm_status_string(st)}")
             torch.cuda.synchronize()
             us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
             med = float(np.median(us))
             tops = 2.0 * fm * fn_ * fk / (med * 1e-6) / 1e12
-            fp8[f"fp8_e4m3_{fm}x{fn_}x{fk}"] = {
+            fp8[f"fp8_{fmt}_{fm}x{fn_}x{fk}"] = {
                 "out": "f32", "median_us": round(med, 3), "min_us": round(float(us.min()), 3),
                 "tops": round(tops, 2), "bound": "mfma", "mfma_peak_tops": PEAK_FP8_TOPS,
                 "roofline_frac": round(tops / PEAK_FP8_TOPS, 4)}

@@ -196,7 +196,8 @@ typedef enum lpgemm_out_dtype LPGEMM_ENUM_BASE {
     LPGEMM_OUT_F32 = 0,     /* IEEE binary32                               */
     LPGEMM_OUT_BF16 = 1,    /* bfloat16 bits (upper half of a binary32)    */
     LPGEMM_OUT_F16 = 2,     /* IEEE binary16                               */
-    LPGEMM_OUT_FP8_E4M3 = 3 /* e4m3 byte (lpgemm_fp8_e4m3 only)            */
+    LPGEMM_OUT_FP8_E4M3 = 3, /* e4m3 byte (lpgemm_fp8_e4m3 only)           */
+    LPGEMM_OUT_FP8_E5M2 = 4  /* e5m2 byte (lpgemm_fp8_e5m2 only)           */
 } lpgemm_out_dtype;
 
 /*
@@ -280,6 +281,38 @@ lpgemm_status lpgemm_int4_int4_scaled_ws(const void *A_packed, const void *B_pac
  * accumulator, C stored in the fp8 dtype.
  */
 lpgemm_status lpgemm_fp8_e4m3(const uint8_t *A, const uint8_t *B, void *C,
+                              lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                              hipStream_t stream);
+
+/*
+ * fp8 GEMM with e5m2 operands (the tutorial's gemm_fp8 takes "e4m3 / e5m2"
+ * into a float32 accumulator):  C[m][n] = out( sum_k a(m,k) * b(n,k) )
+ *   A          device, e5m2 bytes [M][K]
+ *   B          device, e5m2 bytes [N][K]
+ *   C          device, [M][N] binary32 (LPGEMM_OUT_F32) or e5m2 bytes
+ *              (LPGEMM_OUT_FP8_E5M2), written
+ *   M, N, K    any sizes >= 0, K <= LPGEMM_MAX_K
+ * E5M2 is the OCP 8-bit format with infinities (the upper byte of an IEEE
+ * binary16): sign, 5 exponent bits (bias 15), 2 mantissa bits; exponent 0 is
+ * subnormal (smallest 2^-16); exponent 31 is infinity (mantissa 0) or NaN;
+ * the largest finite magnitude is 57344.  Every product is exact in binary32
+ * and no sum of finite products overflows it.  Infinities and NaNs follow
+ * IEEE arithmetic: an infinite operand gives an infinite product (NaN against
+ * zero), opposite infinities in one sum give NaN, a NaN operand gives NaN.
+ * The accuracy of finite results is that of lpgemm_fp8_e4m3, with e(x) the
+ * binary exponent of an e5m2 code (-14 for subnormals): measured on MI355X,
+ * the matrix-core instruction sums e5m2 products in the same groups of 8 k
+ * with the same truncation to a multiple of 2^(E-13), so
+ *     |C - S| <= 7 * sum_groups 2^(EA + EB - 13) + 1.01 * K * 2^-24 * P
+ * for the matrix-core kernel and |C - S| <= 1.01 * K * 2^-24 * P for the
+ * one-thread-per-element kernel.
+ * An e5m2 result rounds the binary32 result to nearest, ties to even;
+ * magnitudes from 61440 (the midpoint above 57344) become infinities, NaN
+ * stays NaN.  K == 0 writes zeros.  Return codes and the choice of kernel as
+ * for lpgemm_fp8_e4m3 (with LPGEMM_OUT_FP8_E5M2 as the only fp8 out_dtype;
+ * C aligned to 16 bytes for binary32, 4 for e5m2, for the tiled kernel).
+ */
+lpgemm_status lpgemm_fp8_e5m2(const uint8_t *A, const uint8_t *B, void *C,
                               lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
                               hipStream_t stream);
 

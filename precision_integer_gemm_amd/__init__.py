@@ -13,7 +13,7 @@ from ._binding import (  # noqa: F401
     ERR_HIP, ERR_INVALID_ARG, ERR_SCRATCH_LIMIT, ERR_UNSUPPORTED, EXPORTS, KERNEL_AUTO, KERNEL_GENERAL,
     KERNEL_FP6, KERNEL_NAMES, KERNEL_SKINNY, KERNEL_TILED, KERNEL_TILED_128, KERNEL_TILED_256, KERNEL_TILED_64,
     LIB_PATH, MAX_K,
-    OK, OUT_BF16, OUT_F16, OUT_F32, OUT_FP8_E4M3, VARIANT_I4I4, VARIANT_W4A8, LpgemmError, lib,
-    lpgemm_fp8_e4m3, lpgemm_int4_int4, lpgemm_int4_int4_scaled, lpgemm_pack_int4, lpgemm_plan,
+    OK, OUT_BF16, OUT_F16, OUT_F32, OUT_FP8_E4M3, OUT_FP8_E5M2, VARIANT_I4I4, VARIANT_W4A8, LpgemmError, lib,
+    lpgemm_fp8_e4m3, lpgemm_fp8_e5m2, lpgemm_int4_int4, lpgemm_int4_int4_scaled, lpgemm_pack_int4, lpgemm_plan,
     lpgemm_set_kernel_override, lpgemm_status_string, lpgemm_unpack_int4, lpgemm_w4a8,
     lpgemm_w4a8_scaled, lpgemm_workspace_size, SIZE_MAX, STATIC_SCRATCH_BYTES, WORKSPACE_ALIGN)

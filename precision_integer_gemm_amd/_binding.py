@@ -23,13 +23,13 @@ KERNEL_NAMES = {KERNEL_AUTO: "auto", KERNEL_GENERAL: "general", KERNEL_TILED: "t
 # lpgemm_variant
 VARIANT_I4I4, VARIANT_W4A8 = 0, 1
 # lpgemm_out_dtype
-OUT_F32, OUT_BF16, OUT_F16, OUT_FP8_E4M3 = 0, 1, 2, 3
+OUT_F32, OUT_BF16, OUT_F16, OUT_FP8_E4M3, OUT_FP8_E5M2 = 0, 1, 2, 3, 4
 MAX_K = 131070
 
 EXPORTS = ("lpgemm_int4_int4", "lpgemm_w4a8", "lpgemm_int4_int4_ws", "lpgemm_w4a8_ws",
            "lpgemm_int4_int4_noalloc",
            "lpgemm_workspace_size", "lpgemm_int4_int4_scaled", "lpgemm_w4a8_scaled",
-           "lpgemm_int4_int4_scaled_ws", "lpgemm_fp8_e4m3", "lpgemm_pack_int4",
+           "lpgemm_int4_int4_scaled_ws", "lpgemm_fp8_e4m3", "lpgemm_fp8_e5m2", "lpgemm_pack_int4",
            "lpgemm_unpack_int4", "lpgemm_status_string", "lpgemm_plan",
            "lpgemm_set_kernel_override")
 SIZE_MAX = 2 ** 64 - 1
@@ -94,8 +94,9 @@ def lib() -> ctypes.CDLL:
         f.restype = ctypes.c_int
     L.lpgemm_int4_int4_scaled_ws.argtypes = [p, p, p, p, p, ctypes.c_int, i64, i64, i64, p, sz, p]
     L.lpgemm_int4_int4_scaled_ws.restype = ctypes.c_int
-    L.lpgemm_fp8_e4m3.argtypes = [p, p, p, ctypes.c_int, i64, i64, i64, p]
-    L.lpgemm_fp8_e4m3.restype = ctypes.c_int
+    for name in ("lpgemm_fp8_e4m3", "lpgemm_fp8_e5m2"):
+        getattr(L, name).argtypes = [p, p, p, ctypes.c_int, i64, i64, i64, p]
+        getattr(L, name).restype = ctypes.c_int
     for name in ("lpgemm_pack_int4", "lpgemm_unpack_int4"):
         f = getattr(L, name)
         f.argtypes = [p, p, i64, i64, p]
@@ -323,12 +324,9 @@ def lpgemm_w4a8_scaled(A, B_packed, scale_a, scale_b, *, dtype=None, out=None, s
     return D
 
 
-def lpgemm_fp8_e4m3(A, B, *, dtype=None, out=None, stream=None):
-    """C[M,N] = A . B^T of e4m3 operands (uint8 codes or torch.float8_e4m3fn
-    tensors [M,K] and [N,K]) with fp32 accumulation; C as float32 (default) or
-    e4m3 codes (dtype=torch.uint8 or torch.float8_e4m3fn)."""
+def _fp8_gemm(name, f8_name, own_code, A, B, dtype, out, stream):
     torch = _torch()
-    f8 = getattr(torch, "float8_e4m3fn", None)
+    f8 = getattr(torch, f8_name, None)
     ok = (torch.uint8,) + ((f8,) if f8 is not None else ())
     _check_dev(A, "A", ok)
     _check_dev(B, "B", ok)
@@ -340,9 +338,9 @@ def lpgemm_fp8_e4m3(A, B, *, dtype=None, out=None, stream=None):
     if dtype == torch.float32:
         code = OUT_F32
     elif dtype in ok:
-        code = OUT_FP8_E4M3
+        code = own_code
     else:
-        raise TypeError("dtype must be torch.float32, torch.uint8 or torch.float8_e4m3fn")
+        raise TypeError(f"dtype must be torch.float32, torch.uint8 or torch.{f8_name}")
     if out is None:
         C = torch.empty((M, N), dtype=dtype, device=A.device)
     else:
@@ -350,9 +348,23 @@ def lpgemm_fp8_e4m3(A, B, *, dtype=None, out=None, stream=None):
         if tuple(out.shape) != (M, N):
             raise ValueError(f"out must have shape ({M}, {N}), got {tuple(out.shape)}")
         C = out
-    _raise(lib().lpgemm_fp8_e4m3(A.data_ptr(), B.data_ptr(), C.data_ptr(), code, M, N, K,
-                                 _stream_handle(stream)), "lpgemm_fp8_e4m3")
+    _raise(getattr(lib(), name)(A.data_ptr(), B.data_ptr(), C.data_ptr(), code, M, N, K,
+                                _stream_handle(stream)), name)
     return C
+
+
+def lpgemm_fp8_e4m3(A, B, *, dtype=None, out=None, stream=None):
+    """C[M,N] = A . B^T of e4m3 operands (uint8 codes or torch.float8_e4m3fn
+    tensors [M,K] and [N,K]) with fp32 accumulation; C as float32 (default) or
+    e4m3 codes (dtype=torch.uint8 or torch.float8_e4m3fn)."""
+    return _fp8_gemm("lpgemm_fp8_e4m3", "float8_e4m3fn", OUT_FP8_E4M3, A, B, dtype, out, stream)
+
+
+def lpgemm_fp8_e5m2(A, B, *, dtype=None, out=None, stream=None):
+    """C[M,N] = A . B^T of e5m2 operands (uint8 codes or torch.float8_e5m2
+    tensors [M,K] and [N,K]) with fp32 accumulation; C as float32 (default) or
+    e5m2 codes (dtype=torch.uint8 or torch.float8_e5m2)."""
+    return _fp8_gemm("lpgemm_fp8_e5m2", "float8_e5m2", OUT_FP8_E5M2, A, B, dtype, out, stream)
 
 
 def lpgemm_pack_int4(logical, *, out=None, stream=None):

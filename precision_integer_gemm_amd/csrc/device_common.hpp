@@ -22,9 +22,13 @@
 
 namespace lpgemm {
 
-// Operand formats: int4 x int4, int8 A with packed int4 B, and e4m3 fp8 A and
-// B (the second workload: fp32 accumulation, fp32 or e4m3 output).
-enum Variant { I4I4 = 0, W4A8 = 1, FP8 = 2 };
+// Operand formats: int4 x int4, int8 A with packed int4 B, and the fp8 GEMM
+// (the second workload: fp32 accumulation) with e4m3 (FP8) or e5m2 (BF8) A
+// and B.
+enum Variant { I4I4 = 0, W4A8 = 1, FP8 = 2, BF8 = 3 };
+
+// One byte per element on both operands, floating point.
+constexpr bool is_fp8(int var) { return var == FP8 || var == BF8; }
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
@@ -48,17 +52,20 @@ __device__ __forceinline__ i32x4 mfma_16x16x64(i32x4 s0, i32x4 s1, i32x4 acc)
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
-// D(32x32, fp32) += S0(32 rows, 64 k) * S1(64 k, 32 cols), both operands e4m3:
-// S0 lane l: row l%32, S1 lane l: column l%32, each the 32 consecutive k from
-// 32 (l / 32), as two 16-byte halves (lo: the first 16 k).  Products are exact
-// in fp32; the sums are rounded in fp32.  D layout as mfma_32x32x32.
+// D(32x32, fp32) += S0(32 rows, 64 k) * S1(64 k, 32 cols), both operands fp8
+// (FMT 0: e4m3, 1: e5m2, the f8f6f4 MFMA's operand format codes): S0 lane l:
+// row l%32, S1 lane l: column l%32, each the 32 consecutive k from 32 (l / 32),
+// as two 16-byte halves (lo: the first 16 k).  Products are exact in fp32; the
+// sums are not IEEE binary32 (see the fp8 entry points' accuracy contract).
+// D layout as mfma_32x32x32.
+template <int FMT>
 __device__ __forceinline__ f32x16 mfma_32x32x64_fp8(i32x4 s0_lo, i32x4 s0_hi, i32x4 s1_lo,
                                                     i32x4 s1_hi, f32x16 acc)
 {
     const i32x8 s0 = {s0_lo.x, s0_lo.y, s0_lo.z, s0_lo.w, s0_hi.x, s0_hi.y, s0_hi.z, s0_hi.w};
     const i32x8 s1 = {s1_lo.x, s1_lo.y, s1_lo.z, s1_lo.w, s1_hi.x, s1_hi.y, s1_hi.z, s1_hi.w};
-    // operand formats 0 / 0: e4m3 x e4m3; scales 2^0 (E8M0 exponent 127)
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(s0, s1, acc, 0, 0, 0, 127, 0, 127);
+    // scales 2^0 (E8M0 exponent 127) on both operands
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(s0, s1, acc, FMT, FMT, 0, 127, 0, 127);
 }
 
 // Split order: 8 nibbles of `d` -> the 4 even-k values (x16) then the 4 odd-k
@@ -140,7 +147,7 @@ __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint
 //     D[m][n] = out(((float)C[m][n] * scale_a[m]) * scale_b[n])
 // where (float) and both multiplies round to nearest even in fp32 and out()
 // converts to fp32 (identity), bf16 or fp16, rounding to nearest even.
-enum OutFormat { OUT_I32 = 0, OUT_F32 = 1, OUT_BF16 = 2, OUT_F16 = 3, OUT_E4M3 = 4 };
+enum OutFormat { OUT_I32 = 0, OUT_F32 = 1, OUT_BF16 = 2, OUT_F16 = 3, OUT_E4M3 = 4, OUT_E5M2 = 5 };
 
 struct Epilogue {
     void *out;             // D (or C), row-major [M][N]
@@ -309,8 +316,42 @@ __device__ __forceinline__ uint32_t float_to_e4m3(float x)
     return s | (uint32_t)__builtin_rintf(__uint_as_float(ax) * 512.0f);
 }
 
+// ---- fp8 (e5m2) values -----------------------------------------------------
+// E5M2 as in the OCP 8-bit formats (the top byte of an IEEE binary16): bit 7
+// sign, bits 6..2 exponent (bias 15), bits 1..0 mantissa; exponent 0
+// subnormal (m * 2^-16); exponent 31 infinity (m = 0) or NaN; largest finite
+// 57344.
+
+// Value of code c.
+__device__ __forceinline__ float e5m2_to_float(uint32_t c)
+{
+    const uint32_t s = (c & 0x80u) << 24, e = (c >> 2) & 31u, m = c & 3u;
+    if (e == 31u) return __uint_as_float(s | (m ? 0x7FC00000u : 0x7F800000u));
+    if (e == 0u) return __uint_as_float(s | __float_as_uint((float)m * 1.52587890625e-05f));  // m * 2^-16
+    return __uint_as_float(s | ((e + 112u) << 23) | (m << 21));
+}
+
+// Nearest code of x, ties to even; magnitudes from 61440 (the midpoint above
+// the largest finite value, which ties to the even neighbour 2^16) become
+// infinity; NaN gives a NaN code with x's sign.
+__device__ __forceinline__ uint32_t float_to_e5m2(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t s = (u >> 24) & 0x80u, ax = u & 0x7FFFFFFFu;
+    if (ax > 0x7F800000u) return s | 0x7Fu;
+    if (ax >= 0x47700000u) return s | 0x7Cu;  // 61440 and beyond (inf included)
+    if (ax >= 0x38800000u) {                    // normal: |x| >= 2^-14
+        // keep 2 mantissa bits, nearest-even on the 21 dropped ones
+        const uint32_t r = (ax + 0xFFFFFu + ((ax >> 21) & 1u)) >> 21;
+        return s | (r - (112u << 2));
+    }
+    // subnormal: quantum 2^-16; the product is exact, rint rounds to even
+    return s | (uint32_t)__builtin_rintf(__uint_as_float(ax) * 65536.0f);
+}
+
 // Store fp32 results v[i] for columns n .. n+3 of row m (columns >= N
-// skipped) as fp32 or e4m3.  Vector stores when all four exist and N % 4 == 0.
+// skipped) as fp32, e4m3 or e5m2.  Vector stores when all four exist and
+// N % 4 == 0.
 template <int OUT>
 __device__ __forceinline__ void store_row4f(const Epilogue &e, int64_t m, int N, int n, const float (&v)[4])
 {
@@ -328,13 +369,14 @@ __device__ __forceinline__ void store_row4f(const Epilogue &e, int64_t m, int N,
         }
     } else {
         uint8_t *row = static_cast<uint8_t *>(e.out) + m * N;
+        auto enc = [](float f) { return OUT == OUT_E5M2 ? float_to_e5m2(f) : float_to_e4m3(f); };
         if (vec) {
-            *reinterpret_cast<uint32_t *>(row + n) = float_to_e4m3(v[0]) | (float_to_e4m3(v[1]) << 8) |
-                                                      (float_to_e4m3(v[2]) << 16) | (float_to_e4m3(v[3]) << 24);
+            *reinterpret_cast<uint32_t *>(row + n) = enc(v[0]) | (enc(v[1]) << 8) | (enc(v[2]) << 16) |
+                                                      (enc(v[3]) << 24);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (n + i < N) row[n + i] = (uint8_t)float_to_e4m3(v[i]);
+                if (n + i < N) row[n + i] = (uint8_t)enc(v[i]);
         }
     }
 }

@@ -46,9 +46,10 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(const uint8_t *__rest
     }
 }
 
-// fp8 (e4m3) product, one thread per output: exact products summed in fp32 in
-// k order; fp32 or e4m3 output.  Any K and alignment.
-template <int OUT>
+// fp8 product (VAR: FP8 e4m3 or BF8 e5m2 operands), one thread per output:
+// exact products summed in fp32 in k order; fp32 output, or the operands' fp8
+// format (OUT_E4M3 / OUT_E5M2).  Any K and alignment.
+template <int VAR, int OUT>
 __global__ __launch_bounds__(256) void gemm_fp8_general_kernel(const uint8_t *__restrict__ A,
                                                                const uint8_t *__restrict__ B,
                                                                Epilogue epi, int64_t M, int64_t N,
@@ -58,15 +59,17 @@ __global__ __launch_bounds__(256) void gemm_fp8_general_kernel(const uint8_t *__
     const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
     if (m >= M || n >= N) return;
     const uint8_t *arow = A + m * K, *brow = B + n * K;
+    auto dec = [](uint32_t c) { return VAR == BF8 ? e5m2_to_float(c) : e4m3_to_float(c); };
     float sum = 0.f;
     for (int64_t k = 0; k < K; ++k) {
-        const float p = e4m3_to_float(arow[k]) * e4m3_to_float(brow[k]);  // exact
+        const float p = dec(arow[k]) * dec(brow[k]);  // exact
         sum += p;
     }
     if (OUT == OUT_F32)
         static_cast<float *>(epi.out)[m * N + n] = sum;
     else
-        static_cast<uint8_t *>(epi.out)[m * N + n] = (uint8_t)float_to_e4m3(sum);
+        static_cast<uint8_t *>(epi.out)[m * N + n] =
+            (uint8_t)(OUT == OUT_E5M2 ? float_to_e5m2(sum) : float_to_e4m3(sum));
 }
 
 // C[0 .. count) = 0: the empty sum (K == 0).  A kernel, not a memset, so the

@@ -55,7 +55,7 @@ struct PipeCfg {
     static constexpr int BM = WM * FM * 32;
     static constexpr int BN = WN * FN * 32;
     static constexpr int RA = (VAR == I4I4) ? BK / 2 : BK;  // LDS bytes per A row
-    static constexpr int RB = (VAR == FP8) ? BK : BK / 2;   // LDS bytes per B row
+    static constexpr int RB = is_fp8(VAR) ? BK : BK / 2;   // LDS bytes per B row
     static constexpr int CPR_A = RA / 16;
     static constexpr int CPR_B = RB / 16;
     static constexpr int A_BYTES = BM * RA;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     const int wn = wave % WN;
 
     const uint32_t lda = (VAR == I4I4) ? (uint32_t)K / 2 : (uint32_t)K;  // global row bytes
-    const uint32_t ldb = (VAR == FP8) ? (uint32_t)K : (uint32_t)K / 2;
+    const uint32_t ldb = is_fp8(VAR) ? (uint32_t)K : (uint32_t)K / 2;
     // This workgroup's K range [k0, k0 + klen) (all of K unless SPLIT), and its
     // offset and length in bytes of an A row and a B row.
     const int nblocks = tiles_m * tiles_n;
@@ -115,9 +115,9 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     const int k0 = chunk * kc;
     const int klen = SPLIT ? min(kc, K - k0) : K;
     const uint32_t a_k0 = (VAR == I4I4) ? (uint32_t)k0 / 2 : (uint32_t)k0;
-    const uint32_t b_k0 = (VAR == FP8) ? (uint32_t)k0 : (uint32_t)k0 / 2;
+    const uint32_t b_k0 = is_fp8(VAR) ? (uint32_t)k0 : (uint32_t)k0 / 2;
     const uint32_t a_len = (VAR == I4I4) ? (uint32_t)klen / 2 : (uint32_t)klen;
-    const uint32_t b_len = (VAR == FP8) ? (uint32_t)klen : (uint32_t)klen / 2;
+    const uint32_t b_len = is_fp8(VAR) ? (uint32_t)klen : (uint32_t)klen / 2;
     const int ktiles = (klen + BK - 1) / BK;
     // Where the tile's results go: C, or this range's workspace slice.
     Epilogue epo = epi;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     // Raw (still packed / int8 / fp8) fragments of one 64-k step, as read
     // from LDS: 16 bytes of a 4-bit row, 32 bytes of a byte-wide row.
     constexpr int AV = (VAR == I4I4) ? 1 : 2;  // 16-byte vectors per A block row
-    constexpr int BV = (VAR == FP8) ? 2 : 1;   // 16-byte vectors per B block row
+    constexpr int BV = is_fp8(VAR) ? 2 : 1;   // 16-byte vectors per B block row
     struct Frags {
         i32x4 b[FN][BV];
         i32x4 a[FM][AV];
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
             const int row = (wn * FN + fn) * 32 + r32;
 #pragma unroll
             for (int v = 0; v < BV; ++v) {
-                const int col = (VAR == FP8) ? 4 * step + 2 * h + v : 2 * step + h;
+                const int col = is_fp8(VAR) ? 4 * step + 2 * h + v : 2 * step + h;
                 f.b[fn][v] = *reinterpret_cast<const i32x4 *>(sb + 16 * lds_chunk<CPR_B>(row, col));
             }
         }
@@ -223,17 +223,17 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     };
 
     // Integer accumulators for the int4 / int8 formats, fp32 for fp8.
-    using Acc = typename std::conditional<VAR == FP8, f32x16, i32x16>::type;
+    using Acc = typename std::conditional<is_fp8(VAR), f32x16, i32x16>::type;
     Acc acc[FN][FM];
     // Unpack and contract one 64-k step: per block two 32x32x32 int8 MFMAs,
     // or one 32x32x64 fp8 MFMA (lane l: 32 consecutive k, 32 (l / 32) onward).
     auto compute = [&](const Frags &f) {
-        if constexpr (VAR == FP8) {
+        if constexpr (is_fp8(VAR)) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm)
-                    acc[fn][fm] = mfma_32x32x64_fp8(f.b[fn][0], f.b[fn][BV - 1], f.a[fm][0],
+                    acc[fn][fm] = mfma_32x32x64_fp8<VAR == BF8 ? 1 : 0>(f.b[fn][0], f.b[fn][BV - 1], f.a[fm][0],
                                                     f.a[fm][AV - 1], acc[fn][fm]);
         } else {
             i32x4 a_lo[FM], a_hi[FM];
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
 #pragma unroll
                     for (int rg = 0; rg < 4; ++rg) {
                         const int n = tn0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h;
-                        if constexpr (VAR == FP8) {
+                        if constexpr (is_fp8(VAR)) {
                             const float c[4] = {acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
                                                 acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]};
                             store_row4f<OUT>(epi, m, N, n, c);

@@ -62,11 +62,11 @@ using I4Small = TiledKernel<I4I4, 2, 2, 2, 2, 128, 3>;
 using W8Small = TiledKernel<W4A8, 2, 2, 2, 2, 128, 3>;
 using I4Tiny = TiledKernel<I4I4, 1, 1, 2, 2, 256, 2>;
 using W8Tiny = TiledKernel<W4A8, 1, 1, 2, 2, 256, 2>;
-// fp8 (e4m3): one byte per element on both operands, the W4A8 kernel's A side
-// for both; 128 k per LDS stage.
-using F8Large = TiledKernel<FP8, 4, 2, 2, 4, 128, 2>;
-using F8Small = TiledKernel<FP8, 2, 2, 2, 2, 128, 3>;
-using F8Tiny = TiledKernel<FP8, 1, 1, 2, 2, 128, 2>;
+// fp8 (FP8: e4m3, BF8: e5m2): one byte per element on both operands, the
+// W4A8 kernel's A side for both; 128 k per LDS stage.
+template <int VAR> using F8Large = TiledKernel<VAR, 4, 2, 2, 4, 128, 2>;
+template <int VAR> using F8Small = TiledKernel<VAR, 2, 2, 2, 2, 128, 3>;
+template <int VAR> using F8Tiny = TiledKernel<VAR, 1, 1, 2, 2, 128, 2>;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 // FP6 path (gemm_fp6.hpp): 256 x 256 tiles, 8 waves of 128 (m) x 64 (n), three
@@ -622,9 +622,10 @@ lpgemm_status run_gemm(lpgemm_variant variant, const void *A, const void *B, voi
     }
 }
 
-// fp8 (e4m3) product: its own argument rules (no packing, any K), the tiled
-// kernel when the operands allow 16-byte staging, else the general kernel.
-template <int OUT>
+// fp8 product (VAR: FP8 or BF8): its own argument rules (no packing, any K),
+// the tiled kernel when the operands allow 16-byte staging, else the general
+// kernel.
+template <int VAR, int OUT>
 lpgemm_status launch_fp8(const uint8_t *A, const uint8_t *B, void *C, int64_t M, int64_t N,
                          int64_t K, hipStream_t stream)
 {
@@ -640,7 +641,7 @@ lpgemm_status launch_fp8(const uint8_t *A, const uint8_t *B, void *C, int64_t M,
     if (!fast || forced == LPGEMM_KERNEL_GENERAL) {
         if (ceil_div(M, 16) > 65535 || ceil_div(N, 16) > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
         const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16));
-        hipLaunchKernelGGL(gemm_fp8_general_kernel<OUT>, grid, dim3(256), 0, stream, A, B, epi, M, N, K);
+        hipLaunchKernelGGL((gemm_fp8_general_kernel<VAR, OUT>), grid, dim3(256), 0, stream, A, B, epi, M, N, K);
         return launched();
     }
     const int cu = device_cu_count();
@@ -663,23 +664,28 @@ lpgemm_status launch_fp8(const uint8_t *A, const uint8_t *B, void *C, int64_t M,
     if (p.workgroups > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
     if (p.tile == 256) p.workgroups = std::min<int64_t>(p.workgroups, cu);
     const int m = (int)M, n = (int)N, k = (int)K;
-    return p.tile == 256 ? launch_tiled<F8Large, OUT>(p, A, B, epi, m, n, k, nullptr, stream)
-           : p.tile == 128 ? launch_tiled<F8Small, OUT>(p, A, B, epi, m, n, k, nullptr, stream)
-                           : launch_tiled<F8Tiny, OUT>(p, A, B, epi, m, n, k, nullptr, stream);
+    return p.tile == 256 ? launch_tiled<F8Large<VAR>, OUT>(p, A, B, epi, m, n, k, nullptr, stream)
+           : p.tile == 128 ? launch_tiled<F8Small<VAR>, OUT>(p, A, B, epi, m, n, k, nullptr, stream)
+                           : launch_tiled<F8Tiny<VAR>, OUT>(p, A, B, epi, m, n, k, nullptr, stream);
 }
 
+// VAR: FP8 (e4m3 operands, F32 or FP8_E4M3 output) or BF8 (e5m2 operands,
+// F32 or FP8_E5M2 output).
+template <int VAR>
 lpgemm_status run_fp8(const uint8_t *A, const uint8_t *B, void *C, lpgemm_out_dtype out_dtype,
                       int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {
+    const lpgemm_out_dtype own = VAR == BF8 ? LPGEMM_OUT_FP8_E5M2 : LPGEMM_OUT_FP8_E4M3;
     if (M < 0 || N < 0 || K < 0) return LPGEMM_ERR_INVALID_ARG;
-    if (out_dtype != LPGEMM_OUT_F32 && out_dtype != LPGEMM_OUT_FP8_E4M3) return LPGEMM_ERR_INVALID_ARG;
+    if (out_dtype != LPGEMM_OUT_F32 && out_dtype != own) return LPGEMM_ERR_INVALID_ARG;
     if (K > LPGEMM_MAX_K) return LPGEMM_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return LPGEMM_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return LPGEMM_ERR_INVALID_ARG;
     if (M > INT32_MAX || N > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
     (void)hipGetLastError();
-    return out_dtype == LPGEMM_OUT_F32 ? launch_fp8<OUT_F32>(A, B, C, M, N, K, stream)
-                                       : launch_fp8<OUT_E4M3>(A, B, C, M, N, K, stream);
+    constexpr int OWN = VAR == BF8 ? OUT_E5M2 : OUT_E4M3;
+    return out_dtype == LPGEMM_OUT_F32 ? launch_fp8<VAR, OUT_F32>(A, B, C, M, N, K, stream)
+                                       : launch_fp8<VAR, OWN>(A, B, C, M, N, K, stream);
 }
 
 // lpgemm_out_dtype -> OutFormat; -1 for an unknown value.
@@ -689,7 +695,8 @@ int out_format_of(lpgemm_out_dtype d)
     case LPGEMM_OUT_F32: return OUT_F32;
     case LPGEMM_OUT_BF16: return OUT_BF16;
     case LPGEMM_OUT_F16: return OUT_F16;
-    case LPGEMM_OUT_FP8_E4M3: return -1;  // fp8 entry point only
+    case LPGEMM_OUT_FP8_E4M3:
+    case LPGEMM_OUT_FP8_E5M2: return -1;  // fp8 entry points only
     }
     return -1;
 }
@@ -806,7 +813,14 @@ lpgemm_status lpgemm_fp8_e4m3(const uint8_t *A, const uint8_t *B, void *C,
                               lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
                               hipStream_t stream)
 {
-    return run_fp8(A, B, C, out_dtype, M, N, K, stream);
+    return run_fp8<FP8>(A, B, C, out_dtype, M, N, K, stream);
+}
+
+lpgemm_status lpgemm_fp8_e5m2(const uint8_t *A, const uint8_t *B, void *C,
+                              lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                              hipStream_t stream)
+{
+    return run_fp8<BF8>(A, B, C, out_dtype, M, N, K, stream);
 }
 
 lpgemm_status lpgemm_pack_int4(const int8_t *logical, uint8_t *packed, int64_t rows, int64_t K,

@@ -127,10 +127,18 @@ def scale_vector(seed: int, which: int, n: int, lo_exp: int = -12, hi_exp: int =
     return bits.view(np.float32)
 
 
-def fp8_codes(seed: int, which: int, rows: int, K: int) -> np.ndarray:
-    """Uniform random e4m3 bytes [rows, K] for the fp8 workload (which = 0: A,
-    1: B), drawn from stream (seed << 8) | which; the two NaN codes
-    (S.1111.111) are replaced by the code with the same sign and exponent and
-    mantissa 0, so every operand is finite."""
+def fp8_codes(seed: int, which: int, rows: int, K: int, fmt: str = "e4m3") -> np.ndarray:
+    """Uniform random fp8 bytes [rows, K] for the fp8 workload (which = 0: A,
+    1: B), drawn from stream (seed << 8) | which, every operand finite: for
+    e4m3 the two NaN codes (S.1111.111) are replaced by the code with the
+    same sign and exponent and mantissa 0; for e5m2 the infinity and NaN codes
+    (exponent field 31) by the codes of the largest finite binade with the
+    same sign and mantissa."""
     c = random_bytes(operand_stream(seed, which), rows * K)
-    return np.where((c & 0x7F) == 0x7F, c & 0xF8, c).astype(np.uint8).reshape(rows, K)
+    if fmt == "e4m3":
+        c = np.where((c & 0x7F) == 0x7F, c & 0xF8, c)
+    elif fmt == "e5m2":
+        c = np.where((c & 0x7C) == 0x7C, c & 0xFB, c)
+    else:
+        raise ValueError(f"unknown fp8 format {fmt!r}")
+    return c.astype(np.uint8).reshape(rows, K)

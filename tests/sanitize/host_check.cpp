@@ -84,6 +84,8 @@ int main()
         CHECK(lpgemm_int4_int4_noalloc(P, P, C, 4, 4, K, nullptr) != LPGEMM_OK);
         CHECK(lpgemm_fp8_e4m3((const uint8_t *)P, (const uint8_t *)P, C, LPGEMM_OUT_F32, 4, 4, K < 0 ? K : 131071,
                               nullptr) != LPGEMM_OK);
+        CHECK(lpgemm_fp8_e5m2((const uint8_t *)P, (const uint8_t *)P, C, LPGEMM_OUT_F32, 4, 4, K < 0 ? K : 131071,
+                              nullptr) != LPGEMM_OK);
     }
     CHECK(lpgemm_int4_int4(P, P, nullptr, 4, 4, 32, nullptr) == LPGEMM_ERR_INVALID_ARG);
     CHECK(lpgemm_int4_int4_ws(P, P, C, 4, 4, 32, nullptr, 64, nullptr) == LPGEMM_ERR_INVALID_ARG);
@@ -94,6 +96,10 @@ int main()
                              (lpgemm_out_dtype)9, 4, 4, 32, nullptr) == LPGEMM_ERR_INVALID_ARG);
     CHECK(lpgemm_int4_int4_scaled_ws(P, P, (const float *)P, (const float *)P, W, LPGEMM_OUT_FP8_E4M3, 4, 4,
                                      32, nullptr, 0, nullptr) == LPGEMM_ERR_INVALID_ARG);
+    CHECK(lpgemm_fp8_e5m2((const uint8_t *)P, (const uint8_t *)P, C, LPGEMM_OUT_FP8_E4M3, 4, 4, 16, nullptr) ==
+          LPGEMM_ERR_INVALID_ARG);
+    CHECK(lpgemm_fp8_e4m3((const uint8_t *)P, (const uint8_t *)P, C, LPGEMM_OUT_FP8_E5M2, 4, 4, 16, nullptr) ==
+          LPGEMM_ERR_INVALID_ARG);
     CHECK(lpgemm_pack_int4((const int8_t *)P, (uint8_t *)W, 3, 5, nullptr) == LPGEMM_ERR_INVALID_ARG);
     CHECK(lpgemm_unpack_int4((const uint8_t *)P, (int8_t *)W, INT64_MAX, 4, nullptr) == LPGEMM_ERR_UNSUPPORTED);
     // the scratch limit of the allocation-free entry point, before any launch

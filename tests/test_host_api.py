@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import precision_integer_gemm_amd as L
@@ -458,3 +459,15 @@ def test_kernel_override_is_per_thread():
     t.join()
     assert seen["other"] == "general"
     assert L.lpgemm_plan(L.VARIANT_W4A8, 4096, 4096, 4096)["kernel"] == "tiled"
+
+
+def test_fp8_input_codes_are_finite_and_seeded():
+    from precision_integer_gemm_amd.inputs import fp8_codes
+    a = fp8_codes(5, 0, 64, 512, "e4m3")
+    assert not ((a & 0x7F) == 0x7F).any() and a.shape == (64, 512)
+    b = fp8_codes(5, 0, 64, 512, "e5m2")
+    assert not ((b & 0x7C) == 0x7C).any()
+    assert np.array_equal(fp8_codes(5, 0, 64, 512), a)            # e4m3 by default
+    assert not np.array_equal(fp8_codes(5, 1, 64, 512), a)        # A and B differ
+    with pytest.raises(ValueError):
+        fp8_codes(5, 0, 4, 4, "e3m4")
