@@ -74,7 +74,7 @@ E5M2_MUTANTS = [
     ("e5m2 overflow early", "if (ax >= 61440.0) return sign | 0x7C;", "if (ax > 57344.0) return sign | 0x7C;"),
     ("e5m2 ties up", "if (dhi < dlo) return sign | (uint8_t)hi;\n    return sign | (uint8_t)((lo & 1) ? hi : lo);\n}\n\nint oracle_fp8_e5m2_encode",
      "if (dhi <= dlo) return sign | (uint8_t)hi;\n    return sign | (uint8_t)((lo & 1) ? hi : lo);\n}\n\nint oracle_fp8_e5m2_encode"),
-    ("e5m2 sum in 2^-31 units", "<< (ea + eb + 32);", "<< (ea + eb + 31);"),
+    ("e5m2 sum in 2^-31 units", "<< (ea + eb + 32));", "<< (ea + eb + 31));"),
     ("e5m2 product sign lost", "const __int128 p = (__int128)(ia * ib)", "const __int128 p = (__int128)(ia * ib < 0 ? -ia * ib : ia * ib)"),
     ("e5m2 inf not special", "if (e == 31) return 0;                     /* infinity or NaN */", ";"),
 ]
