@@ -15,13 +15,15 @@ Pages cited (by title):
   * tilelang PR "[Example] add w4a8 gemm kernel" (#815), reviews of
     torch_convert / ref_program.
   * TileLang tutorial ch. 14 sec. 5 "low_precision_gemm.py", pack_int4,
-    matmul_int4, gemm_blockscaled (the scaled epilogue, one K block) and
+    matmul_int4, gemm_blockscaled (the scaled epilogue with one K block, and
+    the per-K-block scaled product) and
     gemm_fp8 (the fp8 GEMM: e4m3 operands, fp32 accumulation, fp8 C).
 
 Every function here is pinned: the integer GEMMs and pack/unpack by
 ``tests/test_oracle_pins.py`` (hand-worked values, closed forms, brute force,
 an independent numpy computation), the scaled epilogue by
-``tests/test_oracle_scaled.py``, the e4m3 decode/encode and the fp8 product by
+``tests/test_oracle_scaled.py``, the per-K-block product by
+``tests/test_oracle_blockscaled.py``, the e4m3 decode/encode and the fp8 product by
 ``tests/test_oracle_fp8.py`` (PyTorch's float8_e4m3fn, exact rationals, closed
 forms); ``tests/test_oracle_mutants.py`` checks that planted mistakes fail
 them.  No function is left unpinned.
@@ -94,6 +96,7 @@ def _load():
         f.argtypes = [p, i64, p]
         f.restype = ctypes.c_int
     lib.oracle_gemm_fp8.argtypes = [p, p, i64, i64, i64, p, p]
+    lib.oracle_gemm_blockscaled.argtypes = [ctypes.c_int, p, p, p, p, i64, i64, i64, i64, ctypes.c_int, p]
     lib.oracle_gemm_fp8.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -232,6 +235,30 @@ def gemm_scaled(variant: str, A, B_packed, scale_a, scale_b, M: int, N: int, K: 
     """The scaled product: the exact integer GEMM, then the scaled epilogue."""
     C = (gemm_i4i4 if variant == "i4i4" else gemm_w4a8)(A, B_packed, M, N, K)
     return scaled_epilogue(C, scale_a, scale_b, fmt)
+
+
+def gemm_blockscaled(variant: str, A, B_packed, SFA, SFB, M: int, N: int, K: int, g: int,
+                     fmt: int) -> np.ndarray:
+    """Per-K-block scaled product (the tutorial's gemm_blockscaled read for
+    integer operands): the exact integer partial sum of each block of g k,
+    times SFA[m][j] then SFB[n][j], added into a binary32 accumulator in block
+    order, then out() to fmt (0 binary32, 1 bfloat16, 2 binary16); returned
+    as the exact values (float64 [M, N]).  SFA [M, ceil(K/g)], SFB [N,
+    ceil(K/g)] float32; variant "i4i4" (A packed) or "w4a8" (A int8)."""
+    if K % 2 or min(M, N, K) < 0 or g < 1:
+        raise ValueError("need M, N, K >= 0, K even and g >= 1")
+    nb = -(-K // g)
+    a = _bytes2d(A, M, K // 2 if variant == "i4i4" else K, "A")
+    b = _bytes2d(B_packed, N, K // 2, "B_packed")
+    sfa = np.ascontiguousarray(SFA, dtype=np.float32)
+    sfb = np.ascontiguousarray(SFB, dtype=np.float32)
+    if sfa.size != M * nb or sfb.size != N * nb:
+        raise ValueError(f"SFA and SFB must be [{M}, {nb}] and [{N}, {nb}]")
+    out = np.zeros((M, N), dtype=np.float64)
+    _check(_load().oracle_gemm_blockscaled(0 if variant == "i4i4" else 1, _ptr(a), _ptr(b), _ptr(sfa),
+                                           _ptr(sfb), M, N, K, g, int(fmt), _ptr(out)),
+           "gemm_blockscaled")
+    return out
 
 
 # ---- fp8 GEMM (the tutorial's gemm_fp8 structure, e4m3 operands) ------------------

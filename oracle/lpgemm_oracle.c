@@ -274,6 +274,74 @@ int oracle_scaled_epilogue(const int32_t *C, const float *scale_a, const float *
     return 0;
 }
 
+/* ---- per-K-block scaled product ------------------------------------------------
+ * [tutorial] gemm_blockscaled: SFA[M][ceil(K/g)] and SFB[N][ceil(K/g)] hold
+ * float32 scales (g = sf_granularity_k; the page names 128 and 32), applied
+ * along K one block of g at a time into a float32 accumulator, the result
+ * stored as out_dtype.  The page leaves the arithmetic to another chapter; the
+ * reading taken for the integer operands:
+ *   block j covers k in [j g, min(K, (j+1) g)), nb = ceil(K / g) blocks;
+ *   C_j = the exact integer sum of a(m,k) b(n,k) over block j;
+ *   term_j = ((float)C_j * SFA[m][j]) * SFB[n][j]    (binary32, nearest even);
+ *   acc = term_0, then acc = acc + term_j for j = 1, 2, ... in increasing j
+ *   (binary32, nearest even); D[m][n] = out(acc), out() as for the scaled
+ *   epilogue above.  K == 0 (no block) gives +0.
+ * With one block (g >= K) this is the per-channel formula above.  variant 0:
+ * A packed int4 [M][K/2]; variant 1: A int8 [M][K]; B packed int4 [N][K/2]. */
+int oracle_gemm_blockscaled(int variant, const uint8_t *A, const uint8_t *Bp, const float *SFA,
+                            const float *SFB, int64_t M, int64_t N, int64_t K, int64_t g, int fmt,
+                            double *out)
+{
+    int rc = check_dims(M, N, K);
+    if (rc) return rc;
+    if ((variant != 0 && variant != 1) || g < 1 || fmt < 0 || fmt > 2) return ORACLE_ERR_ARG;
+    if (M * N == 0) return ORACLE_OK;
+    const int64_t nb = (K + g - 1) / g;
+    if (out == NULL || (K > 0 && (A == NULL || Bp == NULL || SFA == NULL || SFB == NULL)))
+        return ORACLE_ERR_ARG;
+    int8_t *a = (int8_t *)malloc((size_t)(M * K > 0 ? M * K : 1));
+    int8_t *b = (int8_t *)malloc((size_t)(N * K > 0 ? N * K : 1));
+    if (a == NULL || b == NULL) { free(a); free(b); return ORACLE_ERR_NOMEM; }
+    if (variant == 0) {
+        oracle_unpack_int4(A, M, K, a);
+    } else {
+        for (int64_t i = 0; i < M * K; ++i) a[i] = (int8_t)A[i];
+    }
+    oracle_unpack_int4(Bp, N, K, b);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        const int8_t *arow = a + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const int8_t *brow = b + n * K;
+            volatile float acc = 0.0f;
+            for (int64_t j = 0; j < nb; ++j) {
+                const int64_t k1 = (j + 1) * g < K ? (j + 1) * g : K;
+                int64_t c = 0;
+                for (int64_t k = j * g; k < k1; ++k)
+                    c += (int64_t)arow[k] * (int64_t)brow[k];
+                if (c < INT32_MIN || c > INT32_MAX) bad = 1;
+                volatile float t = (float)c;               /* integer -> binary32, nearest even */
+                volatile float y = t * SFA[m * nb + j];    /* binary32 multiply */
+                volatile float z = y * SFB[n * nb + j];    /* binary32 multiply */
+                if (j == 0)
+                    acc = z;
+                else
+                    acc = acc + z;                         /* binary32 add */
+            }
+            double v = (double)acc;
+            if (fmt == 1)
+                v = round_to_format(v, 8, -126, ldexp(255.0, 120));
+            else if (fmt == 2)
+                v = round_to_format(v, 11, -14, 65504.0);
+            out[m * N + n] = v;
+        }
+    }
+    free(a);
+    free(b);
+    return bad ? ORACLE_ERR_RANGE : ORACLE_OK;
+}
+
 /* ---- fp8 GEMM (second workload) ---------------------------------------------
  * [tutorial] gemm_fp8 (chapter 14, the fp8 example next to matmul_int4): the
  * same A[M,K] . B[N,K]^T structure (T.gemm(..., transpose_B=True)) with fp8

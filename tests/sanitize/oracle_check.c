@@ -29,6 +29,9 @@ int oracle_fp8_e4m3_decode(const uint8_t *codes, int64_t n, double *out);
 int oracle_fp8_e4m3_encode(const double *x, int64_t n, uint8_t *out);
 int oracle_gemm_fp8(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K, double *C,
                     double *Cabs);
+int oracle_gemm_blockscaled(int variant, const uint8_t *A, const uint8_t *Bp, const float *SFA,
+                            const float *SFB, int64_t M, int64_t N, int64_t K, int64_t g, int fmt,
+                            double *out);
 int oracle_fp8_e5m2_decode(const uint8_t *codes, int64_t n, double *out);
 int oracle_fp8_e5m2_encode(const double *x, int64_t n, uint8_t *out);
 int oracle_gemm_fp8_e5m2(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K,
@@ -91,6 +94,19 @@ static void gemms(int64_t M, int64_t N, int64_t K)
     for (int64_t i = 0; i < N; ++i) sb[i] = ldexpf((float)(int32_t)next(), -38);
     for (int fmt = 0; fmt <= 2; ++fmt) CHECK(oracle_scaled_epilogue(C, sa, sb, M, N, fmt, D) == 0);
     CHECK(oracle_scaled_epilogue(C, sa, sb, M, N, 3, D) != 0);   /* unknown format */
+    /* per-K-block scales, g = 32 and 128 (ragged last block), every format */
+    for (int64_t g = 32; g <= 128; g *= 4) {
+        const int64_t nb = (K + g - 1) / g;
+        float *sfa = alloc((size_t)(M * nb) * 4), *sfb = alloc((size_t)(N * nb) * 4);
+        for (int64_t i = 0; i < M * nb; ++i) sfa[i] = ldexpf((float)(int32_t)next(), -40);
+        for (int64_t i = 0; i < N * nb; ++i) sfb[i] = ldexpf((float)(int32_t)next(), -38);
+        for (int fmt = 0; fmt <= 2; ++fmt) {
+            CHECK(oracle_gemm_blockscaled(0, Ap, Bp, sfa, sfb, M, N, K, g, fmt, D) == 0);
+            CHECK(oracle_gemm_blockscaled(1, (const uint8_t *)A8, Bp, sfa, sfb, M, N, K, g, fmt, D) == 0);
+        }
+        CHECK(oracle_gemm_blockscaled(2, Ap, Bp, sfa, sfb, M, N, K, g, 0, D) != 0);   /* unknown variant */
+        free(sfa); free(sfb);
+    }
     free(Ap); free(Bp); free(A8); free(Al); free(C); free(C2); free(Ap2); free(sa); free(sb); free(D);
 }
 

@@ -80,12 +80,36 @@ E5M2_MUTANTS = [
 ]
 
 
+# Mistakes in the per-K-block scaled product, caught by test_oracle_blockscaled.py.
+BLOCKSCALED_MUTANTS = [
+    ("block boundary off by one", "for (int64_t k = j * g; k < k1; ++k)",
+     "for (int64_t k = j * g + (j > 0); k < k1 + (j + 1 < nb); ++k)"),
+    ("last partial block dropped", "const int64_t nb = (K + g - 1) / g;\n    if (out == NULL",
+     "const int64_t nb = K / g;\n    if (out == NULL"),
+    ("scales multiplied first", "volatile float y = t * SFA[m * nb + j];    /* binary32 multiply */\n"
+     "                volatile float z = y * SFB[n * nb + j];",
+     "volatile float y = SFA[m * nb + j] * SFB[n * nb + j];\n                volatile float z = y * t;"),
+    ("SFB indexed by the output row", "volatile float z = y * SFB[n * nb + j];",
+     "volatile float z = y * SFB[(m % N) * nb + j];"),
+    ("SFA of the next block", "volatile float y = t * SFA[m * nb + j];",
+     "volatile float y = t * SFA[m * nb + (j + 1 < nb ? j + 1 : j)];"),
+    ("accumulated in double", "volatile float acc = 0.0f;\n            for (int64_t j = 0; j < nb; ++j) {\n                const int64_t k1",
+     "volatile double acc = 0.0;\n            for (int64_t j = 0; j < nb; ++j) {\n                const int64_t k1"),
+    ("blocks added last to first", "for (int64_t j = 0; j < nb; ++j) {\n                const int64_t k1",
+     "for (int64_t jj = 0; jj < nb; ++jj) {\n                const int64_t j = nb - 1 - jj;\n                const int64_t k1"),
+    ("scales applied after the sum", "volatile float y = t * SFA[m * nb + j];    /* binary32 multiply */",
+     "volatile float y = t * (j == 0 ? SFA[m * nb] : 1.0f);"),
+]
+
+
 @pytest.mark.parametrize("what,old,new,pins",
                          [m + ("tests/test_oracle_pins.py",) for m in MUTANTS] +
                          [m + ("tests/test_oracle_scaled.py",) for m in SCALED_MUTANTS] +
                          [m + ("tests/test_oracle_fp8.py",) for m in FP8_MUTANTS] +
-                         [m + ("tests/test_oracle_fp8_e5m2.py",) for m in E5M2_MUTANTS],
-                         ids=[m[0] for m in MUTANTS + SCALED_MUTANTS + FP8_MUTANTS + E5M2_MUTANTS])
+                         [m + ("tests/test_oracle_fp8_e5m2.py",) for m in E5M2_MUTANTS] +
+                         [m + ("tests/test_oracle_blockscaled.py",) for m in BLOCKSCALED_MUTANTS],
+                         ids=[m[0] for m in MUTANTS + SCALED_MUTANTS + FP8_MUTANTS + E5M2_MUTANTS +
+                              BLOCKSCALED_MUTANTS])
 def test_pins_catch_planted_mistake(tmp_path, what, old, new, pins):
     for d in ("oracle", "tests", "precision_integer_gemm_amd"):
         shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
