@@ -244,6 +244,52 @@ lpgemm_status lpgemm_int4_int4_scaled_ws(const void *A_packed, const void *B_pac
                                          hipStream_t stream);
 
 /*
+ * Per-K-block scaled product (the tutorial's gemm_blockscaled, ch. 14 sec. 5,
+ * "low_precision_gemm.py": scale tables SFA[M, ceil(K/g)] and SFB[N, ceil(K/g)]
+ * in the float32 accumulator type, applied along K one block of
+ * sf_granularity_k = g at a time into a float32 accumulator, result in
+ * out_dtype), for the integer operands of lpgemm_int4_int4 / lpgemm_w4a8:
+ *
+ *     C_j[m][n] = sum over k in [j g, min(K, (j+1) g)) of a(m,k) b(n,k)   (exact)
+ *     term_j    = ((float)C_j[m][n] * SFA[m][j]) * SFB[n][j]
+ *     acc       = term_0 + term_1 + ... + term_(nb-1), added left to right
+ *     D[m][n]   = out(acc)
+ *
+ * with nb = ceil(K / g) blocks (the last one shorter when g does not divide
+ * K); (float) converts to binary32 rounding to nearest even (exact while
+ * |C_j| < 2^24), each * and + is a binary32 operation rounding to nearest
+ * even (no fused multiply-add), and out() is the conversion of the scaled
+ * entry points.  The order of the additions is fixed, so the result is
+ * unique.  With g >= K (one block) this is the per-channel product of
+ * lpgemm_int4_int4_scaled / lpgemm_w4a8_scaled.  K == 0 gives +0.
+ *   A / A_packed  as for the unscaled call
+ *   B_packed      device, packed int4 [N][K/2]
+ *   SFA           device, float [M][nb] row-major (4-byte aligned)
+ *   SFB           device, float [N][nb] row-major (4-byte aligned)
+ *   g             block length in k: a power of two, 32 <= g <= 2^30 (the
+ *                 page names 128 and 32)
+ *   D             device, [M][N] of out_dtype (F32, BF16 or F16), written;
+ *                 aligned to its element size
+ * Returns LPGEMM_ERR_INVALID_ARG for negative sizes, odd K, a bad g or
+ * out_dtype, a null or misaligned pointer that would be dereferenced;
+ * LPGEMM_ERR_UNSUPPORTED for K above LPGEMM_MAX_K or a forced kernel other
+ * than GENERAL / TILED / TILED_128 / TILED_64; LPGEMM_ERR_HIP if a launch
+ * failed.  K % 32 == 0 with 16-byte aligned A and B (and D aligned to 16
+ * bytes for F32, 8 for BF16 / F16) takes the tiled matrix-core kernel (the
+ * integer partial of each block in int32 matrix-core accumulators, added
+ * where the block ends), anything else a one-thread-per-element kernel; both
+ * give the same bits.  The library allocates nothing.
+ */
+lpgemm_status lpgemm_int4_int4_blockscaled(const void *A_packed, const void *B_packed, const float *SFA,
+                                           const float *SFB, int64_t g, void *D,
+                                           lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                                           hipStream_t stream);
+
+lpgemm_status lpgemm_w4a8_blockscaled(const int8_t *A, const uint8_t *B_packed, const float *SFA,
+                                      const float *SFB, int64_t g, void *D, lpgemm_out_dtype out_dtype,
+                                      int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * fp8 GEMM (second workload):  C[m][n] = out( sum_k a(m,k) * b(n,k) )
  *   A          device, e4m3 bytes [M][K]
  *   B          device, e4m3 bytes [N][K]

@@ -29,7 +29,8 @@ MAX_K = 131070
 EXPORTS = ("lpgemm_int4_int4", "lpgemm_w4a8", "lpgemm_int4_int4_ws", "lpgemm_w4a8_ws",
            "lpgemm_int4_int4_noalloc",
            "lpgemm_workspace_size", "lpgemm_int4_int4_scaled", "lpgemm_w4a8_scaled",
-           "lpgemm_int4_int4_scaled_ws", "lpgemm_fp8_e4m3", "lpgemm_fp8_e5m2", "lpgemm_pack_int4",
+           "lpgemm_int4_int4_scaled_ws", "lpgemm_int4_int4_blockscaled", "lpgemm_w4a8_blockscaled",
+           "lpgemm_fp8_e4m3", "lpgemm_fp8_e5m2", "lpgemm_pack_int4",
            "lpgemm_unpack_int4", "lpgemm_status_string", "lpgemm_plan",
            "lpgemm_set_kernel_override")
 SIZE_MAX = 2 ** 64 - 1
@@ -94,6 +95,10 @@ def lib() -> ctypes.CDLL:
         f.restype = ctypes.c_int
     L.lpgemm_int4_int4_scaled_ws.argtypes = [p, p, p, p, p, ctypes.c_int, i64, i64, i64, p, sz, p]
     L.lpgemm_int4_int4_scaled_ws.restype = ctypes.c_int
+    for name in ("lpgemm_int4_int4_blockscaled", "lpgemm_w4a8_blockscaled"):
+        f = getattr(L, name)
+        f.argtypes = [p, p, p, p, i64, p, ctypes.c_int, i64, i64, i64, p]
+        f.restype = ctypes.c_int
     for name in ("lpgemm_fp8_e4m3", "lpgemm_fp8_e5m2"):
         getattr(L, name).argtypes = [p, p, p, ctypes.c_int, i64, i64, i64, p]
         getattr(L, name).restype = ctypes.c_int
@@ -321,6 +326,55 @@ def lpgemm_w4a8_scaled(A, B_packed, scale_a, scale_b, *, dtype=None, out=None, s
     _raise(lib().lpgemm_w4a8_scaled(A.data_ptr(), B_packed.data_ptr(), scale_a.data_ptr(),
                                     scale_b.data_ptr(), D.data_ptr(), _out_code(dtype), M, N, K,
                                     _stream_handle(stream)), "lpgemm_w4a8_scaled")
+    return D
+
+
+def _check_block_scales(SFA, SFB, M, N, K, g):
+    torch = _torch()
+    nb = -(-K // g) if g > 0 else 0
+    for name, t, n in (("SFA", SFA, M), ("SFB", SFB, N)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.float32:
+            raise TypeError(f"{name} must be a float32 tensor on a GPU device")
+        if tuple(t.shape) != (n, nb) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with shape ({n}, {nb}) for K={K}, g={g}")
+
+
+def lpgemm_int4_int4_blockscaled(A_packed, B_packed, SFA, SFB, g, *, dtype=None, out=None, stream=None):
+    """D[M,N] = out(sum_j ((float)C_j * SFA[m,j]) * SFB[n,j]) over the K blocks
+    of g (a power of two >= 32) of the int4 x int4 product, added in block order
+    in binary32; SFA [M, ceil(K/g)], SFB [N, ceil(K/g)] float32."""
+    torch = _torch()
+    _check_dev(A_packed, "A_packed", (torch.int8, torch.uint8))
+    _check_dev(B_packed, "B_packed", (torch.int8, torch.uint8))
+    M, half = A_packed.shape
+    N, half_b = B_packed.shape
+    if half != half_b:
+        raise ValueError(f"packed K mismatch: A has {half} bytes per row, B {half_b}")
+    _check_block_scales(SFA, SFB, M, N, 2 * half, g)
+    dtype = dtype or (out.dtype if out is not None else torch.bfloat16)
+    D = _scaled_out(out, dtype, M, N, A_packed.device)
+    _raise(lib().lpgemm_int4_int4_blockscaled(A_packed.data_ptr(), B_packed.data_ptr(), SFA.data_ptr(),
+                                              SFB.data_ptr(), g, D.data_ptr(), _out_code(dtype), M, N,
+                                              2 * half, _stream_handle(stream)),
+           "lpgemm_int4_int4_blockscaled")
+    return D
+
+
+def lpgemm_w4a8_blockscaled(A, B_packed, SFA, SFB, g, *, dtype=None, out=None, stream=None):
+    """lpgemm_int4_int4_blockscaled for int8 A [M, K] and packed int4 B."""
+    torch = _torch()
+    _check_dev(A, "A", (torch.int8,))
+    _check_dev(B_packed, "B_packed", (torch.uint8, torch.int8))
+    M, K = A.shape
+    N, half = B_packed.shape
+    if K != 2 * half:
+        raise ValueError(f"K mismatch: A has K={K}, B_packed holds {2 * half}")
+    _check_block_scales(SFA, SFB, M, N, K, g)
+    dtype = dtype or (out.dtype if out is not None else torch.bfloat16)
+    D = _scaled_out(out, dtype, M, N, A.device)
+    _raise(lib().lpgemm_w4a8_blockscaled(A.data_ptr(), B_packed.data_ptr(), SFA.data_ptr(), SFB.data_ptr(),
+                                         g, D.data_ptr(), _out_code(dtype), M, N, K, _stream_handle(stream)),
+           "lpgemm_w4a8_blockscaled")
     return D
 
 

@@ -151,8 +151,10 @@ enum OutFormat { OUT_I32 = 0, OUT_F32 = 1, OUT_BF16 = 2, OUT_F16 = 3, OUT_E4M3 =
 
 struct Epilogue {
     void *out;             // D (or C), row-major [M][N]
-    const float *scale_a;  // [M], scaled formats only
-    const float *scale_b;  // [N], scaled formats only
+    const float *scale_a;  // [M], scaled formats only; SFA [M][nb] with block scales
+    const float *scale_b;  // [N], scaled formats only; SFB [N][nb] with block scales
+    int32_t nb = 0;        // block scales: number of K blocks, ceil(K / g)
+    int32_t lg = 0;        // block scales: log2 of the block length g
 };
 
 // fp32 -> bf16 bits, round to nearest even; a NaN stays a quiet NaN.
@@ -350,13 +352,30 @@ __device__ __forceinline__ uint32_t float_to_e5m2(float x)
 }
 
 // Store fp32 results v[i] for columns n .. n+3 of row m (columns >= N
-// skipped) as fp32, e4m3 or e5m2.  Vector stores when all four exist and
-// N % 4 == 0.
+// skipped) as fp32, bf16, fp16, e4m3 or e5m2 (nearest even).  Vector stores
+// when all four exist and N % 4 == 0.
 template <int OUT>
 __device__ __forceinline__ void store_row4f(const Epilogue &e, int64_t m, int N, int n, const float (&v)[4])
 {
     const bool vec = (N % 4) == 0 && n + 3 < N;
-    if (OUT == OUT_F32) {
+    if (OUT == OUT_BF16 || OUT == OUT_F16) {
+        uint16_t *row = static_cast<uint16_t *>(e.out) + m * N;
+        uint32_t hb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x = v[i];
+            asm volatile("" : "+v"(x));  // convert the binary32 value itself (no fused rounding)
+            hb[i] = out_bits<OUT>(x);
+        }
+        if (vec) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2 *>(row + n) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (n + i < N) row[n + i] = (uint16_t)hb[i];
+        }
+    } else if (OUT == OUT_F32) {
         float *row = static_cast<float *>(e.out) + m * N;
         if (vec) {
             *reinterpret_cast<i32x4 *>(row + n) =
@@ -404,6 +423,22 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voffset, uint32_t lds
         "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"  // one wait state between an M0 write and an LDS DMA
         "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voffset), "s"(rsrc), "s"(lds_base)
+        : "memory");
+}
+
+// 4 bytes per lane from rsrc[voffset] into LDS at lds_base + 4 * lane (the
+// per-K-block scale tables, one float per lane from anywhere in the table).
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voffset, uint32_t lds_base)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "v"(voffset), "s"(rsrc), "s"(lds_base)

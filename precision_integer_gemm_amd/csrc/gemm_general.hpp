@@ -46,6 +46,50 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(const uint8_t *__rest
     }
 }
 
+// Per-K-block scaled product, one thread per output element: block j (k in
+// [j g, min(K, (j+1) g)), g = 2^epi.lg, epi.nb blocks) is summed exactly in
+// int32, then ((float)C_j * SFA[m][j]) * SFB[n][j] is added to a binary32
+// accumulator in increasing j, every step rounding to nearest even; the
+// accumulator starts at -0 (so the first term is taken as it is), or is +0
+// when there is no block (K == 0).  Any even K and any alignment.
+template <int VAR, int OUT>
+__global__ __launch_bounds__(256) void gemm_blockscaled_general_kernel(const uint8_t *__restrict__ A,
+                                                                       const uint8_t *__restrict__ B,
+                                                                       Epilogue epi, int64_t M,
+                                                                       int64_t N, int64_t K)
+{
+    const int64_t n = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
+    const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
+    if (m >= M || n >= N) return;
+    const int64_t half = K / 2, g2 = ((int64_t)1 << epi.lg) / 2, nb = epi.nb;
+    const uint8_t *brow = B + n * half;
+    const float *sfa = epi.scale_a + m * nb, *sfb = epi.scale_b + n * nb;
+    float acc = nb > 0 ? -0.0f : 0.0f;
+    for (int64_t j = 0; j < nb; ++j) {
+        const int64_t p0 = j * g2, p1 = min(half, p0 + g2);  // byte pairs of the block
+        int32_t c = 0;
+        if (VAR == I4I4) {
+            const uint8_t *arow = A + m * half;
+            for (int64_t q = p0; q < p1; ++q) {
+                const uint32_t a = arow[q], b = brow[q];
+                c += int4_at(a, 0) * int4_at(b, 0) + int4_at(a, 1) * int4_at(b, 1);
+            }
+        } else {
+            const int8_t *arow = reinterpret_cast<const int8_t *>(A) + m * K;
+            for (int64_t q = p0; q < p1; ++q) {
+                const uint32_t b = brow[q];
+                c += (int32_t)arow[2 * q] * int4_at(b, 0) + (int32_t)arow[2 * q + 1] * int4_at(b, 1);
+            }
+        }
+        acc = acc + scaled(c, sfa[j], sfb[j]);
+    }
+    asm volatile("" : "+v"(acc));  // convert the binary32 value itself
+    if (OUT == OUT_F32)
+        static_cast<float *>(epi.out)[m * N + n] = acc;
+    else
+        static_cast<uint16_t *>(epi.out)[m * N + n] = (uint16_t)out_bits<OUT>(acc);
+}
+
 // fp8 product (VAR: FP8 e4m3 or BF8 e5m2 operands), one thread per output:
 // exact products summed in fp32 in k order; fp32 output, or the operands' fp8
 // format (OUT_E4M3 / OUT_E5M2).  Any K and alignment.

@@ -39,16 +39,32 @@
 // b % tiles and stores its sums into slice b / tiles of an M x N int32
 // workspace (epi.out), which a second kernel sums into C.
 //
+// Per-K-block scales (SBP > 0, integer formats, the tutorial's
+// gemm_blockscaled read for integer operands): the int32 accumulators hold
+// one block's partial sum; where a block of g k ends, each element becomes
+// ((float)C_j * SFA[m][j]) * SFB[n][j] and is added to an fp32 accumulator
+// (started at -0, so the first block's term is taken as it is), and the
+// int32 accumulators restart.  The stage copy also brings the stage's blocks'
+// scale rows into LDS (4-byte DMA, one float per lane), in a ring of
+// STAGES + 1 slots so that a wave still flushing a tile's last block never
+// races the refill of that block's slot.  SBP is the number of blocks per
+// 128-k stage: 4 (g = 32), 2 (g = 64) or 1 (g >= 128, the stage inside one
+// block).  With g = 32 each MFMA must contract one whole block, so the
+// fragments are read with a different lane-to-k map: lanes 0-31 feed k 0-15
+// and lanes 32-63 k 16-31 of the first instruction (k 32-63: the second),
+// two 8-byte LDS reads per packed row instead of one 16-byte read.
+//
 // Requirements (checked on the host): K % 32 == 0, 16-byte aligned bases,
 // M, N < 2^31, K <= 131070; with SPLIT kc % 256 == 0 and a grid of exactly
-// tiles x ranges.
+// tiles x ranges; with SBP g = 128 / SBP (SBP > 1) or g >= 128 (SBP = 1), a
+// power of two.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace lpgemm {
 
-template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES>
+template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, int SBP = 0>
 struct PipeCfg {
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = 64 * kWaves;
@@ -65,11 +81,22 @@ struct PipeCfg {
     static constexpr int NA = A_BYTES / 1024 / kWaves;  // DMA instructions per wave per stage
     static constexpr int NB = B_BYTES / 1024 / kWaves;
     static constexpr int SHIFT = (VAR == I4I4) ? 8 : 4;
+    // Block-scale ring: SBP blocks' SFA rows (BM floats each) and SFB rows
+    // (BN floats each) per slot, padded to whole 4-byte DMA instructions
+    // (NS per wave per stage), STAGES + 1 slots.
+    static constexpr int SCALES = (BM + BN) * SBP;
+    static constexpr int NS = SBP ? (SCALES + 64 * kWaves - 1) / (64 * kWaves) : 0;
+    static constexpr int SCALE_SLOT_BYTES = NS * 64 * kWaves * 4;
+    static constexpr int SCALE_SLOTS = SBP ? STAGES + 1 : 0;
+    static constexpr int LDS_BYTES_ALL = LDS_BYTES + SCALE_SLOTS * SCALE_SLOT_BYTES;
+    static_assert(SBP == 0 || SBP == 1 || SBP == 2 || SBP == 4, "blocks per stage");
+    static_assert(SBP == 0 || (BK == 128 && !is_fp8(VAR)), "block scales: integer formats, 128-k stages");
+    static_assert(SBP == 0 || (BM * SBP) % 64 == 0, "a scale DMA instruction must not straddle SFA and SFB");
     static_assert(BK % 64 == 0, "BK must be a multiple of 64");
     static_assert(NA * 1024 * kWaves == A_BYTES && NB * 1024 * kWaves == B_BYTES,
                   "each wave must issue whole 1 KB DMA instructions");
     static_assert(CPR_A <= 16 && CPR_B <= 16, "row too long for the swizzle");
-    static constexpr bool kFits = STAGES >= 2 && LDS_BYTES <= 160 * 1024;
+    static constexpr bool kFits = STAGES >= 2 && LDS_BYTES_ALL <= 160 * 1024;
 };
 
 // Position of 16-byte chunk `col` of tile row `row` in a row-major LDS tile
@@ -82,18 +109,23 @@ __device__ __forceinline__ int lds_chunk(int row, int col)
     return row * CPR + (col ^ ((row / rows_per_256) % CPR));
 }
 
-template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, int OUT, bool SPLIT = false>
+template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, int OUT, bool SPLIT = false,
+          int SBP = 0>
 __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pipelined_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N,
     int K, int tiles_m, int tiles_n, int xcds, int kc)
 {
     static_assert(!SPLIT || OUT == OUT_I32, "split K adds int32 partial sums");
-    using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, STAGES>;
+    static_assert(SBP == 0 || (!SPLIT && (OUT == OUT_F32 || OUT == OUT_BF16 || OUT == OUT_F16)),
+                  "block scales: whole K per tile, float output");
+    using Cfg = PipeCfg<VAR, FM, FN, WM, WN, BK, STAGES, SBP>;
+    constexpr bool K32 = SBP == 4;  // g = 32: one block per MFMA instruction
     static_assert(Cfg::kFits, "LDS ring does not fit in 160 KB");
     constexpr int RA = Cfg::RA, RB = Cfg::RB, CPR_A = Cfg::CPR_A, CPR_B = Cfg::CPR_B;
     constexpr int NA = Cfg::NA, NB = Cfg::NB;
     constexpr int STEPS = BK / 64;
-    constexpr int kPerStage = NA + NB;  // DMA instructions per wave per stage
+    constexpr int NS = Cfg::NS;
+    constexpr int kPerStage = NA + NB + NS;  // DMA instructions per wave per stage
     constexpr int kPrologue = STAGES;  // stages loaded before a tile's first step
     // 16-byte stores per wave for a tile with no edge (a lower bound on the
     // vector-memory instructions its epilogue issues).
@@ -143,6 +175,27 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     }
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
+    // Block scales: DMA instruction i of this wave moves scale elements e =
+    // (wave * NS + i) * 64 + lane of the slot: SFA[m0 + r][j] for e < BM * SBP
+    // (r = e % BM, block jj = e / BM of the stage), then SFB[n0 + r][j].
+    // s_off is the byte offset of the element's row inside its table tile;
+    // the stage adds 4 j.  Elements past the slot's SCALES are padding.
+    const int nb = SBP ? epi.nb : 0, lg = SBP ? epi.lg : 0;
+    uint32_t s_off[NS > 0 ? NS : 1];
+    int s_jj[NS > 0 ? NS : 1];
+    bool s_live[NS > 0 ? NS : 1], s_isb[NS > 0 ? NS : 1];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int e0 = (wave * NS + i) * 64;  // wave-uniform
+        const int e = e0 + lane;
+        s_isb[i] = e0 >= Cfg::BM * SBP;
+        s_live[i] = e < Cfg::SCALES;
+        const int eb = s_isb[i] ? e - Cfg::BM * SBP : e;
+        const int rows = s_isb[i] ? Cfg::BN : Cfg::BM;
+        s_jj[i] = eb / rows;
+        s_off[i] = (uint32_t)(eb % rows) * (uint32_t)nb * 4u;
+    }
+
     // Persistent tile loop: workgroup b takes tiles b, b + G, b + 2G, ... (G =
     // number of workgroups).  Tiles are renumbered so that each XCD
     // (workgroup b runs on XCD b % xcds) walks a contiguous range of tile
@@ -164,10 +217,14 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     int v = (int)blockIdx.x - chunk * nblocks;
     int m0, n0;
     tile_origin(v, m0, n0);
-    i32x4 rsrc_a, rsrc_b;
+    i32x4 rsrc_a, rsrc_b, rsrc_sa, rsrc_sb;
     auto set_rsrc = [&]() {
         rsrc_a = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)min(Cfg::BM, M - m0) * lda);
         rsrc_b = make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)min(Cfg::BN, N - n0) * ldb);
+        if constexpr (SBP > 0) {
+            rsrc_sa = make_rsrc(epi.scale_a + (int64_t)m0 * nb, (uint32_t)min(Cfg::BM, M - m0) * nb * 4u);
+            rsrc_sb = make_rsrc(epi.scale_b + (int64_t)n0 * nb, (uint32_t)min(Cfg::BN, N - n0) * nb * 4u);
+        }
     };
     set_rsrc();
 
@@ -186,6 +243,18 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
             const uint32_t off = (kb + b_col[i] < b_len) ? b_off[i] + b_k0 + kb : kOutOfRange;
             dma16(rsrc_b, off, base + Cfg::A_BYTES + (uint32_t)(wave * NB + i) * 1024u);
         }
+        if constexpr (SBP > 0) {
+            // the stage's blocks: jb (the block of its first k) .. jb + SBP - 1
+            const uint32_t sbase = lds0 + (uint32_t)(STAGES * Cfg::STAGE_BYTES) +
+                                   (uint32_t)(kt % (STAGES + 1)) * Cfg::SCALE_SLOT_BYTES;
+            const int jb = (kt * BK) >> lg;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const int j = jb + s_jj[i];
+                const uint32_t off = (s_live[i] && j < nb) ? s_off[i] + 4u * (uint32_t)j : kOutOfRange;
+                dma4(s_isb[i] ? rsrc_sb : rsrc_sa, off, sbase + (uint32_t)(wave * NS + i) * 256u);
+            }
+        }
     };
 
     const int h = lane >> 5;    // which 16-k half of an MFMA operand this lane feeds
@@ -199,9 +268,40 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
         i32x4 b[FN][BV];
         i32x4 a[FM][AV];
     };
+    // g = 32: per packed row the two 8-byte halves 8h of the step's two
+    // 16-byte chunks (k 16h..16h+15 and 32+16h..32+16h+15 of the step), per
+    // int8 row chunks h and 2 + h.
     auto read_frags = [&](int slot, int step, Frags &f) {
         const uint8_t *sa = smem + slot * Cfg::STAGE_BYTES;
         const uint8_t *sb = sa + Cfg::A_BYTES;
+        if constexpr (K32) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int row = (wn * FN + fn) * 32 + r32;
+                const u32x2 x = *reinterpret_cast<const u32x2 *>(sb + 16 * lds_chunk<CPR_B>(row, 2 * step) + 8 * h);
+                const u32x2 y =
+                    *reinterpret_cast<const u32x2 *>(sb + 16 * lds_chunk<CPR_B>(row, 2 * step + 1) + 8 * h);
+                f.b[fn][0] = i32x4{(int32_t)x.x, (int32_t)x.y, (int32_t)y.x, (int32_t)y.y};
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int row = (wm * FM + fm) * 32 + r32;
+                if constexpr (VAR == I4I4) {
+                    const u32x2 x =
+                        *reinterpret_cast<const u32x2 *>(sa + 16 * lds_chunk<CPR_A>(row, 2 * step) + 8 * h);
+                    const u32x2 y =
+                        *reinterpret_cast<const u32x2 *>(sa + 16 * lds_chunk<CPR_A>(row, 2 * step + 1) + 8 * h);
+                    f.a[fm][0] = i32x4{(int32_t)x.x, (int32_t)x.y, (int32_t)y.x, (int32_t)y.y};
+                } else {
+#pragma unroll
+                    for (int v = 0; v < AV; ++v)
+                        f.a[fm][v] = *reinterpret_cast<const i32x4 *>(
+                            sa + 16 * lds_chunk<CPR_A>(row, 4 * step + 2 * v + h));
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int row = (wn * FN + fn) * 32 + r32;
@@ -227,7 +327,41 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     Acc acc[FN][FM];
     // Unpack and contract one 64-k step: per block two 32x32x32 int8 MFMAs,
     // or one 32x32x64 fp8 MFMA (lane l: 32 consecutive k, 32 (l / 32) onward).
-    auto compute = [&](const Frags &f) {
+    // Block scales: fp32 accumulators, and the scale rows of one block.
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x16 facc[SBP > 0 ? FN : 1][SBP > 0 ? FM : 1];
+    // SFA[m][j] of this lane's rows and SFB[n][j] of its columns (four groups
+    // of four) for block j, which lies in the stage of K tile kt.
+    auto block_scales = [&](int kt, int j, float (&sa)[FM], f32x4 (&sb)[FN][4]) {
+        const int jj = j - ((kt * BK) >> lg);
+        const float *slot = reinterpret_cast<const float *>(smem + STAGES * Cfg::STAGE_BYTES +
+                                                            (kt % (STAGES + 1)) * Cfg::SCALE_SLOT_BYTES);
+        const float *ta = slot + jj * Cfg::BM;
+        const float *tb = slot + Cfg::BM * SBP + jj * Cfg::BN;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) sa[fm] = ta[(wm * FM + fm) * 32 + r32];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg)
+                sb[fn][rg] = *reinterpret_cast<const f32x4 *>(tb + (wn * FN + fn) * 32 + 8 * rg + 4 * h);
+    };
+    // fa += ((float)C_j * SFA) * SFB element by element, each operation a
+    // binary32 one rounding to nearest even (c holds C_j << SHIFT, exactly).
+    auto add_block = [&](f32x16 &fa, const i32x16 &c, float sa, const f32x4 (&sb)[4]) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float t = (float)(c[r] >> Cfg::SHIFT);
+            const float y = t * sa;
+            float z = y * sb[r / 4][r % 4];
+            asm volatile("" : "+v"(z));  // two separate roundings, no fused operation
+            fa[r] = fa[r] + z;
+        }
+    };
+
+    auto compute = [&](const Frags &f, int kt, int st) {
+        (void)kt;
+        (void)st;
         if constexpr (is_fp8(VAR)) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
@@ -256,6 +390,68 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
                 }
             }
         }
+    };
+
+    // One 64-k step with block scales.  g = 32: each instruction contracts
+    // one whole block (blocks j1 and j1 + 1) from zero and is added at once;
+    // g >= 64: the step's products go into the int32 accumulators, which are
+    // added and cleared where the step ends block j (or ends K).  Blocks at
+    // or past nb (the zero-filled steps after K) are skipped.
+    auto compute_scaled = [&](const Frags &f, int kt, int st) {
+        if constexpr (SBP > 0) {
+            const int ks = kt * BK + 64 * st;  // the step's first k
+            if constexpr (K32) {
+                const int j1 = ks >> 5;
+                if (j1 >= nb) return;
+                const bool second = j1 + 1 < nb;
+                float sa1[FM], sa2[FM];
+                f32x4 sb1[FN][4], sb2[FN][4];
+                block_scales(kt, j1, sa1, sb1);
+                if (second) block_scales(kt, j1 + 1, sa2, sb2);
+                i32x4 a_lo[FM], a_hi[FM];
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    i32x4 b_lo, b_hi;
+                    unpack_chunk<VAR == W4A8>(f.b[fn][0], b_lo, b_hi);
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) {
+                        if (fn == 0) {
+                            if (VAR == I4I4) {
+                                unpack_chunk<false>(f.a[fm][0], a_lo[fm], a_hi[fm]);
+                            } else {
+                                a_lo[fm] = f.a[fm][0];
+                                a_hi[fm] = f.a[fm][AV - 1];
+                            }
+                        }
+                        add_block(facc[fn][fm], mfma_32x32x32(b_lo, a_lo[fm], i32x16{}), sa1[fm], sb1[fn]);
+                        if (second)
+                            add_block(facc[fn][fm], mfma_32x32x32(b_hi, a_hi[fm], i32x16{}), sa2[fm], sb2[fn]);
+                    }
+                }
+            } else {
+                compute(f, kt, st);
+                const int j = ks >> lg;
+                const bool ends = ((ks + 64) & ((1 << lg) - 1)) == 0 || ks + 64 >= K;
+                if (j < nb && ends) {
+                    float sa[FM];
+                    f32x4 sb[FN][4];
+                    block_scales(kt, j, sa, sb);
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int fm = 0; fm < FM; ++fm) {
+                            add_block(facc[fn][fm], acc[fn][fm], sa[fm], sb[fn]);
+                            acc[fn][fm] = Acc{};
+                        }
+                }
+            }
+        }
+    };
+    auto step = [&](const Frags &f, int kt, int st) {
+        if constexpr (SBP > 0)
+            compute_scaled(f, kt, st);
+        else
+            compute(f, kt, st);
     };
 
     // Wait until this wave's loads of the stage issued `after` stages before
@@ -293,6 +489,15 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j) acc[i][j] = Acc{};
+        if constexpr (SBP > 0) {
+            // -0 + x == x for every x: the first block's term is taken as it is
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) facc[i][j][r] = -0.0f;
+        }
         Frags cur, nxt;
         read_frags(0, 0, cur);
 
@@ -311,7 +516,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
                     lds_barrier();
                     read_frags((kt + 1) % STAGES, 0, nxt);
                 }
-                compute(cur);
+                step(cur, kt, st);
                 if (st + 1 == STEPS) issue_stage(kt + STAGES);
                 cur = nxt;
             }
@@ -322,7 +527,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
 #pragma unroll
             for (int st = 0; st < STEPS; ++st) {
                 if (st + 1 < STEPS) read_frags(slot, st + 1, nxt);
-                compute(cur);
+                step(cur, ktiles - 1, st);
                 cur = nxt;
             }
         }
@@ -332,6 +537,23 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
         const int vn = v + (int)gridDim.x;
         // Epilogue: lane holds C[m][n .. n+3] for m = l%32 of each column block.
         auto store_tile = [&]() {
+            if constexpr (SBP > 0) {
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) {
+                        const int m = tm0 + (wm * FM + fm) * 32 + r32;
+                        if (m >= M) continue;
+#pragma unroll
+                        for (int rg = 0; rg < 4; ++rg) {
+                            const int n = tn0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h;
+                            const float c[4] = {facc[fn][fm][4 * rg + 0], facc[fn][fm][4 * rg + 1],
+                                                facc[fn][fm][4 * rg + 2], facc[fn][fm][4 * rg + 3]};
+                            store_row4f<OUT>(epi, m, N, n, c);
+                        }
+                    }
+                return;
+            }
             // Scales first (one per row block, four per column group), then
             // the stores: the scale reads are not reordered behind stores to D.
             float sa[FM], sb[FN][4][4];

@@ -701,6 +701,114 @@ int out_format_of(lpgemm_out_dtype d)
     return -1;
 }
 
+// ---- per-K-block scaled product ----------------------------------------------
+// The tiled kernel with block scales (gemm_pipelined.hpp, SBP blocks per
+// 128-k stage): 128 x 128 tiles (4 waves of 64 x 64) or 64 x 64 tiles (4
+// waves of 32 x 32), three stages, one tile per workgroup.
+template <int VAR, int FM, int FN, int SBP>
+struct BsKernel {
+    using Cfg = PipeCfg<VAR, FM, FN, 2, 2, 128, 3, SBP>;
+    template <int OUT>
+    static void *fn()
+    {
+        return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, 2, 2, 128, 3, OUT, false, SBP>);
+    }
+};
+
+template <class TK, int OUT>
+lpgemm_status launch_bs(int tiles_m, int tiles_n, const uint8_t *a, const uint8_t *b, Epilogue epi,
+                        int m, int n, int k, hipStream_t stream)
+{
+    static std::once_flag once[kMaxDevices];
+    static hipError_t attr_err[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERR_HIP;
+    std::call_once(once[dev], [dev] {
+        attr_err[dev] = hipFuncSetAttribute(TK::template fn<OUT>(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            TK::Cfg::LDS_BYTES_ALL);
+    });
+    if (attr_err[dev] != hipSuccess) return LPGEMM_ERR_HIP;
+    int xcds = kXcds, kc = k;
+    void *args[] = {(void *)&a,       (void *)&b,       (void *)&epi,  (void *)&m,    (void *)&n,
+                    (void *)&k,       (void *)&tiles_m, (void *)&tiles_n, (void *)&xcds, (void *)&kc};
+    const hipError_t e = hipLaunchKernel(TK::template fn<OUT>(), dim3((unsigned)(tiles_m * tiles_n)),
+                                         dim3(TK::Cfg::kThreads), args, TK::Cfg::LDS_BYTES_ALL, stream);
+    return e == hipSuccess ? LPGEMM_OK : LPGEMM_ERR_HIP;
+}
+
+template <int VAR, int OUT, int SBP>
+lpgemm_status launch_bs_tile(int tile, int tiles_m, int tiles_n, const uint8_t *a, const uint8_t *b,
+                             Epilogue epi, int m, int n, int k, hipStream_t stream)
+{
+    return tile == 128 ? launch_bs<BsKernel<VAR, 2, 2, SBP>, OUT>(tiles_m, tiles_n, a, b, epi, m, n, k, stream)
+                       : launch_bs<BsKernel<VAR, 1, 1, SBP>, OUT>(tiles_m, tiles_n, a, b, epi, m, n, k, stream);
+}
+
+template <int VAR, int OUT>
+lpgemm_status launch_blockscaled(const uint8_t *A, const uint8_t *B, Epilogue epi, int64_t M,
+                                 int64_t N, int64_t K, hipStream_t stream)
+{
+    const uintptr_t d_align = OUT == OUT_F32 ? 16u : 8u;
+    const bool fast = K > 0 && K % 32 == 0 && aligned16(A) && aligned16(B) &&
+                      (reinterpret_cast<uintptr_t>(epi.out) & (d_align - 1)) == 0;
+    const int forced = t_override;
+    const bool t128 = forced == LPGEMM_KERNEL_TILED_128, t64 = forced == LPGEMM_KERNEL_TILED_64;
+    if (forced != LPGEMM_KERNEL_AUTO && forced != LPGEMM_KERNEL_TILED && forced != LPGEMM_KERNEL_GENERAL &&
+        !t128 && !t64)
+        return LPGEMM_ERR_UNSUPPORTED;
+    if ((forced == LPGEMM_KERNEL_TILED || t128 || t64) && !fast) return LPGEMM_ERR_UNSUPPORTED;
+    if (!fast || forced == LPGEMM_KERNEL_GENERAL) {
+        if (ceil_div(M, 16) > 65535 || ceil_div(N, 16) > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+        const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16));
+        hipLaunchKernelGGL((gemm_blockscaled_general_kernel<VAR, OUT>), grid, dim3(256), 0, stream, A, B, epi,
+                           M, N, K);
+        return launched();
+    }
+    // 64-tiles where 128-tiles would leave more than half the compute units idle
+    const int64_t small_tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    const int tile = t128 ? 128 : t64 ? 64 : small_tiles * 2 >= (int64_t)device_cu_count() ? 128 : 64;
+    const int64_t tiles_m = ceil_div(M, tile), tiles_n = ceil_div(N, tile);
+    if (tiles_m * tiles_n > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+    const int m = (int)M, n = (int)N, k = (int)K, tm = (int)tiles_m, tn = (int)tiles_n;
+    switch (epi.lg) {
+    case 5: return launch_bs_tile<VAR, OUT, 4>(tile, tm, tn, A, B, epi, m, n, k, stream);
+    case 6: return launch_bs_tile<VAR, OUT, 2>(tile, tm, tn, A, B, epi, m, n, k, stream);
+    default: return launch_bs_tile<VAR, OUT, 1>(tile, tm, tn, A, B, epi, m, n, k, stream);
+    }
+}
+
+// Arguments of the block-scaled entry points; then the launch.
+template <int VAR>
+lpgemm_status run_blockscaled(const void *A, const uint8_t *B, const float *SFA, const float *SFB,
+                              int64_t g, void *D, lpgemm_out_dtype out_dtype, int64_t M, int64_t N,
+                              int64_t K, hipStream_t stream)
+{
+    if (M < 0 || N < 0 || K < 0 || (K & 1)) return LPGEMM_ERR_INVALID_ARG;
+    if (g < 32 || g > ((int64_t)1 << 30) || (g & (g - 1))) return LPGEMM_ERR_INVALID_ARG;
+    const int f = out_format_of(out_dtype);
+    if (f < 0) return LPGEMM_ERR_INVALID_ARG;
+    if (K > LPGEMM_MAX_K) return LPGEMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return LPGEMM_OK;
+    const uintptr_t d_elt = f == OUT_F32 ? 4u : 2u;
+    if (D == nullptr || (reinterpret_cast<uintptr_t>(D) & (d_elt - 1))) return LPGEMM_ERR_INVALID_ARG;
+    if (K > 0 && (A == nullptr || B == nullptr || SFA == nullptr || SFB == nullptr ||
+                  (reinterpret_cast<uintptr_t>(SFA) & 3u) || (reinterpret_cast<uintptr_t>(SFB) & 3u)))
+        return LPGEMM_ERR_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
+    int lg = 0;
+    while (((int64_t)1 << lg) < g) ++lg;
+    Epilogue epi{D, SFA, SFB};
+    epi.nb = (int32_t)ceil_div(K, g);
+    epi.lg = lg;
+    const uint8_t *a = static_cast<const uint8_t *>(A);
+    (void)hipGetLastError();
+    switch (f) {
+    case OUT_F32: return launch_blockscaled<VAR, OUT_F32>(a, B, epi, M, N, K, stream);
+    case OUT_BF16: return launch_blockscaled<VAR, OUT_BF16>(a, B, epi, M, N, K, stream);
+    default: return launch_blockscaled<VAR, OUT_F16>(a, B, epi, M, N, K, stream);
+    }
+}
+
 lpgemm_status run_elementwise(bool pack, const void *src, void *dst, int64_t rows, int64_t K,
                               hipStream_t stream)
 {
@@ -807,6 +915,22 @@ lpgemm_status lpgemm_w4a8_scaled(const int8_t *A, const uint8_t *B_packed, const
     if (f < 0) return LPGEMM_ERR_INVALID_ARG;
     return run_gemm(LPGEMM_VARIANT_W4A8, A, B_packed, D, scale_a, scale_b, f, M, N, K, nullptr, 0,
                     stream);
+}
+
+lpgemm_status lpgemm_int4_int4_blockscaled(const void *A_packed, const void *B_packed, const float *SFA,
+                                           const float *SFB, int64_t g, void *D,
+                                           lpgemm_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                                           hipStream_t stream)
+{
+    return run_blockscaled<I4I4>(A_packed, static_cast<const uint8_t *>(B_packed), SFA, SFB, g, D, out_dtype,
+                                 M, N, K, stream);
+}
+
+lpgemm_status lpgemm_w4a8_blockscaled(const int8_t *A, const uint8_t *B_packed, const float *SFA,
+                                      const float *SFB, int64_t g, void *D, lpgemm_out_dtype out_dtype,
+                                      int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    return run_blockscaled<W4A8>(A, B_packed, SFA, SFB, g, D, out_dtype, M, N, K, stream);
 }
 
 lpgemm_status lpgemm_fp8_e4m3(const uint8_t *A, const uint8_t *B, void *C,

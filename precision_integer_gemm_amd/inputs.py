@@ -127,6 +127,15 @@ def scale_vector(seed: int, which: int, n: int, lo_exp: int = -12, hi_exp: int =
     return bits.view(np.float32)
 
 
+def block_scale_table(seed: int, which: int, rows: int, K: int, g: int, lo_exp: int = -12,
+                      hi_exp: int = 0) -> np.ndarray:
+    """float32 scales [rows, ceil(K / g)] for the per-K-block scaled product
+    (which = 0: SFA, 1: SFB), drawn like scale_vector (random sign, exponent in
+    [lo_exp, hi_exp], random 23-bit mantissa) from the same streams."""
+    nb = -(-K // g)
+    return scale_vector(seed, which, rows * nb, lo_exp, hi_exp).reshape(rows, nb)
+
+
 def fp8_codes(seed: int, which: int, rows: int, K: int, fmt: str = "e4m3") -> np.ndarray:
     """Uniform random fp8 bytes [rows, K] for the fp8 workload (which = 0: A,
     1: B), drawn from stream (seed << 8) | which, every operand finite: for
