@@ -21,9 +21,10 @@ workload after a 512 MiB read that evicts its operands from L2 and MALL;
 `per_config_scaled_bf16` times the scaled product (per-row and per-column
 scales, bf16 output) of each workload alone; `per_config_fp8` times the second
 workload, the fp8 GEMM (e4m3 and e5m2 operands) with fp32 output, at 4096^3
-and 8192^3, and
-`per_config_long_k` W4A8 decode shapes with K = 28672 on the narrow-M kernel's
-split-K path (both outside the step and `value`).  `ceiling` holds what the chip sustains, measured
+and 8192^3; `per_config_blockscaled` the per-K-block scaled product (g = 128
+and 32, bf16 output) on three workloads; and `per_config_long_k` W4A8 decode
+shapes with K = 28672 on the narrow-M kernel's split-K path (all outside the
+step and `value`).  `ceiling` holds what the chip sustains, measured
 live by the probe kernels of _ceiling.so (matrix cores only, per format; LDS
 reads; the FP6 GEMM's inner loop without global memory), and `roofline`
 adds the dominant call's fraction of the sustained ceiling of its format.
@@ -56,6 +57,14 @@ PEAK_INT8_TOPS = 5000.0
 PEAK_FP8_TOPS = 5000.0
 PEAK_FP6_TOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
+# Vector ALU, one non-packed 32-bit operation per lane: the published fp32
+# vector peak (157.3 TFLOP/s) counts packed FMAs (2 flops x 2 values per
+# lane slot), so one plain operation per lane per cycle is a quarter of it:
+# 256 CUs x 64 lanes x 2.4 GHz = 39.3 T lane-operations/s.
+PEAK_VALU_TOPS = 157.3 / 4.0
+# Per output element and K block, the block-scaled product needs at least
+# four binary32 operations: convert the partial, two multiplies, one add.
+BLOCK_OPS = 4
 
 # Step order: each W4A8 skinny call reads a B that no call has touched for
 # >= 300 MB of other traffic, so it streams from HBM, not the 256 MB MALL.
@@ -537,6 +546,54 @@ def main() -> int:
                               "roofline_frac": round(max(t_mfma, t_hbm) / (med * 1e-6), 4)}
             del copies, D
 
+    # The per-K-block scaled product (bf16 output) on three workloads, g = 128
+    # and 32, alone and timed like `per_config_scaled_bf16`.  Its roofline
+    # takes the largest of the matrix-core time, the HBM time and the vector
+    # ALU time of BLOCK_OPS operations per output element and block.
+    blockscaled = {}
+    if args.isolated_reps > 0:
+        from precision_integer_gemm_amd.inputs import block_scale_table
+        by_name = {w["case"].name: w for w in work}
+        for name, g in (("w4a8_4096", 128), ("w4a8_4096", 32), ("i4i4_8192", 128),
+                        ("w4a8_skinny_m16", 128)):
+            if name not in by_name:
+                continue
+            w = by_name[name]
+            c = w["case"]
+            nb = -(-c.K // g)
+            sfa = torch.from_numpy(block_scale_table(c.seed, 0, c.M, c.K, g)).to(dev)
+            sfb = torch.from_numpy(block_scale_table(c.seed, 1, c.N, c.K, g)).to(dev)
+            D = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
+            fn = L.lib().lpgemm_int4_int4_blockscaled if c.variant == "i4i4" else L.lib().lpgemm_w4a8_blockscaled
+            copies = [w["b"]] + [w["b"].clone() for _ in range(2 if c.b_bytes > (64 << 20) else 0)]
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.isolated_reps)]
+            for j in range(-1, args.isolated_reps):
+                if j >= 0:
+                    evs[j][0].record(stream)
+                st = fn(w["a"].data_ptr(), copies[max(j, 0) % len(copies)].data_ptr(), sfa.data_ptr(),
+                        sfb.data_ptr(), g, D.data_ptr(), L.OUT_BF16, c.M, c.N, c.K, handle)
+                if j >= 0:
+                    evs[j][1].record(stream)
+                if st != L.OK:
+                    raise RuntimeError(f"{c.name} blockscaled: {L.lpgemm_status_string(st)}")
+            torch.cuda.synchronize()
+            us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+            med = float(np.median(us))
+            d_bytes = c.a_bytes + c.b_bytes + 2 * c.M * c.N + 4 * nb * (c.M + c.N)
+            t_mfma = c.ops / (PEAK_INT8_TOPS * 1e12)
+            t_hbm = d_bytes / (PEAK_HBM_GBS * 1e9)
+            t_alu = BLOCK_OPS * c.M * c.N * nb / (PEAK_VALU_TOPS * 1e12)
+            t_roof = max(t_mfma, t_hbm, t_alu)
+            bound = "mfma" if t_roof == t_mfma else "hbm" if t_roof == t_hbm else "alu"
+            blockscaled[f"{name}_g{g}"] = {
+                "out": "bf16", "g": g, "median_us": round(med, 3), "min_us": round(float(us.min()), 3),
+                "tops": round(c.ops / (med * 1e-6) / 1e12, 2), "gbs": round(d_bytes / (med * 1e-6) / 1e9, 1),
+                "roofline_us": {"mfma": round(t_mfma * 1e6, 2), "hbm": round(t_hbm * 1e6, 2),
+                                "alu": round(t_alu * 1e6, 2)},
+                "bound": bound, "roofline_frac": round(t_roof / (med * 1e-6), 4)}
+            del copies, D
+
     # The second workload, the fp8 GEMM (e4m3 and e5m2 operands) with fp32
     # accumulation and fp32 output, alone (not part of the step or of `value`): priced at the
     # 5.0 PFLOP/s dense fp8 peak.
@@ -688,6 +745,7 @@ def main() -> int:
         "per_config_cold": cold,
         "per_config_scaled_bf16": scaled,
         "per_config_fp8": fp8,
+        "per_config_blockscaled": blockscaled,
         "per_config_long_k": long_k,
         "ceiling": ceiling,
     }

@@ -111,7 +111,7 @@ __device__ __forceinline__ int lds_chunk(int row, int col)
 
 template <int VAR, int FM, int FN, int WM, int WN, int BK, int STAGES, int OUT, bool SPLIT = false,
           int SBP = 0>
-__global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pipelined_kernel(
+__global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN == 4)) ? 2 : 1) void gemm_pipelined_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N,
     int K, int tiles_m, int tiles_n, int xcds, int kc)
 {
@@ -330,32 +330,72 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     // Block scales: fp32 accumulators, and the scale rows of one block.
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     f32x16 facc[SBP > 0 ? FN : 1][SBP > 0 ? FM : 1];
-    // SFA[m][j] of this lane's rows and SFB[n][j] of its columns (four groups
-    // of four) for block j, which lies in the stage of K tile kt.
-    auto block_scales = [&](int kt, int j, float (&sa)[FM], f32x4 (&sb)[FN][4]) {
-        const int jj = j - ((kt * BK) >> lg);
-        const float *slot = reinterpret_cast<const float *>(smem + STAGES * Cfg::STAGE_BYTES +
-                                                            (kt % (STAGES + 1)) * Cfg::SCALE_SLOT_BYTES);
-        const float *ta = slot + jj * Cfg::BM;
-        const float *tb = slot + Cfg::BM * SBP + jj * Cfg::BN;
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) sa[fm] = ta[(wm * FM + fm) * 32 + r32];
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg)
-                sb[fn][rg] = *reinterpret_cast<const f32x4 *>(tb + (wn * FN + fn) * 32 + 8 * rg + 4 * h);
-    };
     // fa += ((float)C_j * SFA) * SFB element by element, each operation a
-    // binary32 one rounding to nearest even (c holds C_j << SHIFT, exactly).
-    auto add_block = [&](f32x16 &fa, const i32x16 &c, float sa, const f32x4 (&sb)[4]) {
+    // binary32 one rounding to nearest even; c holds C_j << SHIFT exactly.
+    // PRE: sa already holds SFA * 2^-SHIFT, and (float)c * sa is then the
+    // same real number as C_j * SFA, so it rounds to the same binary32 value
+    // with one operation less (see prescale).
+    auto add_block = [&](auto pre, f32x16 &fa, const i32x16 &c, float sa,
+                         const f32x4 (&sb)[4]) __attribute__((always_inline)) {
+        constexpr bool PRE = decltype(pre)::value;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float t = (float)(c[r] >> Cfg::SHIFT);
+            const float t = PRE ? (float)c[r] : (float)(c[r] >> Cfg::SHIFT);
             const float y = t * sa;
             float z = y * sb[r / 4][r % 4];
             asm volatile("" : "+v"(z));  // two separate roundings, no fused operation
             fa[r] = fa[r] + z;
+        }
+    };
+    // Fold 2^-SHIFT into this wave's SFA values when that is exact for every
+    // lane: (float)c is exact while |c| <= 2^24, which |C_j| <= 64 g (int4 x
+    // int4) or 1024 g (W4A8) guarantees for g <= 1024, and SFA * 2^-SHIFT is
+    // exact unless it falls below the normal range.  Wave-uniform answer.
+    auto prescale = [&](float (&sa)[FM]) __attribute__((always_inline)) {
+        bool ok = lg <= 10;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const float a = __builtin_fabsf(sa[fm]);
+            ok = ok && (a == 0.f || !(a < 0x1p-126f * (float)(1 << Cfg::SHIFT)));
+        }
+        if (!__all(ok)) return false;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) sa[fm] *= 1.0f / (float)(1 << Cfg::SHIFT);
+        return true;
+    };
+    using Pre = std::true_type;
+    using Raw = std::false_type;
+    // Add block j (a block of the stage of K tile kt) held in acc to facc and
+    // clear acc: SFA[m][j] of this lane's rows, SFB[n][j] of its columns (four
+    // groups of four), read from the stage's scale slot.
+    auto flush = [&](int kt, int j) __attribute__((always_inline)) {
+        if constexpr (SBP > 0) {
+            const int jj = j - ((kt * BK) >> lg);
+            const float *slot = reinterpret_cast<const float *>(smem + STAGES * Cfg::STAGE_BYTES +
+                                                                (kt % (STAGES + 1)) * Cfg::SCALE_SLOT_BYTES);
+            const float *ta = slot + jj * Cfg::BM;
+            const float *tb = slot + Cfg::BM * SBP + jj * Cfg::BN;
+            float sa[FM];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) sa[fm] = ta[(wm * FM + fm) * 32 + r32];
+            auto body = [&](auto pre) __attribute__((always_inline)) {
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    f32x4 sb[4];
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg)
+                        sb[rg] = *reinterpret_cast<const f32x4 *>(tb + (wn * FN + fn) * 32 + 8 * rg + 4 * h);
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) {
+                        add_block(pre, facc[fn][fm], acc[fn][fm], sa[fm], sb);
+                        acc[fn][fm] = Acc{};
+                    }
+                }
+            };
+            if (prescale(sa))
+                body(Pre{});
+            else
+                body(Raw{});
         }
     };
 
@@ -397,50 +437,65 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_pip
     // g >= 64: the step's products go into the int32 accumulators, which are
     // added and cleared where the step ends block j (or ends K).  Blocks at
     // or past nb (the zero-filled steps after K) are skipped.
-    auto compute_scaled = [&](const Frags &f, int kt, int st) {
+    auto compute_scaled = [&](const Frags &f, int kt, int st) __attribute__((always_inline)) {
         if constexpr (SBP > 0) {
             const int ks = kt * BK + 64 * st;  // the step's first k
             if constexpr (K32) {
                 const int j1 = ks >> 5;
                 if (j1 >= nb) return;
-                const bool second = j1 + 1 < nb;
-                float sa1[FM], sa2[FM];
-                f32x4 sb1[FN][4], sb2[FN][4];
-                block_scales(kt, j1, sa1, sb1);
-                if (second) block_scales(kt, j1 + 1, sa2, sb2);
-                i32x4 a_lo[FM], a_hi[FM];
+                i32x4 a_lo[FM], a_hi[FM], b_lo[FN], b_hi[FN];
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    if (VAR == I4I4) {
+                        unpack_chunk<false>(f.a[fm][0], a_lo[fm], a_hi[fm]);
+                    } else {
+                        a_lo[fm] = f.a[fm][0];
+                        a_hi[fm] = f.a[fm][AV - 1];
+                    }
+                }
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
-                    i32x4 b_lo, b_hi;
-                    unpack_chunk<VAR == W4A8>(f.b[fn][0], b_lo, b_hi);
+                    unpack_chunk<VAR == W4A8>(f.b[fn][0], b_lo[fn], b_hi[fn]);
 #pragma unroll
-                    for (int fm = 0; fm < FM; ++fm) {
-                        if (fn == 0) {
-                            if (VAR == I4I4) {
-                                unpack_chunk<false>(f.a[fm][0], a_lo[fm], a_hi[fm]);
-                            } else {
-                                a_lo[fm] = f.a[fm][0];
-                                a_hi[fm] = f.a[fm][AV - 1];
-                            }
-                        }
-                        add_block(facc[fn][fm], mfma_32x32x32(b_lo, a_lo[fm], i32x16{}), sa1[fm], sb1[fn]);
-                        if (second)
-                            add_block(facc[fn][fm], mfma_32x32x32(b_hi, a_hi[fm], i32x16{}), sa2[fm], sb2[fn]);
-                    }
+                    for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_32x32x32(b_lo[fn], a_lo[fm], i32x16{});
+                }
+                flush(kt, j1);
+                if (j1 + 1 < nb) {
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_32x32x32(b_hi[fn], a_hi[fm], i32x16{});
+                    flush(kt, j1 + 1);
                 }
             } else {
                 compute(f, kt, st);
                 const int j = ks >> lg;
                 const bool ends = ((ks + 64) & ((1 << lg) - 1)) == 0 || ks + 64 >= K;
                 if (j < nb && ends) {
+                    // all scale rows first, then the unfolded terms: with two
+                    // waves of 64 x 64 per SIMD this measured faster than the
+                    // folded form and per-column-group reads (4096^3 W4A8, g =
+                    // 128: 159 against 176 us)
+                    const int jj = j - ((kt * BK) >> lg);
+                    const float *slot = reinterpret_cast<const float *>(
+                        smem + STAGES * Cfg::STAGE_BYTES + (kt % (STAGES + 1)) * Cfg::SCALE_SLOT_BYTES);
+                    const float *ta = slot + jj * Cfg::BM;
+                    const float *tb = slot + Cfg::BM * SBP + jj * Cfg::BN;
                     float sa[FM];
                     f32x4 sb[FN][4];
-                    block_scales(kt, j, sa, sb);
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) sa[fm] = ta[(wm * FM + fm) * 32 + r32];
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int rg = 0; rg < 4; ++rg)
+                            sb[fn][rg] =
+                                *reinterpret_cast<const f32x4 *>(tb + (wn * FN + fn) * 32 + 8 * rg + 4 * h);
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                         for (int fm = 0; fm < FM; ++fm) {
-                            add_block(facc[fn][fm], acc[fn][fm], sa[fm], sb[fn]);
+                            add_block(Raw{}, facc[fn][fm], acc[fn][fm], sa[fm], sb[fn]);
                             acc[fn][fm] = Acc{};
                         }
                 }

@@ -703,15 +703,17 @@ int out_format_of(lpgemm_out_dtype d)
 
 // ---- per-K-block scaled product ----------------------------------------------
 // The tiled kernel with block scales (gemm_pipelined.hpp, SBP blocks per
-// 128-k stage): 128 x 128 tiles (4 waves of 64 x 64) or 64 x 64 tiles (4
-// waves of 32 x 32), three stages, one tile per workgroup.
-template <int VAR, int FM, int FN, int SBP>
+// 128-k stage): 128 x 128 tiles (8 waves of 64 x 32: the fp32 accumulators
+// beside the int32 ones fit two waves per SIMD without spilling, which 4
+// waves of 64 x 64 do not) or 64 x 64 tiles (4 waves of 32 x 32), three
+// stages, one tile per workgroup.
+template <int VAR, int FM, int FN, int WM, int WN, int SBP>
 struct BsKernel {
-    using Cfg = PipeCfg<VAR, FM, FN, 2, 2, 128, 3, SBP>;
+    using Cfg = PipeCfg<VAR, FM, FN, WM, WN, 128, 3, SBP>;
     template <int OUT>
     static void *fn()
     {
-        return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, 2, 2, 128, 3, OUT, false, SBP>);
+        return reinterpret_cast<void *>(&gemm_pipelined_kernel<VAR, FM, FN, WM, WN, 128, 3, OUT, false, SBP>);
     }
 };
 
@@ -740,8 +742,12 @@ template <int VAR, int OUT, int SBP>
 lpgemm_status launch_bs_tile(int tile, int tiles_m, int tiles_n, const uint8_t *a, const uint8_t *b,
                              Epilogue epi, int m, int n, int k, hipStream_t stream)
 {
-    return tile == 128 ? launch_bs<BsKernel<VAR, 2, 2, SBP>, OUT>(tiles_m, tiles_n, a, b, epi, m, n, k, stream)
-                       : launch_bs<BsKernel<VAR, 1, 1, SBP>, OUT>(tiles_m, tiles_n, a, b, epi, m, n, k, stream);
+    if (tile == 64)
+        return launch_bs<BsKernel<VAR, 1, 1, 2, 2, SBP>, OUT>(tiles_m, tiles_n, a, b, epi, m, n, k, stream);
+    if constexpr (SBP == 4)
+        return launch_bs<BsKernel<VAR, 2, 1, 2, 4, SBP>, OUT>(tiles_m, tiles_n, a, b, epi, m, n, k, stream);
+    else
+        return launch_bs<BsKernel<VAR, 2, 2, 2, 2, SBP>, OUT>(tiles_m, tiles_n, a, b, epi, m, n, k, stream);
 }
 
 template <int VAR, int OUT>
@@ -764,9 +770,14 @@ lpgemm_status launch_blockscaled(const uint8_t *A, const uint8_t *B, Epilogue ep
                            M, N, K);
         return launched();
     }
-    // 64-tiles where 128-tiles would leave more than half the compute units idle
+    // 64-tiles for up to 64 rows (16 x 28672 x 8192, g = 128: 67 against 80 us)
+    // and where 128-tiles would leave more than half the compute units idle;
+    // else 128-tiles (4096^3 W4A8, g = 128: 188 against 238 us)
     const int64_t small_tiles = ceil_div(M, 128) * ceil_div(N, 128);
-    const int tile = t128 ? 128 : t64 ? 64 : small_tiles * 2 >= (int64_t)device_cu_count() ? 128 : 64;
+    const int tile = t128 ? 128
+                     : t64 ? 64
+                     : M > 64 && small_tiles * 2 >= (int64_t)device_cu_count() ? 128
+                                                                                  : 64;
     const int64_t tiles_m = ceil_div(M, tile), tiles_n = ceil_div(N, tile);
     if (tiles_m * tiles_n > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
     const int m = (int)M, n = (int)N, k = (int)K, tm = (int)tiles_m, tn = (int)tiles_n;

@@ -98,6 +98,24 @@ int main()
                                      32, nullptr, 0, nullptr) == LPGEMM_ERR_INVALID_ARG);
     CHECK(lpgemm_fp8_e5m2((const uint8_t *)P, (const uint8_t *)P, C, LPGEMM_OUT_FP8_E4M3, 4, 4, 16, nullptr) ==
           LPGEMM_ERR_INVALID_ARG);
+    // block-scaled products: every argument error before any HIP call
+    const float *F = (const float *)P;
+    for (int64_t g : {0L, 16L, 48L, 100L, (int64_t)1 << 31})
+        CHECK(lpgemm_int4_int4_blockscaled(P, P, F, F, g, W, LPGEMM_OUT_F32, 4, 4, 64, nullptr) ==
+              LPGEMM_ERR_INVALID_ARG);
+    CHECK(lpgemm_w4a8_blockscaled((const int8_t *)P, (const uint8_t *)P, F, F, 32, W, LPGEMM_OUT_FP8_E4M3, 4, 4,
+                                  64, nullptr) == LPGEMM_ERR_INVALID_ARG);
+    CHECK(lpgemm_w4a8_blockscaled((const int8_t *)P, (const uint8_t *)P, F, F, 32, W, LPGEMM_OUT_F32, 4, 4, 63,
+                                  nullptr) == LPGEMM_ERR_INVALID_ARG);
+    CHECK(lpgemm_int4_int4_blockscaled(P, P, nullptr, F, 32, W, LPGEMM_OUT_BF16, 4, 4, 64, nullptr) ==
+          LPGEMM_ERR_INVALID_ARG);
+    CHECK(lpgemm_int4_int4_blockscaled(P, P, F, (const float *)((const char *)P + 2), 32, W, LPGEMM_OUT_BF16, 4, 4,
+                                       64, nullptr) == LPGEMM_ERR_INVALID_ARG);
+    CHECK(lpgemm_int4_int4_blockscaled(P, P, F, F, 32, (char *)W + 1, LPGEMM_OUT_F16, 4, 4, 64, nullptr) ==
+          LPGEMM_ERR_INVALID_ARG);
+    CHECK(lpgemm_int4_int4_blockscaled(P, P, F, F, 32, W, LPGEMM_OUT_F32, 4, 4, 131072, nullptr) ==
+          LPGEMM_ERR_UNSUPPORTED);
+    CHECK(lpgemm_int4_int4_blockscaled(P, P, F, F, 32, W, LPGEMM_OUT_F32, 0, 4, 64, nullptr) == LPGEMM_OK);
     CHECK(lpgemm_fp8_e4m3((const uint8_t *)P, (const uint8_t *)P, C, LPGEMM_OUT_FP8_E5M2, 4, 4, 16, nullptr) ==
           LPGEMM_ERR_INVALID_ARG);
     CHECK(lpgemm_pack_int4((const int8_t *)P, (uint8_t *)W, 3, 5, nullptr) == LPGEMM_ERR_INVALID_ARG);

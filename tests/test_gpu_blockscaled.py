@@ -213,3 +213,24 @@ def test_tensor_wrappers(torch):
     with pytest.raises(ValueError):
         L.lpgemm_w4a8_blockscaled(torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
                                   torch.from_numpy(sfa[:, :1].copy()).to(dev), torch.from_numpy(sfb).to(dev), g)
+
+
+@pytest.mark.parametrize("kernel", ["t128", "t64", "general"])
+@pytest.mark.parametrize("variant", ["i4i4", "w4a8"])
+def test_tiny_scales_and_long_blocks(torch, variant, kernel):
+    # the tiled kernel folds 2^-shift into SFA only where that is exact: here
+    # some SFA rows sit at or below 2^-118 (subnormal once folded, or
+    # subnormal already), and g = 2048 lets a block's partial exceed what a
+    # folded conversion keeps exact; every such wave must take the unfolded
+    # path and still match the oracle bit for bit (subnormal results included)
+    M, N, K = 96, 80, 4160
+    for g, seed in ((2048, 31), (64, 32), (32, 33)):
+        say(f"blockscaled tiny scales {variant} {kernel} g={g}")
+        A, B, sfa, sfb = case(variant, M, N, K, g, seed)
+        sfa[5] = np.float32(2.0 ** -125)
+        sfa[37] = np.float32(3 * 2.0 ** -140)              # subnormal
+        sfa[70, :] = np.float32(-1.5 * 2.0 ** -119)
+        sfb[3] = np.float32(2.0 ** -20)                    # products into the subnormal range
+        want = oracle.gemm_blockscaled(variant, A, B, sfa, sfb, M, N, K, g, oracle.FMT_F32)
+        assert (np.abs(want[37]) < 2.0 ** -126).any() or (want[37] == 0).all()
+        check(run_bs(torch, variant, A, B, sfa, sfb, g, M, N, K, "f32", KERNELS[kernel]), want)
