@@ -253,8 +253,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328134.0, "fetch_scale": 2.0, "write_kib": 364860.1,
-                  "write_scale": 1.0, "sources_sha256": "d8dcb8a5b05d453781ccc2fed9c1dc55e3b85ee3be7d365a5b910ebb5d04ebdf"},
+    "i4i4_8192": {"fetch_kib": 327967.8, "fetch_scale": 2.0, "write_kib": 361256.6,
+                  "write_scale": 1.0, "sources_sha256": "913508a16e6e83de6db002c41a32c43b4d306c2f4f05c21856ce0aa97a93f5d0"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",
