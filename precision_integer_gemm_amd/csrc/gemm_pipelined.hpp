@@ -325,8 +325,6 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
     // Integer accumulators for the int4 / int8 formats, fp32 for fp8.
     using Acc = typename std::conditional<is_fp8(VAR), f32x16, i32x16>::type;
     Acc acc[FN][FM];
-    // Unpack and contract one 64-k step: per block two 32x32x32 int8 MFMAs,
-    // or one 32x32x64 fp8 MFMA (lane l: 32 consecutive k, 32 (l / 32) onward).
     // Block scales: fp32 accumulators, and the scale rows of one block.
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     f32x16 facc[SBP > 0 ? FN : 1][SBP > 0 ? FM : 1];
@@ -399,6 +397,8 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
         }
     };
 
+    // Unpack and contract one 64-k step: per block two 32x32x32 int8 MFMAs,
+    // or one 32x32x64 fp8 MFMA (lane l: 32 consecutive k, 32 (l / 32) onward).
     auto compute = [&](const Frags &f, int kt, int st) {
         (void)kt;
         (void)st;
