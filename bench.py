@@ -254,7 +254,7 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
     "i4i4_8192": {"fetch_kib": 327967.8, "fetch_scale": 2.0, "write_kib": 361256.6,
-                  "write_scale": 1.0, "sources_sha256": "913508a16e6e83de6db002c41a32c43b4d306c2f4f05c21856ce0aa97a93f5d0"},
+                  "write_scale": 1.0, "sources_sha256": "28535d277e12a177604c9adfeee98d339ffd6a27d9b036a1e07f46c50ecd9442"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",
