@@ -471,3 +471,50 @@ def test_fp8_input_codes_are_finite_and_seeded():
     assert not np.array_equal(fp8_codes(5, 1, 64, 512), a)        # A and B differ
     with pytest.raises(ValueError):
         fp8_codes(5, 0, 4, 4, "e3m4")
+
+
+@pytest.mark.parametrize("fn", ["lpgemm_int4_int4_blockscaled", "lpgemm_w4a8_blockscaled"])
+def test_blockscaled_argument_errors(fn):
+    # every rejection happens before any HIP call
+    f = getattr(L.lib(), fn)
+    for g in (0, 16, 48, 100, 1 << 31, -32):
+        assert f(P, P, P, P, g, P, L.OUT_F32, 4, 4, 64, None) == L.ERR_INVALID_ARG, g
+    assert f(P, P, P, P, 32, P, L.OUT_FP8_E4M3, 4, 4, 64, None) == L.ERR_INVALID_ARG   # fp8 out
+    assert f(P, P, P, P, 32, P, 9, 4, 4, 64, None) == L.ERR_INVALID_ARG                # unknown out
+    assert f(P, P, P, P, 32, P, L.OUT_F32, 4, 4, 63, None) == L.ERR_INVALID_ARG        # odd K
+    assert f(P, P, P, P, 32, P, L.OUT_F32, -1, 4, 64, None) == L.ERR_INVALID_ARG       # negative M
+    assert f(P, P, None, P, 32, P, L.OUT_F32, 4, 4, 64, None) == L.ERR_INVALID_ARG     # null SFA
+    assert f(P, P, P, None, 32, P, L.OUT_F32, 4, 4, 64, None) == L.ERR_INVALID_ARG     # null SFB
+    assert f(P, P, P + 2, P, 32, P, L.OUT_F32, 4, 4, 64, None) == L.ERR_INVALID_ARG    # misaligned SFA
+    assert f(P, P, P, P, 32, P + 2, L.OUT_F32, 4, 4, 64, None) == L.ERR_INVALID_ARG    # misaligned fp32 D
+    assert f(P, P, P, P, 32, P + 1, L.OUT_BF16, 4, 4, 64, None) == L.ERR_INVALID_ARG   # misaligned bf16 D
+    assert f(P, P, P, P, 32, None, L.OUT_F32, 4, 4, 64, None) == L.ERR_INVALID_ARG     # null D
+    assert f(P, P, P, P, 32, P, L.OUT_F32, 4, 4, L.MAX_K + 2, None) == L.ERR_UNSUPPORTED
+    assert f(None, None, None, None, 32, None, L.OUT_F32, 0, 4, 64, None) == L.OK       # empty
+    L.lpgemm_set_kernel_override(L.KERNEL_SKINNY)
+    try:
+        assert f(P, P, P, P, 32, P, L.OUT_F32, 4, 4, 64, None) == L.ERR_UNSUPPORTED
+    finally:
+        L.lpgemm_set_kernel_override(L.KERNEL_AUTO)
+
+
+@pytest.mark.parametrize("fn,own", [("lpgemm_fp8_e4m3", L.OUT_FP8_E4M3), ("lpgemm_fp8_e5m2", L.OUT_FP8_E5M2)])
+def test_fp8_argument_errors(fn, own):
+    f = getattr(L.lib(), fn)
+    other = L.OUT_FP8_E5M2 if own == L.OUT_FP8_E4M3 else L.OUT_FP8_E4M3
+    assert f(P, P, P, other, 4, 4, 16, None) == L.ERR_INVALID_ARG     # the other format's output
+    assert f(P, P, P, L.OUT_BF16, 4, 4, 16, None) == L.ERR_INVALID_ARG
+    assert f(P, P, P, L.OUT_F32, -1, 4, 16, None) == L.ERR_INVALID_ARG
+    assert f(P, P, None, own, 4, 4, 16, None) == L.ERR_INVALID_ARG
+    assert f(P, P, P, L.OUT_F32, 4, 4, L.MAX_K + 1, None) == L.ERR_UNSUPPORTED
+    assert f(None, None, None, L.OUT_F32, 0, 4, 16, None) == L.OK
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros((4, 16), dtype=torch.uint8)
+    s = torch.ones((4, 1), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        L.lpgemm_int4_int4_blockscaled(a, a, s, s, 32)
+    with pytest.raises(ValueError):
+        L.lpgemm_fp8_e5m2(a, a)
