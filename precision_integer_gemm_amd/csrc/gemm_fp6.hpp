@@ -83,31 +83,34 @@ __device__ __forceinline__ i32x6 e3m2_from_int4(i32x4 q)
 }
 
 // Both operands in one launch, one thread per fragment lane slot.  A
-// workgroup of four waves takes one row block over four consecutive k blocks
-// (wave w: k block 4 g + w), so each 32-row group's 128-byte line of packed
-// input is read once, by the four waves together; lane l of a wave loads the
-// 16 bytes of its slot (row l % 32, k half l / 32), encodes them and writes
-// the slot's 16 + 8 bytes (each wave writes one whole 1.5 KB fragment).
-// Workgroups [0, ga) cover A, the rest B.  Requires K % 32 == 0 and 16-byte
-// aligned operands.  Measured on MI355X against the earlier two launches of
-// a 32-row x 2048-k LDS-staged kernel (outputs byte-identical): 8192^3
-// 34.1 -> 28.2 us (6.0 TB/s of packed reads and FP6 writes), 3000 x 5120 x
-// 6144 20.3 -> 14.0 us, 4096^3 16.0 -> 11.1 us.
-__global__ __launch_bounds__(256) void fp6_convert_pair_kernel(const uint8_t *__restrict__ A,
+// workgroup of kFp6ConvWaves waves takes one row block over that many
+// consecutive k blocks (wave w: k block kFp6ConvWaves g + w), so each 32-row
+// group's 512-byte run of packed input is read once, by the waves together;
+// lane l of a wave loads the 16 bytes of its slot (row l % 32, k half l / 32),
+// encodes them and writes the slot's 16 + 8 bytes (each wave writes one whole
+// 1.5 KB fragment).  Workgroups [0, ga) cover A, the rest B.  Requires
+// K % 32 == 0 and 16-byte aligned operands.  Measured on MI355X with both
+// operands evicted from the caches first (outputs byte-identical): four waves
+// per workgroup 32.6 us for 8192^3 and 16.4 us for 3000 x 5120 x 6144, eight
+// 31.2 / 15.0 us, sixteen 30.4 / 15.4 us (5.5 TB/s of packed reads and FP6
+// writes); two or four k blocks per wave were slower.  (The earlier two
+// launches of a 32-row x 2048-k LDS-staged kernel: 8192^3 34.1 us warm.)
+constexpr int kFp6ConvWaves = 16;
+__global__ __launch_bounds__(64 * kFp6ConvWaves) void fp6_convert_pair_kernel(const uint8_t *__restrict__ A,
                                                                uint8_t *__restrict__ A6, int64_t MA,
                                                                const uint8_t *__restrict__ B,
                                                                uint8_t *__restrict__ B6, int64_t NB,
                                                                int K, int64_t ga)
 {
     const int K64 = (K + 63) / 64;
-    const int kgroups = (K64 + 3) / 4;
+    const int kgroups = (K64 + kFp6ConvWaves - 1) / kFp6ConvWaves;
     const bool is_a = (int64_t)blockIdx.x < ga;
     const int64_t g = is_a ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - ga;
     const uint8_t *X = is_a ? A : B;
     uint8_t *X6 = is_a ? A6 : B6;
     const int64_t R = is_a ? MA : NB;
     const int64_t rb = g / kgroups;
-    const int kb = (int)(g % kgroups) * 4 + (int)(threadIdx.x >> 6);
+    const int kb = (int)(g % kgroups) * kFp6ConvWaves + (int)(threadIdx.x >> 6);
     if (kb >= K64) return;
     const int lane = threadIdx.x & 63;
     const int64_t row = rb * 32 + (lane & 31);

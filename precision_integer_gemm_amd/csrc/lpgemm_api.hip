@@ -300,8 +300,8 @@ lpgemm_status make_plan(lpgemm_variant variant, const void *A, const void *B, co
         p.tiles_m = (int)ceil_div(M, Fp6Tile::BM);
         p.tiles_n = (int)ceil_div(N, Fp6Tile::BN);
         if ((int64_t)p.tiles_m * p.tiles_n > INT32_MAX) return LPGEMM_ERR_UNSUPPORTED;
-        // the conversion grid: one workgroup per row block and four k blocks
-        if ((ceil_div(M, 32) + ceil_div(N, 32)) * ceil_div(ceil_div(K, 64), 4) > INT32_MAX)
+        // the conversion grid: one workgroup per row block and kFp6ConvWaves k blocks
+        if ((ceil_div(M, 32) + ceil_div(N, 32)) * ceil_div(ceil_div(K, 64), kFp6ConvWaves) > INT32_MAX)
             return LPGEMM_ERR_UNSUPPORTED;
         p.workgroups = std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, cu_count);
         p.ws_bytes = fp6_workspace(M, N, K);
@@ -502,9 +502,9 @@ lpgemm_status launch_fp6(const Plan &p, const uint8_t *a, const uint8_t *b, Epil
     const int64_t bytes_a = (int64_t)align_ws((uint64_t)fp6_bytes(m, k));
     uint8_t *a6 = static_cast<uint8_t *>(ws);
     uint8_t *b6 = a6 + bytes_a;
-    const int64_t kgroups = ceil_div(ceil_div(k, 64), 4);
+    const int64_t kgroups = ceil_div(ceil_div(k, 64), kFp6ConvWaves);
     const int64_t ga = ceil_div(m, 32) * kgroups, gb = ceil_div(n, 32) * kgroups;  // < 2^31 (plan)
-    hipLaunchKernelGGL(fp6_convert_pair_kernel, dim3((unsigned)(ga + gb)), dim3(256), 0, stream, a, a6,
+    hipLaunchKernelGGL(fp6_convert_pair_kernel, dim3((unsigned)(ga + gb)), dim3(64 * kFp6ConvWaves), 0, stream, a, a6,
                        (int64_t)m, b, b6, (int64_t)n, k, ga);
     const uint8_t *ca6 = a6, *cb6 = b6;
     int tiles_m = p.tiles_m, tiles_n = p.tiles_n, xcds = kXcds;
