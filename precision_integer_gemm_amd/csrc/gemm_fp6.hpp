@@ -241,9 +241,13 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_fp6
         i32x8 b[FN];
         i32x8 a[FM];
     };
+    // The 8-byte half is read through a volatile LDS pointer: otherwise the
+    // compiler pairs the halves of two fragments into one ds_read2st64_b64,
+    // whose result then has to be moved into the two operands, and waits for
+    // it right after issuing it.
     auto frag_at = [&](const uint8_t *p) {
         const i32x4 lo = *reinterpret_cast<const i32x4 *>(p + 16 * lane);
-        const i32x2 hi = *reinterpret_cast<const i32x2 *>(p + 1024 + 8 * lane);
+        const i32x2 hi = *(const volatile __attribute__((address_space(3))) i32x2 *)(p + 1024 + 8 * lane);
         return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, 0, 0};  // the MFMA reads six dwords
     };
     auto read_frags = [&](int slot, int step, Frags &f) {
@@ -305,6 +309,19 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_fp6
                     read_frags((kt + 1) % STAGES, 0, nxt);
                 }
                 compute(cur);
+                // The next step's fragment reads go out between this step's
+                // first MFMAs (three after each of the first four), so their
+                // latency hides behind the wave's own matrix-core work.
+                constexpr int kReadsPerGroup = 3;
+                constexpr int kGroups = 2 * (FM + FN) / kReadsPerGroup;
+                static_assert(kGroups * kReadsPerGroup == 2 * (FM + FN) && kGroups <= FM * FN,
+                              "fragment reads must spread over whole MFMA groups");
+#pragma unroll
+                for (int g = 0; g < kGroups; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerGroup, 0);  // LDS reads
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - kGroups, 0);
                 // The slot of stage kt is free once every wave has passed the
                 // barrier; its refill goes out after this step's MFMAs.
                 if (st + 1 == KS) issue_stage(kt + STAGES);
