@@ -312,15 +312,16 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_fp6
                 // The next step's fragment reads go out between this step's
                 // first MFMAs (three after each of the first four), so their
                 // latency hides behind the wave's own matrix-core work.
-                constexpr int kReadsPerGroup = 3;
-                constexpr int kGroups = 2 * (FM + FN) / kReadsPerGroup;
-                static_assert(kGroups * kReadsPerGroup == 2 * (FM + FN) && kGroups <= FM * FN,
-                              "fragment reads must spread over whole MFMA groups");
+                constexpr int kReads = 2 * (FM + FN), kPer = 3;
+                constexpr int kGroups = (kReads + kPer - 1) / kPer;
+                static_assert(kGroups <= FM * FN, "more read groups than MFMAs");
 #pragma unroll
-                for (int g = 0; g < kGroups; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerGroup, 0);  // LDS reads
+                for (int g = 0; g + 1 < kGroups; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // LDS reads
                 }
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, kReads - (kGroups - 1) * kPer, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - kGroups, 0);
                 // The slot of stage kt is free once every wave has passed the
                 // barrier; its refill goes out after this step's MFMAs.
