@@ -253,8 +253,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328023.6, "fetch_scale": 2.0, "write_kib": 361853.3,
-                  "write_scale": 1.0, "sources_sha256": "2ccafc9270e318c4bee88697b39a94c3f8a9cab2d90f0a85a1d82a458911730f"},
+    "i4i4_8192": {"fetch_kib": 328130.8, "fetch_scale": 2.0, "write_kib": 363642.4,
+                  "write_scale": 1.0, "sources_sha256": "22d8b4c6ed0dd22753b106af2a3f081e0c62340b9b4d39b0614dc5d557136da5"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",
