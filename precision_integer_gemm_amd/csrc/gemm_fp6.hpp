@@ -48,6 +48,7 @@ typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x6 __attribute__((ext_vector_type(6)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x32 __attribute__((ext_vector_type(32)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFp6FragBytes = 1536;  // 64 lanes x 32 six-bit codes
 constexpr int kFp6MfmaFormat = 3;    // E3M2 operand format of the f8f6f4 MFMA
@@ -134,7 +135,10 @@ struct Fp6Cfg {
     static constexpr int A_BYTES = (BM / 32) * SPAN;
     static constexpr int B_BYTES = (BN / 32) * SPAN;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    // Two slots for a tile's scale vectors (scaled outputs): BM + BN floats,
+    // rounded up to whole 64-float DMA instructions.
+    static constexpr int SCALE_SLOT = 4 * ((BM + BN + 63) / 64 * 64);
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + 2 * SCALE_SLOT;
     static constexpr int NA = A_BYTES / 1024 / kWaves;  // DMA instructions per wave per stage
     static constexpr int NB = B_BYTES / 1024 / kWaves;
     static_assert(NA * 1024 * kWaves == A_BYTES && NB * 1024 * kWaves == B_BYTES,
@@ -206,8 +210,13 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_fp6
     tile_origin(v, m0, n0);
     // Buffer resources start at the tile's first row block, so offsets stay
     // below 2^31; row blocks past the matrix lie beyond the range: zeros.
-    i32x4 rsrc_a, rsrc_b;
+    constexpr bool kScaled = OUT != OUT_I32;
+    i32x4 rsrc_a, rsrc_b, rsrc_sa, rsrc_sb;
     auto set_rsrc = [&]() {
+        if constexpr (kScaled) {
+            rsrc_sa = make_rsrc(epi.scale_a + m0, (uint32_t)min(Cfg::BM, M - m0) * 4u);
+            rsrc_sb = make_rsrc(epi.scale_b + n0, (uint32_t)min(Cfg::BN, N - n0) * 4u);
+        }
         const int rba = m0 / 32, rbb = n0 / 32;
         rsrc_a = make_rsrc(A6 + (int64_t)rba * K64 * kFp6FragBytes,
                            (uint32_t)min(Cfg::BM / 32, RBA - rba) * (uint32_t)K64 * kFp6FragBytes);
@@ -279,6 +288,24 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_fp6
             wait_vmcnt<0>();
     };
 
+    // Scaled outputs: a tile's scale vectors go into LDS slot p with the
+    // tile's first copies, element e = 64 wave + lane being scale_a[m0 + e]
+    // for e < BM, then scale_b[n0 + e - BM] (zeros past M and N).  The
+    // epilogue then reads them from LDS, so no global load of its own has to
+    // be waited for behind the next tile's copies.
+    const uint32_t lds_scales = lds0 + (uint32_t)(STAGES * Cfg::STAGE_BYTES);
+    int par = 0;  // slot of the current tile's scales
+    auto issue_scales = [&](int p) {
+        if constexpr (kScaled) {
+            static_assert(Cfg::BM % 64 == 0, "a scale DMA instruction must not straddle the two vectors");
+            for (int e0 = wave * 64; e0 < Cfg::BM + Cfg::BN; e0 += 64 * Cfg::kWaves) {  // wave-uniform
+                const bool isb = e0 >= Cfg::BM;
+                const uint32_t off = (uint32_t)((isb ? e0 - Cfg::BM : e0) + lane) * 4u;
+                dma4(isb ? rsrc_sb : rsrc_sa, off, lds_scales + (uint32_t)(p * Cfg::SCALE_SLOT + e0 * 4));
+            }
+        }
+    };
+    issue_scales(0);
 #pragma unroll
     for (int s = 0; s < kPrologue; ++s) issue_stage(s);
     bool stores_pending = false;
@@ -341,19 +368,34 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_fp6
         wait_vmcnt<0>();
 
         const int tm0 = m0, tn0 = n0;
+        const int tpar = par;
         const int vn = v + (int)gridDim.x;
         auto store_tile = [&]() {
             float sa[FM], sb[FN][4][4];
+            if constexpr (kScaled) {
+                const float *ss =
+                    reinterpret_cast<const float *>(smem + STAGES * Cfg::STAGE_BYTES + tpar * Cfg::SCALE_SLOT);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = tm0 + (wm * FM + fm) * 32 + r32;
-                sa[fm] = m < M ? load_scale_a<OUT>(epi, m) : 0.f;
+                for (int fm = 0; fm < FM; ++fm) sa[fm] = ss[(wm * FM + fm) * 32 + r32];
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const f32x4 q = *reinterpret_cast<const f32x4 *>(
+                            ss + Cfg::BM + (wn * FN + fn) * 32 + 8 * rg + 4 * h);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sb[fn][rg][i] = q[i];
+                    }
+            } else {
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) sa[fm] = 0.f;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sb[fn][rg][i] = 0.f;
             }
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg)
-                    load_scale_b4<OUT>(epi, N, tn0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h, sb[fn][rg]);
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -375,19 +417,19 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8) ? 2 : 1) void gemm_fp6
             if (vn < nblocks) {
                 tile_origin(vn, m0, n0);
                 set_rsrc();
+                issue_scales(par ^ 1);
 #pragma unroll
                 for (int s = 0; s < kPrologue; ++s) issue_stage(s);
             }
         };
-        if constexpr (OUT == OUT_I32) {
-            start_next();
-            store_tile();
-        } else {
-            store_tile();
-            start_next();
-        }
+        // The next tile's copies go out before this tile's stores (one store
+        // instruction per row segment of a whole tile, in every format), so
+        // the next tile's first wait does not also wait for the stores.
+        start_next();
+        store_tile();
         if (vn >= nblocks) break;
-        stores_pending = OUT == OUT_I32 && (N % 4) == 0 && tm0 + Cfg::BM <= M && tn0 + Cfg::BN <= N;
+        par ^= 1;
+        stores_pending = (N % 4) == 0 && tm0 + Cfg::BM <= M && tn0 + Cfg::BN <= N;
         v = vn;
     }
 }

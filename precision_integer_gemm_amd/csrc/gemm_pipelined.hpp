@@ -77,7 +77,11 @@ struct PipeCfg {
     static constexpr int A_BYTES = BM * RA;
     static constexpr int B_BYTES = BN * RB;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    // Without block scales: two slots for a tile's per-row / per-column
+    // scale vectors (scaled outputs), BM + BN floats rounded up to whole
+    // 64-float DMA instructions.
+    static constexpr int CHAN_SLOT = 4 * ((BM + BN + 63) / 64 * 64);
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + (SBP == 0 ? 2 * CHAN_SLOT : 0);
     static constexpr int NA = A_BYTES / 1024 / kWaves;  // DMA instructions per wave per stage
     static constexpr int NB = B_BYTES / 1024 / kWaves;
     static constexpr int SHIFT = (VAR == I4I4) ? 8 : 4;
@@ -217,6 +221,8 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
     int v = (int)blockIdx.x - chunk * nblocks;
     int m0, n0;
     tile_origin(v, m0, n0);
+    // Per-row / per-column scales of a scaled integer output (one K block).
+    constexpr bool kChan = OUT != OUT_I32 && SBP == 0 && !is_fp8(VAR);
     i32x4 rsrc_a, rsrc_b, rsrc_sa, rsrc_sb;
     auto set_rsrc = [&]() {
         rsrc_a = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)min(Cfg::BM, M - m0) * lda);
@@ -224,6 +230,9 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
         if constexpr (SBP > 0) {
             rsrc_sa = make_rsrc(epi.scale_a + (int64_t)m0 * nb, (uint32_t)min(Cfg::BM, M - m0) * nb * 4u);
             rsrc_sb = make_rsrc(epi.scale_b + (int64_t)n0 * nb, (uint32_t)min(Cfg::BN, N - n0) * nb * 4u);
+        } else if constexpr (kChan) {
+            rsrc_sa = make_rsrc(epi.scale_a + m0, (uint32_t)min(Cfg::BM, M - m0) * 4u);
+            rsrc_sb = make_rsrc(epi.scale_b + n0, (uint32_t)min(Cfg::BN, N - n0) * 4u);
         }
     };
     set_rsrc();
@@ -527,6 +536,24 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
     // Stages 0 .. kPrologue-1 of the first tile.  Slots past the last K tile
     // are filled too (with zeros: every offset is out of range), which keeps
     // the number of loads in flight the same in every iteration.
+    // Scaled outputs: a tile's scale vectors go into LDS slot p with the
+    // tile's first copies, element e = 64 wave + lane being scale_a[m0 + e]
+    // for e < BM, then scale_b[n0 + e - BM] (zeros past M and N).  The
+    // epilogue reads them from LDS, so no global load of its own has to be
+    // waited for behind the next tile's copies.
+    const uint32_t lds_chan = lds0 + (uint32_t)(STAGES * Cfg::STAGE_BYTES);
+    int par = 0;  // slot of the current tile's scales
+    auto issue_scales = [&](int p) {
+        if constexpr (kChan) {
+            static_assert(Cfg::BM % 64 == 0, "a scale DMA instruction must not straddle the two vectors");
+            for (int e0 = wave * 64; e0 < Cfg::BM + Cfg::BN; e0 += 64 * Cfg::kWaves) {  // wave-uniform
+                const bool isb = e0 >= Cfg::BM;
+                const uint32_t off = (uint32_t)((isb ? e0 - Cfg::BM : e0) + lane) * 4u;
+                dma4(isb ? rsrc_sb : rsrc_sa, off, lds_chan + (uint32_t)(p * Cfg::CHAN_SLOT + e0 * 4));
+            }
+        }
+    };
+    issue_scales(0);
 #pragma unroll
     for (int s = 0; s < kPrologue; ++s) issue_stage(s);
     bool stores_pending = false;  // a full tile's stores were issued after the prologue
@@ -589,6 +616,7 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
         wait_vmcnt<0>();  // the zero-fill loads past the end
 
         const int tm0 = m0, tn0 = n0;
+        const int tpar = par;
         const int vn = v + (int)gridDim.x;
         // Epilogue: lane holds C[m][n .. n+3] for m = l%32 of each column block.
         auto store_tile = [&]() {
@@ -609,19 +637,33 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
                     }
                 return;
             }
-            // Scales first (one per row block, four per column group), then
-            // the stores: the scale reads are not reordered behind stores to D.
+            // Scales from this tile's LDS slot (one per row block, four per
+            // column group).
             float sa[FM], sb[FN][4][4];
+            if constexpr (kChan) {
+                const float *ss =
+                    reinterpret_cast<const float *>(smem + STAGES * Cfg::STAGE_BYTES + tpar * Cfg::CHAN_SLOT);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = tm0 + (wm * FM + fm) * 32 + r32;
-                sa[fm] = m < M ? load_scale_a<OUT>(epi, m) : 0.f;
+                for (int fm = 0; fm < FM; ++fm) sa[fm] = ss[(wm * FM + fm) * 32 + r32];
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const f32x4 q = *reinterpret_cast<const f32x4 *>(
+                            ss + Cfg::BM + (wn * FN + fn) * 32 + 8 * rg + 4 * h);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sb[fn][rg][i] = q[i];
+                    }
+            } else {
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) sa[fm] = 0.f;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sb[fn][rg][i] = 0.f;
             }
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg)
-                    load_scale_b4<OUT>(epi, N, tn0 + (wn * FN + fn) * 32 + 8 * rg + 4 * h, sb[fn][rg]);
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -649,24 +691,19 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
             if (vn < nblocks) {
                 tile_origin(vn, m0, n0);
                 set_rsrc();
+                issue_scales(par ^ 1);
 #pragma unroll
                 for (int s = 0; s < kPrologue; ++s) issue_stage(s);
             }
         };
-        if constexpr (OUT == OUT_I32) {
-            // The next tile's loads go out before this tile's stores, so the
-            // next tile's first wait does not also wait for the stores.
-            start_next();
-            store_tile();
-        } else {
-            // The scaled epilogue reads scale vectors: stores first, so that
-            // the compiler's waits for those reads never wait on the next
-            // tile's loads.
-            store_tile();
-            start_next();
-        }
+        // The next tile's loads go out before this tile's stores (one store
+        // instruction per row segment of a whole tile, in every format), so
+        // the next tile's first wait does not also wait for the stores.
+        start_next();
+        store_tile();
         if (vn >= nblocks) break;
-        stores_pending = OUT == OUT_I32 && (N % 4) == 0 && tm0 + Cfg::BM <= M && tn0 + Cfg::BN <= N;
+        par ^= 1;
+        stores_pending = (N % 4) == 0 && tm0 + Cfg::BM <= M && tn0 + Cfg::BN <= N;
         v = vn;
     }
 }
