@@ -97,26 +97,6 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     const i32x4 rsrc_b = make_rsrc(B, (uint32_t)N * ldb);
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
-    // A fragments of this wave's K slice (zeros past the range and past M):
-    // the 32 k of lane group g as two 16-k MFMA operands, in k order.
-    i32x4 a_lo[KSTEPS], a_hi[KSTEPS];
-#pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-        const int kl = k_begin + 128 * j + 32 * g;
-        if constexpr (VAR == I4I4) {
-            const uint32_t off = kl < klen && r16 < mrows
-                                     ? (uint32_t)(m0 + r16) * lda + (uint32_t)(k0 + kl) / 2
-                                     : kOutOfRange;
-            unpack_chunk<true>(buffer_load16(rsrc_a, off), a_lo[j], a_hi[j]);
-        } else {
-            const uint32_t off = kl < klen && r16 < mrows
-                                     ? (uint32_t)(m0 + r16) * lda + (uint32_t)(k0 + kl)
-                                     : kOutOfRange;
-            a_lo[j] = buffer_load16(rsrc_a, off);
-            a_hi[j] = buffer_load16(rsrc_a, off == kOutOfRange ? kOutOfRange : off + 16);
-        }
-    }
-
     // DMA of strip s into buffer b: this wave's instructions are KSTEPS
     // consecutive 1 KB pieces of the buffer; lane l of piece j fetches the
     // global chunk stored at buffer position q = 64 j + l.
@@ -149,6 +129,31 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     int s = (int)blockIdx.x - set * G;
     if (s >= strips) return;
     issue_strip(s, 0);
+
+    // A fragments of this wave's K slice (zeros past the range and past M):
+    // the 32 k of lane group g as two 16-k MFMA operands, in k order.  They
+    // are loaded after the first strip's copies, so the first wait below can
+    // leave them in flight: every compute unit reads all of A at once, and
+    // the second strip's copies should not wait for that.  kALoads counts
+    // these loads (one per step for packed A, two for int8 A).
+    i32x4 a_lo[KSTEPS], a_hi[KSTEPS];
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) {
+        const int kl = k_begin + 128 * j + 32 * g;
+        if constexpr (VAR == I4I4) {
+            const uint32_t off = kl < klen && r16 < mrows
+                                     ? (uint32_t)(m0 + r16) * lda + (uint32_t)(k0 + kl) / 2
+                                     : kOutOfRange;
+            unpack_chunk<true>(buffer_load16(rsrc_a, off), a_lo[j], a_hi[j]);
+        } else {
+            const uint32_t off = kl < klen && r16 < mrows
+                                     ? (uint32_t)(m0 + r16) * lda + (uint32_t)(k0 + kl)
+                                     : kOutOfRange;
+            a_lo[j] = buffer_load16(rsrc_a, off);
+            a_hi[j] = buffer_load16(rsrc_a, off == kOutOfRange ? kOutOfRange : off + 16);
+        }
+    }
+    constexpr int kALoads = VAR == I4I4 ? KSTEPS : 2 * KSTEPS;
     int it = 0;
     int prev = -1;  // strip whose partial tiles await reduction
     // Scales of the strip this wave will reduce next, read one iteration
@@ -183,7 +188,10 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     };
     for (;;) {
         const int b = it & 1;
-        wait_vmcnt<0>();
+        if (it == 0)
+            wait_vmcnt<kALoads>();  // this wave's copies of strip s (A's loads are younger)
+        else
+            wait_vmcnt<0>();
         lds_barrier();  // strip s is in buffer b; partial tiles of `prev` are in red[b ^ 1]
 
         // Reduce and store the previous strip (one wave, rotating).
