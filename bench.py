@@ -148,6 +148,11 @@ SWEEP_DMA = [(1, 1024, f, pol) for f in (2, 4, 8) for pol in (0, 2)] + \
             [(2, 512, f, pol) for f in (4, 8) for pol in (0, 2)] + \
             [(4, 256, f, pol) for f in (4, 8, 16) for pol in (0, 2)] + \
             [(8, 256, f, 2) for f in (4, 8)]
+# The narrow-M GEMM's own copy pattern without its arithmetic: 64 KB strips
+# per workgroup, wave w copying row w as four 1 KB `nt` pieces; in flight 0 =
+# one strip per workgroup with a barrier per strip (the GEMM's schedule), else
+# that many pieces per wave with no barrier.
+SWEEP_STRIP = [(1, 1024, f, 2) for f in (0, 4, 8)]
 
 
 def stream_sweep(torch, dev, stream, nbytes: int) -> dict:
@@ -164,7 +169,7 @@ def stream_sweep(torch, dev, stream, nbytes: int) -> dict:
     n_out = 32 * cus * 1024
     out = torch.empty(n_out, dtype=torch.int32, device=dev)
     rows = []
-    for mode, table in ((0, SWEEP_BUF), (1, SWEEP_DMA)):
+    for mode, table in ((0, SWEEP_BUF), (1, SWEEP_DMA), (2, SWEEP_STRIP)):
         for wpc, threads, inflight, pol in table:
             us = []
             for r in range(STREAM_REPS + STREAM_COPIES):
@@ -180,7 +185,7 @@ def stream_sweep(torch, dev, stream, nbytes: int) -> dict:
                 if r >= STREAM_COPIES:
                     us.append(e0.elapsed_time(e1) * 1e3)
             med = float(np.median(us))
-            rows.append({"loads": "buffer" if mode == 0 else "to_lds", "wg_per_cu": wpc,
+            rows.append({"loads": ("buffer", "to_lds", "strips")[mode], "wg_per_cu": wpc,
                          "threads": threads, "in_flight": inflight,
                          "policy": {0: "-", 1: "sc0", 2: "nt", 16: "sc1", 18: "sc1 nt"}[pol],
                          "median_us": round(med, 2), "min_us": round(float(np.min(us)), 2),

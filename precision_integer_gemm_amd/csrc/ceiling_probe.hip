@@ -243,6 +243,38 @@ __global__ void stream_dma(i32x4 rsrc, int64_t pieces, int32_t *out)
     if (lane == 0) out[(int64_t)blockIdx.x * waves + wave] = slot;
 }
 
+// Direct-to-LDS pass in the narrow-M GEMM's own pattern: the buffer is taken
+// as 64 KB strips (16 rows of 4 KB), workgroup b copying strips b, b + G, ...
+// (G = grid size) and wave w of its 16 copying row w as four 1 KB `nt`
+// pieces.  F = 0: one strip per workgroup in flight -- issue its pieces, wait
+// for them, barrier, next strip (the GEMM's schedule without its arithmetic);
+// F > 0: F pieces in flight per wave, no barrier.  The data is not read back.
+template <int F>
+__global__ __launch_bounds__(1024) void stream_strips(i32x4 rsrc, int64_t strips, int32_t *out)
+{
+    extern __shared__ __align__(1024) uint8_t lds[];
+    constexpr int kSlots = F == 0 ? 4 : F;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t ring = (uint32_t)reinterpret_cast<uintptr_t>(lds) + (uint32_t)(wave * kSlots) * 1024u;
+    int slot = 0;
+    for (int64_t s = blockIdx.x; s < strips; s += gridDim.x) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            lpgemm::dma16_nt(rsrc, (uint32_t)(s * 65536) + (uint32_t)(wave * 4096 + t * 1024 + 16 * lane),
+                             ring + (uint32_t)slot * 1024u);
+            slot = slot + 1 == kSlots ? 0 : slot + 1;
+            if constexpr (F > 0) lpgemm::wait_vmcnt<F - 1>();
+        }
+        if constexpr (F == 0) {
+            lpgemm::wait_vmcnt<0>();
+            lpgemm::lds_barrier();
+        }
+    }
+    lpgemm::wait_vmcnt<0>();
+    if (lane == 0) out[(int64_t)blockIdx.x * 16 + wave] = slot;
+}
+
 }  // namespace
 
 // Work of one launch: operations (kinds 0-2, 4) or LDS bytes read (kind 3).
@@ -316,7 +348,11 @@ extern "C" int ceiling_probe_wall_clock_khz(void)
 //           18 (sc1 nt)};
 //   mode 1  direct-to-LDS: `blocks` x `threads` threads, `inflight` in {2, 4,
 //           8, 16} 1 KB pieces per wave, `policy` 0 or 2 (nt); each workgroup
-//           holds threads / 64 * inflight KB of LDS (at most 160 KB).
+//           holds threads / 64 * inflight KB of LDS (at most 160 KB);
+//   mode 2  direct-to-LDS in 64 KB strips (the narrow-M GEMM's pattern):
+//           1024 threads, `inflight` 0 (one strip per workgroup, barrier per
+//           strip), 4 or 8 pieces per wave, `policy` 2 (nt); `bytes` a
+//           multiple of 64 KB.
 // `out` holds at least blocks * threads ints.  Returns 0, -1 for arguments
 // outside these sets, -2 if the launch failed.
 extern "C" int ceiling_probe_stream_sweep(const void *buf, int64_t bytes, int mode, int blocks,
@@ -350,6 +386,13 @@ extern "C" int ceiling_probe_stream_sweep(const void *buf, int64_t bytes, int mo
         fn = LPG_DMA(2, false) : LPG_DMA(4, false) : LPG_DMA(8, false) : LPG_DMA(16, false)
            : LPG_DMA(2, true) : LPG_DMA(4, true) : LPG_DMA(8, true) : LPG_DMA(16, true) : nullptr;
 #undef LPG_DMA
+    } else if (mode == 2) {
+        if (threads != 1024 || policy != 2 || (bytes & 65535)) return -1;
+        n = bytes / 65536;
+        lds = 16 * (inflight == 0 ? 4 : inflight) * 1024;
+        fn = inflight == 0 ? (const void *)stream_strips<0>
+           : inflight == 4 ? (const void *)stream_strips<4>
+           : inflight == 8 ? (const void *)stream_strips<8> : nullptr;
     }
     if (fn == nullptr) return -1;
     if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
