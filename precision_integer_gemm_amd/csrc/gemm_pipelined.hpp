@@ -732,10 +732,72 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
                 for (int s = 0; s < kPrologue; ++s) issue_stage(s);
             }
         };
+        // The workgroup's last tile: no copies follow, so the stage ring is
+        // free and C goes out through it as whole rows, one 1 KB row piece
+        // per wave instruction (the MFMA layout stores 32-byte pieces of 32
+        // rows per instruction, which HBM absorbs more slowly).  Passes of
+        // kRows rows: the waves holding a pass's 32-row blocks write them
+        // (shifted integers, padded rows), then every wave stores rows of it.
+        constexpr bool kStageC = Cfg::BN == 256 && SBP == 0 && !is_fp8(VAR);
+        auto store_tile_staged = [&]() {
+          if constexpr (kStageC) {
+            // Lane indices taken afresh here (an opaque copy of the thread
+            // id), so that no address of this path is computed before the
+            // K loop and kept live through it.
+            int tid = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            const int sl = tid & 63, sr32 = sl & 31, sh = sl >> 5;
+            constexpr int kPitch = Cfg::BN * 4 + 16;
+            constexpr int kRows = ((STAGES * Cfg::STAGE_BYTES / kPitch) / 32 * 32) < Cfg::BM
+                                      ? (STAGES * Cfg::STAGE_BYTES / kPitch) / 32 * 32
+                                      : Cfg::BM;
+            static_assert(kRows >= 32, "the stage ring holds fewer than 32 staged rows");
+            const float *ss =
+                reinterpret_cast<const float *>(smem + STAGES * Cfg::STAGE_BYTES + tpar * Cfg::CHAN_SLOT);
+            float sb4[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (kChan) {
+                const f32x4 q = *reinterpret_cast<const f32x4 *>(ss + Cfg::BM + 4 * sl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sb4[i] = q[i];
+            }
+#pragma unroll
+            for (int p0 = 0; p0 < Cfg::BM; p0 += kRows) {
+                if (p0 > 0) lds_barrier();  // the previous pass's rows have been read
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int rb = (wm * FM + fm) * 32;  // first tile row of the block
+                    if (rb < p0 || rb >= p0 + kRows) continue;
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int rg = 0; rg < 4; ++rg) {
+                            const int col = (wn * FN + fn) * 32 + 8 * rg + 4 * sh;
+                            const i32x4 c = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
+                                                  acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
+                                            Cfg::SHIFT;
+                            *reinterpret_cast<i32x4 *>(smem + (rb - p0 + sr32) * kPitch + 4 * col) = c;
+                        }
+                }
+                lds_barrier();
+                for (int r = p0 + wave; r < p0 + kRows && r < Cfg::BM; r += Cfg::kWaves) {
+                    const int m = tm0 + r;
+                    if (m >= M) break;
+                    const i32x4 c = *reinterpret_cast<const i32x4 *>(smem + (r - p0) * kPitch + 16 * sl);
+                    store_row4<OUT>(epo, m, N, tn0 + 4 * sl, c, kChan ? ss[r] : 0.f, sb4);
+                }
+            }
+          }
+        };
         // The next tile's loads go out before this tile's stores (one store
         // instruction per row segment of a whole tile, in every format), so
         // the next tile's first wait does not also wait for the stores.
         start_next();
+        if constexpr (kStageC) {
+            if (vn >= nblocks) {
+                store_tile_staged();
+                break;
+            }
+        }
         store_tile();
         if (vn >= nblocks) break;
         par ^= 1;
