@@ -195,6 +195,53 @@ def stream_sweep(torch, dev, stream, nbytes: int) -> dict:
     return {"bytes": nbytes, "configs": len(rows), "best": best, "rows": rows}
 
 
+# C-store patterns (`ceiling_probe_store`): 256 workgroups per 64 MB of int32
+# C, each writing one 256 x 256 tile in the tiled GEMMs' MFMA layout (32 bytes
+# of 32 rows per instruction), as whole 1 KB rows, or staged through LDS as
+# the GEMMs' last tile is; four rotated output buffers.
+STORE_SHAPES = [(4096, 4096), (3072, 5120), (8192, 8192)]
+STORE_PATTERNS = {0: "mfma_layout", 1: "whole_rows", 2: "lds_staged"}
+
+
+def store_probe(torch, dev, stream) -> dict:
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "precision_integer_gemm_amd", "_ceiling.so"))
+    lib.ceiling_probe_store.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]
+    lib.ceiling_probe_store.restype = ctypes.c_int
+    out = []
+    for M, N in STORE_SHAPES:
+        bufs = [torch.empty((M, N), dtype=torch.int32, device=dev) for _ in range(4)]
+        for p in STORE_PATTERNS:  # each pattern writes {m, n, 0, 0} at (m, n .. n + 3)
+            bufs[0].fill_(-1)
+            if lib.ceiling_probe_store(p, bufs[0].data_ptr(), M, N, stream.cuda_stream) != 0:
+                raise RuntimeError(f"store probe {p} {M}x{N} failed")
+            v = bufs[0].view(M, N // 4, 4)
+            ok = bool((v[:, :, 0] == torch.arange(M, device=dev).view(M, 1)).all()) and \
+                bool((v[:, :, 1] == torch.arange(0, N, 4, device=dev).view(1, N // 4)).all())
+            if not ok:
+                raise RuntimeError(f"store probe {p} {M}x{N} wrote a wrong element")
+        us = {name: [] for name in STORE_PATTERNS.values()}
+        n = 0
+        for r in range(STREAM_REPS + 3):
+            for p, name in STORE_PATTERNS.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                lib.ceiling_probe_store(p, bufs[n % 4].data_ptr(), M, N, stream.cuda_stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                n += 1
+                if r >= 3:
+                    us[name].append(e0.elapsed_time(e1) * 1e3)
+        med = {k: round(float(np.median(v)), 2) for k, v in us.items()}
+        out.append({"M": M, "N": N, "bytes": M * N * 4, "median_us": med,
+                    "tb_s": {k: round(M * N * 4 / (v * 1e-6) / 1e12, 2) for k, v in med.items()}})
+        print(json.dumps(out[-1]), file=sys.stderr, flush=True)
+        del bufs
+    return {"store_patterns": out}
+
+
 def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0) -> dict:
     import ctypes
 
@@ -304,6 +351,8 @@ def parse():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the sustained-ceiling probes")
     ap.add_argument("--stream-sweep", action="store_true",
                     help="only sweep the streaming-read probe over the decode weights' size")
+    ap.add_argument("--store-probe", action="store_true",
+                    help="only time the C-store pattern probes (MFMA layout, whole rows, staged)")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="summarise a rocprofv3 kernel_trace.csv per kernel and grid (no GPU use)")
     return ap.parse_args()
@@ -388,6 +437,9 @@ def main() -> int:
     if args.stream_sweep:
         print(json.dumps({"stream_sweep": stream_sweep(torch, dev, torch.cuda.current_stream(),
                                                        stream_bytes)}))
+        return 0
+    if args.store_probe:
+        print(json.dumps(store_probe(torch, dev, torch.cuda.current_stream())))
         return 0
 
     names = [n for n in STEP_ORDER if args.case is None or n in args.case]

@@ -275,7 +275,77 @@ __global__ __launch_bounds__(1024) void stream_strips(i32x4 rsrc, int64_t strips
     if (lane == 0) out[(int64_t)blockIdx.x * 16 + wave] = slot;
 }
 
+// C-store patterns: one 256 x 256 int32 tile per 512-thread workgroup of an
+// M x N row-major matrix (M, N multiples of 256), tile t at tile row t / (N / 256).
+//   P = 0: the tiled GEMMs' MFMA layout: wave w (wm = w / 4, wn = w % 4) holds
+//          4 x 2 blocks of 32 x 32; each instruction writes 16 bytes at row
+//          (wm 4 + fm) 32 + lane % 32, column (wn 2 + fn) 32 + 8 rg + 4 (lane / 32),
+//          i.e. 32 bytes of each of 32 rows;
+//   P = 1: whole rows: wave w writes rows w, w + 8, ..., one 1 KB row per instruction;
+//   P = 2: P = 0's registers written into LDS in two passes of 128 rows (rows
+//          padded by 16 bytes), each followed by P = 1's stores of those rows
+//          (the GEMMs' last-tile epilogue).
+// Element (m, n .. n + 3) holds {m, n, 0, 0} in every pattern.
+template <int P>
+__global__ __launch_bounds__(512) void store_pattern(int32_t *C, int N)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    constexpr int kPitch = 1024 + 16;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / 4, wn = w % 4, r32 = lane & 31, h = lane >> 5;
+    const int tiles_n = N / 256;
+    const int tm0 = ((int)blockIdx.x / tiles_n) * 256, tn0 = ((int)blockIdx.x % tiles_n) * 256;
+    if constexpr (P == 1) {
+        for (int r = w; r < 256; r += 8)
+            *reinterpret_cast<i32x4 *>(C + (int64_t)(tm0 + r) * N + tn0 + 4 * lane) = i32x4{tm0 + r, tn0 + 4 * lane, 0, 0};
+    } else {
+        for (int half = 0; half < (P == 2 ? 2 : 1); ++half) {
+            if (P == 2 && half) __syncthreads();
+            for (int fn = 0; fn < 2; ++fn)
+                for (int fm = 0; fm < 4; ++fm) {
+                    const int rt = (wm * 4 + fm) * 32 + r32;  // row in the tile
+                    if (P == 2 && rt / 128 != half) continue;
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int nt = (wn * 2 + fn) * 32 + 8 * rg + 4 * h;
+                        const i32x4 v = i32x4{tm0 + rt, tn0 + nt, 0, 0};
+                        if constexpr (P == 0)
+                            *reinterpret_cast<i32x4 *>(C + (int64_t)(tm0 + rt) * N + tn0 + nt) = v;
+                        else
+                            *reinterpret_cast<i32x4 *>(lds + (rt - 128 * half) * kPitch + 4 * nt) = v;
+                    }
+                }
+            if constexpr (P == 2) {
+                __syncthreads();
+                for (int r = w; r < 128; r += 8)
+                    *reinterpret_cast<i32x4 *>(C + (int64_t)(tm0 + 128 * half + r) * N + tn0 + 4 * lane) =
+                        *reinterpret_cast<const i32x4 *>(lds + r * kPitch + 16 * lane);
+            }
+        }
+    }
+}
+
 }  // namespace
+
+// One launch of C-store pattern `pattern` (0, 1, 2: see store_pattern) over
+// the M x N int32 matrix C (device, M and N positive multiples of 256).
+// Returns 0, -1 for bad arguments, -2 if the launch failed.
+extern "C" int ceiling_probe_store(int pattern, int32_t *C, int M, int N, hipStream_t stream)
+{
+    if (C == nullptr || M <= 0 || N <= 0 || M % 256 || N % 256 || pattern < 0 || pattern > 2 ||
+        (int64_t)M * N > (int64_t(1) << 31))
+        return -1;
+    const void *fn = pattern == 0 ? (const void *)store_pattern<0>
+                     : pattern == 1 ? (const void *)store_pattern<1>
+                                    : (const void *)store_pattern<2>;
+    const int lds = pattern == 2 ? 128 * (1024 + 16) : 0;
+    if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+        return -2;
+    int n = N;
+    void *args[] = {&C, &n};
+    if (hipLaunchKernel(fn, dim3((unsigned)((M / 256) * (N / 256))), dim3(512), args, lds, stream) != hipSuccess)
+        return -2;
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
 
 // Work of one launch: operations (kinds 0-2, 4) or LDS bytes read (kind 3).
 extern "C" double ceiling_probe_work(int kind, int blocks, int iters)
