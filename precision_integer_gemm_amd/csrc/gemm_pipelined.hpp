@@ -737,8 +737,9 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
         // per wave instruction (the MFMA layout stores 32-byte pieces of 32
         // rows per instruction, which HBM absorbs more slowly).  Passes of
         // kRows rows: the waves holding a pass's 32-row blocks write them
-        // (shifted integers, padded rows), then every wave stores rows of it.
-        constexpr bool kStageC = Cfg::BN == 256 && SBP == 0 && !is_fp8(VAR);
+        // (shifted integers, or binary32 bits for fp8 operands; padded rows),
+        // then every wave stores rows of it.
+        constexpr bool kStageC = Cfg::BN == 256 && SBP == 0;
         auto store_tile_staged = [&]() {
           if constexpr (kStageC) {
             // Lane indices taken afresh here (an opaque copy of the thread
@@ -772,9 +773,15 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
 #pragma unroll
                         for (int rg = 0; rg < 4; ++rg) {
                             const int col = (wn * FN + fn) * 32 + 8 * rg + 4 * sh;
-                            const i32x4 c = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
-                                                  acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
-                                            Cfg::SHIFT;
+                            i32x4 c;
+                            if constexpr (is_fp8(VAR)) {  // binary32 results, staged as their bits
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) c[i] = __float_as_int(acc[fn][fm][4 * rg + i]);
+                            } else {
+                                c = i32x4{acc[fn][fm][4 * rg + 0], acc[fn][fm][4 * rg + 1],
+                                          acc[fn][fm][4 * rg + 2], acc[fn][fm][4 * rg + 3]} >>
+                                    Cfg::SHIFT;
+                            }
                             *reinterpret_cast<i32x4 *>(smem + (rb - p0 + sr32) * kPitch + 4 * col) = c;
                         }
                 }
@@ -783,7 +790,13 @@ __global__ __launch_bounds__(64 * WM * WN, (FM * FN <= 8 && (SBP == 0 || WM * WN
                     const int m = tm0 + r;
                     if (m >= M) break;
                     const i32x4 c = *reinterpret_cast<const i32x4 *>(smem + (r - p0) * kPitch + 16 * sl);
-                    store_row4<OUT>(epo, m, N, tn0 + 4 * sl, c, kChan ? ss[r] : 0.f, sb4);
+                    if constexpr (is_fp8(VAR)) {
+                        const float cf[4] = {__int_as_float(c[0]), __int_as_float(c[1]), __int_as_float(c[2]),
+                                             __int_as_float(c[3])};
+                        store_row4f<OUT>(epo, m, N, tn0 + 4 * sl, cf);
+                    } else {
+                        store_row4<OUT>(epo, m, N, tn0 + 4 * sl, c, kChan ? ss[r] : 0.f, sb4);
+                    }
                 }
             }
           }
