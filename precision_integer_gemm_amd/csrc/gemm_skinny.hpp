@@ -59,13 +59,14 @@ struct SkinnyCfg {
     static_assert(kLdsBytes <= 160 * 1024, "strip buffers exceed the LDS");
 };
 
-template <int VAR, int KW, int KSTEPS, int OUT, bool SPLIT>
+template <int VAR, int KW, int KSTEPS, int OUT, bool SPLIT, bool WHOLE_A = false>
 __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, Epilogue epi, int M, int N, int K,
     int kc)
 {
     static_assert(!SPLIT || OUT == OUT_I32, "split K adds int32 partial sums");
     static_assert(VAR == W4A8 || VAR == I4I4, "4-bit B with an int8 or int4 A");
+    static_assert(!WHOLE_A || VAR == W4A8, "whole-line A loads: int8 A");
     // x16 pre-scale of each 4-bit operand, removed exactly at the end
     constexpr int kShift = VAR == I4I4 ? 8 : 4;
     using Cfg = SkinnyCfg<KW, KSTEPS>;
@@ -136,16 +137,36 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     // leave them in flight: every compute unit reads all of A at once, and
     // the second strip's copies should not wait for that.  kALoads counts
     // these loads (one per step for packed A, two for int8 A).
+    // int8 A with WHOLE_A (taken for more than 8 rows): a lane's two
+    // operands are bytes 32 g .. 32 g + 31 of a step's 128 for row r16.
+    // Loaded that way, consecutive lanes read different rows and every
+    // instruction uses half of each 128-byte line it touches; instead each
+    // step is loaded as two instructions of 8 rows x 128 bytes in which eight
+    // consecutive lanes read one whole line (lane l: row l / 8, plus 8 in the
+    // second, 16-byte chunk l % 8), the first wait also waits for A, and the
+    // operands are put in place by ds_bpermute once the second strip's copies
+    // are out.  With few rows the MFMA-layout loads stay, left in flight by
+    // the first wait.
     i32x4 a_lo[KSTEPS], a_hi[KSTEPS];
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
-        const int kl = k_begin + 128 * j + 32 * g;
         if constexpr (VAR == I4I4) {
+            const int kl = k_begin + 128 * j + 32 * g;
             const uint32_t off = kl < klen && r16 < mrows
                                      ? (uint32_t)(m0 + r16) * lda + (uint32_t)(k0 + kl) / 2
                                      : kOutOfRange;
             unpack_chunk<true>(buffer_load16(rsrc_a, off), a_lo[j], a_hi[j]);
+        } else if constexpr (WHOLE_A) {
+            const int kl = k_begin + 128 * j + 16 * (lane & 7);  // this lane's 16 bytes of the step
+            const int row0 = lane >> 3, row1 = 8 + (lane >> 3);
+            a_lo[j] = buffer_load16(rsrc_a, kl < klen && row0 < mrows
+                                                ? (uint32_t)(m0 + row0) * lda + (uint32_t)(k0 + kl)
+                                                : kOutOfRange);
+            a_hi[j] = buffer_load16(rsrc_a, kl < klen && row1 < mrows
+                                                ? (uint32_t)(m0 + row1) * lda + (uint32_t)(k0 + kl)
+                                                : kOutOfRange);
         } else {
+            const int kl = k_begin + 128 * j + 32 * g;
             const uint32_t off = kl < klen && r16 < mrows
                                      ? (uint32_t)(m0 + r16) * lda + (uint32_t)(k0 + kl)
                                      : kOutOfRange;
@@ -154,6 +175,35 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
         }
     }
     constexpr int kALoads = VAR == I4I4 ? KSTEPS : 2 * KSTEPS;
+    // int8 A: from the whole-line layout (a_lo: rows 0-7, a_hi: rows 8-15)
+    // to the MFMA operands.  Even lanes of zlo keep a_lo (chunk 2 g' of rows
+    // 0-7), odd lanes take a_hi from the even neighbour (the same chunk of
+    // rows 8-15); zhi the other way round for the odd chunks; then one
+    // bpermute per dword: lane (r16, g) reads lane 8 (r16 % 8) + 2 g, plus
+    // 1 for the low operand of rows 8-15 or the high operand of rows 0-7.
+    auto place_a = [&]() {
+        if constexpr (WHOLE_A) {
+            const int up = r16 >> 3;
+            const int src_lo = 4 * (8 * (r16 & 7) + 2 * g + up);
+            const int src_hi = 4 * (8 * (r16 & 7) + 2 * g + 1 - up);
+            const bool odd = (lane & 1) != 0;
+            int v_lo[KSTEPS][4], v_hi[KSTEPS][4];
+#pragma unroll
+            for (int j = 0; j < KSTEPS; ++j)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    // quad_perm [1, 0, 3, 2]: each lane takes its neighbour's value
+                    const int sw = __builtin_amdgcn_mov_dpp(a_hi[j][d], 0xB1, 0xF, 0xF, false);
+                    v_lo[j][d] = __builtin_amdgcn_ds_bpermute(src_lo, odd ? sw : a_lo[j][d]);
+                    v_hi[j][d] = __builtin_amdgcn_ds_bpermute(src_hi, odd ? a_lo[j][d] : sw);
+                }
+#pragma unroll
+            for (int j = 0; j < KSTEPS; ++j) {
+                a_lo[j] = i32x4{v_lo[j][0], v_lo[j][1], v_lo[j][2], v_lo[j][3]};
+                a_hi[j] = i32x4{v_hi[j][0], v_hi[j][1], v_hi[j][2], v_hi[j][3]};
+            }
+        }
+    };
     int it = 0;
     int prev = -1;  // strip whose partial tiles await reduction
     // Scales of the strip this wave will reduce next, read one iteration
@@ -188,10 +238,14 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
     };
     for (;;) {
         const int b = it & 1;
-        if (it == 0)
-            wait_vmcnt<kALoads>();  // this wave's copies of strip s (A's loads are younger)
-        else
+        if (it == 0) {
+            if constexpr (WHOLE_A)
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): strip s and A, seen by the compiler
+            else
+                wait_vmcnt<kALoads>();  // this wave's copies of strip s (A's loads are younger)
+        } else {
             wait_vmcnt<0>();
+        }
         lds_barrier();  // strip s is in buffer b; partial tiles of `prev` are in red[b ^ 1]
 
         // Reduce and store the previous strip (one wave, rotating).
@@ -207,6 +261,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(
         // the barrier above).
         const int sn = s + G;
         if (sn < strips) issue_strip(sn, b ^ 1);
+        if (it == 0) place_a();  // waits for A, behind the second strip's copies
         if (OUT != OUT_I32 && wave == it % KW && r16 < mrows)
             load_scales<OUT>(epi, m0 + r16, N, s * 16 + 4 * g, pend_sa, pend_sb);
 

@@ -413,12 +413,12 @@ lpgemm_status launch_tiled(const Plan &p, const uint8_t *a, const uint8_t *b, Ep
 // Launch the narrow-M kernel for K ranges up to KSTEPS * 1024 (SPLIT: several
 // ranges added into C, which is zeroed first by a fill kernel); the first
 // launch on each device raises its dynamic-LDS limit to the two strip buffers.
-template <int VAR, int KSTEPS, int OUT, bool SPLIT>
+template <int VAR, int KSTEPS, int OUT, bool SPLIT, bool WHOLE_A = false>
 lpgemm_status launch_skinny(const Plan &p, const uint8_t *a, const uint8_t *b, Epilogue epi, int m,
                             int n, int k, hipStream_t stream)
 {
     using Cfg = SkinnyCfg<kSkinnyKW, KSTEPS>;
-    constexpr auto kernel = &gemm_skinny_kernel<VAR, kSkinnyKW, KSTEPS, OUT, SPLIT>;
+    constexpr auto kernel = &gemm_skinny_kernel<VAR, kSkinnyKW, KSTEPS, OUT, SPLIT, WHOLE_A>;
     static std::once_flag once[kMaxDevices];
     static hipError_t attr_err[kMaxDevices];
     int dev = 0;
@@ -467,6 +467,21 @@ lpgemm_status launch_skinny_steps(const Plan &p, const uint8_t *a, const uint8_t
 {
     if (p.k_chunks > 1 && p.k_steps != 4) return LPGEMM_ERR_INVALID_ARG;  // ranges > 4096 k
     if (p.k_chunks > 1 && p.k_seq) return launch_skinny_seq<VAR, OUT>(p, a, b, epi, m, n, k, stream);
+    // int8 A over more than 8 rows: whole-line A loads (gemm_skinny.hpp)
+    if constexpr (VAR == W4A8) {
+        if (m > 8) {
+            if constexpr (OUT == OUT_I32) {
+                if (p.k_chunks > 1) return launch_skinny<VAR, 4, OUT, true, true>(p, a, b, epi, m, n, k, stream);
+            } else {
+                if (p.k_chunks > 1) return LPGEMM_ERR_INVALID_ARG;
+            }
+            switch (p.k_steps) {
+            case 1: return launch_skinny<VAR, 1, OUT, false, true>(p, a, b, epi, m, n, k, stream);
+            case 2: return launch_skinny<VAR, 2, OUT, false, true>(p, a, b, epi, m, n, k, stream);
+            default: return launch_skinny<VAR, 4, OUT, false, true>(p, a, b, epi, m, n, k, stream);
+            }
+        }
+    }
     if constexpr (OUT == OUT_I32) {
         if (p.k_chunks > 1) return launch_skinny<VAR, 4, OUT, true>(p, a, b, epi, m, n, k, stream);
     } else {

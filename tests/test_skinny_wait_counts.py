@@ -3,7 +3,8 @@
 The kernel issues the first strip's direct-to-LDS copies, then A's loads, and
 its first `s_waitcnt vmcnt(n)` leaves n operations in flight: n must not
 exceed the number of vector-memory operations issued after the last copy, or
-the wait could pass before the strip has landed.  The loads are counted in
+the wait could pass before the strip has landed (the whole-line A instances
+wait for everything, n = 0).  The loads are counted in
 the source (one per step for packed int4 A, two for int8 A); this test builds
 every instance the library uses to assembly and counts them in the code the
 compiler actually emitted.
@@ -18,17 +19,21 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "precision_integer_gemm_amd", "csrc")
 
-INSTANCES = [(var, ks, out, False) for var in ("W4A8", "I4I4") for ks in (1, 2, 4)
+INSTANCES = [(var, ks, out, False, False) for var in ("W4A8", "I4I4") for ks in (1, 2, 4)
              for out in ("OUT_I32", "OUT_F32", "OUT_BF16", "OUT_F16")]
-INSTANCES += [(var, 4, "OUT_I32", True) for var in ("W4A8", "I4I4")]
+INSTANCES += [(var, 4, "OUT_I32", True, False) for var in ("W4A8", "I4I4")]
+# int8 A over more than 8 rows: whole-line A loads, whose first wait is vmcnt(0)
+INSTANCES += [("W4A8", ks, out, False, True) for ks in (1, 2, 4)
+              for out in ("OUT_I32", "OUT_F32", "OUT_BF16", "OUT_F16")]
+INSTANCES += [("W4A8", 4, "OUT_I32", True, True)]
 
 
 def _source():
     lines = ['#include "gemm_skinny.hpp"', "namespace lpgemm {"]
-    for var, ks, out, split in INSTANCES:
+    for var, ks, out, split, whole in INSTANCES:
         lines.append(f"template __global__ void gemm_skinny_kernel<{var}, 16, {ks}, {out}, "
-                     f"{'true' if split else 'false'}>(const uint8_t *, const uint8_t *, Epilogue, "
-                     "int, int, int, int);")
+                     f"{'true' if split else 'false'}, {'true' if whole else 'false'}>(const uint8_t *, "
+                     "const uint8_t *, Epilogue, int, int, int, int);")
     lines.append("}")
     return "\n".join(lines) + "\n"
 
