@@ -305,8 +305,8 @@ def sustained_ceilings(torch, dev, stream, reps: int = 3, stream_bytes: int = 0)
 # for 256 MiB written (x1.0).  Valid only for the kernel sources it was taken
 # on (their SHA-256 below); any change reports null until re-measured.
 TRAFFIC = {
-    "i4i4_8192": {"fetch_kib": 328116.8, "fetch_scale": 2.0, "write_kib": 363501.6,
-                  "write_scale": 1.0, "sources_sha256": "fad5a19b47a65c6448be7899db88ee9d3fa5ed900a44a812dc28b6363b80e622"},
+    "i4i4_8192": {"fetch_kib": 328192.5, "fetch_scale": 2.0, "write_kib": 360797.8,
+                  "write_scale": 1.0, "sources_sha256": "da139566518226640ac6925e97a82a29bde159baca7c6af30b721540fe476688"},
 }
 TRAFFIC_SOURCES = ["precision_integer_gemm_amd/csrc/gemm_pipelined.hpp",
                    "precision_integer_gemm_amd/csrc/gemm_fp6.hpp",
