@@ -407,8 +407,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the GEMM shards by N or M with no exchange, and this build runs and reports a "
-              "single GPU.", file=sys.stderr)
+              "the GEMM shards by N or M with no exchange, and the benchmark runs and reports "
+              "a single GPU.", file=sys.stderr)
         return 2
 
     import torch
