@@ -342,7 +342,7 @@ def parse():
     ap.add_argument("--case", action="append", default=None,
                     help="restrict the step to these workloads (profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline and parity rows")
-    ap.add_argument("--cpu-macs", type=float, default=1.6e11,
+    ap.add_argument("--cpu-macs", type=float, default=6e11,
                     help="multiply-accumulates per workload in the CPU baseline sample")
     ap.add_argument("--isolated-reps", type=int, default=20,
                     help="back-to-back launches per workload for the isolated per-kernel times")
